@@ -1,0 +1,112 @@
+"""fp64 CPU oracle for the forward selective scan -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library never loads it and
+shares no code with it (the oracle is plain C compiled with gcc, see
+``ssm_oracle.c``; this file only marshals numpy arrays into it).
+
+Functions:
+  build()    -- compile ssm_oracle.c into liboracle.so with gcc (no fast-math,
+                no FMA contraction).
+  scan(...)  -- the sequential recurrence in fp64 (see ssm_oracle.c for the
+                definition and the page sections it follows).
+  combine()  -- the operator combine (a2,b2)(x)(a1,b1) = (a2 a1, a2 b1 + b2)
+                from fengwang.github.io "complex parallel scan", section "the
+                mathematical essence of the parallel scan".
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+against closed forms, special cases and invariants; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+DISC = {"zoh": 0, "euler": 1, "trap": 2}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc.  Returns the path of the shared library."""
+    cmd = [
+        "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+        "-ffp-contract=off", "-pthread", "-o", _LIB, _SRC, "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    dp = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.oracle_scan_f64.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int] + [dp] * 13 + [ctypes.c_int]
+    lib.oracle_scan_f64.restype = ctypes.c_int
+    lib.oracle_combine_f64.argtypes = [i64, dp, dp, dp, dp, dp, dp]
+    lib.oracle_combine_f64.restype = None
+    _lib = lib
+    return lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan(u, delta, A, Bm, Cm, Dskip=None, theta=None, lam=None, *, disc: str, is_complex: bool,
+         h0=None, q0=None, nthreads: int = 0, return_q: bool = False):
+    """Run the fp64 oracle.
+
+    Shapes (row-major): u, delta, lam: (B,L,D); A: (D,N); Bm, Cm: (B,L,N) real
+    or (B,L,N,2) complex; Dskip: (D,); theta: (B,L,D,N).  h0/q0 optionally give
+    the state and the previous step's q = Bm*u to continue from, with the
+    layout of h_last.  Returns (y (B,L,D), h_last (B,D,N[,2])) and q_last when
+    return_q is set.  Inputs are widened to fp64 (exact for fp32/bf16 values).
+    """
+    lib = _load()
+    u, delta, A, Bm, Cm = map(_f64, (u, delta, A, Bm, Cm))
+    Dskip, theta, lam, h0, q0 = map(_f64, (Dskip, theta, lam, h0, q0))
+    B, L, D = u.shape
+    N = A.shape[1]
+    cw = (2,) if is_complex else ()
+    y = np.empty((B, L, D), dtype=np.float64)
+    h_last = np.empty((B, D, N) + cw, dtype=np.float64)
+    q_last = np.empty((B, D, N) + cw, dtype=np.float64)
+    rc = lib.oracle_scan_f64(
+        B, L, D, N, DISC[disc], int(bool(is_complex)),
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(theta), _ptr(lam),
+        _ptr(h0), _ptr(q0), _ptr(y), _ptr(h_last), _ptr(q_last), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_scan_f64 returned {rc}")
+    if return_q:
+        return y, h_last, q_last
+    return y, h_last
+
+
+def combine(a2, b2, a1, b1):
+    """(a2,b2)(x)(a1,b1) = (a2*a1, a2*b1 + b2) elementwise on complex arrays."""
+    lib = _load()
+    a2, b2, a1, b1 = (np.ascontiguousarray(np.asarray(v, dtype=np.complex128)) for v in (a2, b2, a1, b1))
+    n = a2.size
+    ao = np.empty(n, dtype=np.complex128)
+    bo = np.empty(n, dtype=np.complex128)
+    lib.oracle_combine_f64(n, *(x.ctypes.data_as(ctypes.c_void_p) for x in (a2, b2, a1, b1, ao, bo)))
+    return ao.reshape(a2.shape), bo.reshape(a2.shape)

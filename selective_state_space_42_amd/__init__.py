@@ -1,0 +1,16 @@
+"""MI355X-native forward selective scan (HIP kernels for gfx950 behind a C ABI).
+
+The compute path is the shared library ``libssmscan.so`` built from ``csrc/``;
+``scan.py`` is the thin ctypes binding (argument marshalling only).  The
+binding is imported lazily so that ``selective_state_space_42_amd.inputs`` can
+be used without loading the HIP library.
+"""
+
+__all__ = ["ssm_scan_fwd", "ssm_scan_workspace_bytes", "ssm_scan_status_string", "ssm_scan_abi_version"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import scan
+        return getattr(scan, name)
+    raise AttributeError(name)
