@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Throughput of the forward selective scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--algo auto]
+
+A step is one full scan (discretisation, recurrence, output contraction,
+carry between tiles) over one batch of seeded synthetic inputs that are
+already resident in HBM.  Rank 0 prints one JSON line:
+
+  value      tokens*channels/s = B*L*D / (seconds per step)
+  roofline   algorithmic HBM bytes per launch / kernel time vs 8.0 TB/s
+             (algorithmic bytes: every input read once, every output written
+             once); `traffic` comes from the committed
+             rocprofv3 counter summary when it was taken on the current
+             kernel sources, else null
+  cpu_baseline  the fp64 oracle timed on the host's cores over a bounded
+             sample of channels of the same workload
+
+The default workload is the largest one (B=1, D=1024, L=2^20, N=16, complex
+exp-trapezoidal, bf16 I/O, fp32 arithmetic), on which the HBM-bandwidth target
+is stated.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selective-scan tokens*channels/s + achieved HBM GB/s (% of MI355X peak)"
+UNIT = "tokens*channels/s"
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "complex_trap_bf16_b1_d1024_l1048576_n16"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w) -> int:
+    """Each input read once and each output written once."""
+    e = 4 if w.io_dtype == "f32" else 2
+    B, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
+    trap = 1 if w.disc == "trap" else 0
+    cplx = 1 if w.is_complex else 0
+    return (e * B * L * D * (3 + trap)          # u, delta, (lambda), y
+            + e * B * L * D * N * cplx          # theta
+            + 2 * e * B * L * N * (1 + cplx)    # B, C
+            + 4 * D * N + 4 * D                 # A, D
+            + 4 * B * D * N * (1 + cplx))       # h_last
+
+
+def kernel_source_hash() -> str:
+    csrc = os.path.join(ROOT, "selective_state_space_42_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".h", ".hip")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str, algo: str):
+    """HBM bytes per launch from the committed counter summary, if current."""
+    try:
+        rec = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload, {}).get(algo)
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inputs, w, y_gpu, target_s: float):
+    """Time the fp64 oracle on a bounded channel sample; also report its parity.
+
+    Channels are taken in groups of one per host thread (spread evenly over D)
+    until about `target_s` seconds of oracle time are spent, so the host
+    memory for the fp64 copy stays bounded.  Only the oracle calls are timed.
+    """
+    import numpy as np
+    import torch
+
+    import oracle
+    from selective_state_space_42_amd.inputs import channel_sample
+
+    threads = max(1, min(os.cpu_count() or 1, 64))
+    order = np.random.default_rng(0).permutation(w.dim).tolist()
+    spent, tc, used, err, groups = 0.0, 0, 0, 0.0, 0
+    for g0 in range(0, w.dim, threads):
+        idx = sorted(order[g0:g0 + threads])
+        x = channel_sample(inputs, idx)
+        t0 = time.perf_counter()
+        y_ref, _ = oracle.scan(x["u"], x["delta"], x["A"], x["Bm"], x["Cm"], x["Dskip"], x["theta"], x["lam"],
+                               disc=w.disc, is_complex=w.is_complex, nthreads=len(idx))
+        spent += time.perf_counter() - t0
+        tc += w.batch * w.seqlen * len(idx)
+        used = max(used, len(idx))
+        groups += 1
+        yg = y_gpu.index_select(2, torch.as_tensor(idx, device=y_gpu.device)).float().cpu().double().numpy()
+        err = max(err, float(np.max(np.abs(yg - y_ref)) / np.max(np.abs(y_ref))))
+        del x, y_ref, yg
+        if spent >= target_s:
+            break
+    return {
+        "value": tc / spent, "unit": UNIT, "cores": used, "kind": "oracle",
+        "sample": f"{tc // (w.batch * w.seqlen)} of {w.dim} channels (random, seed 0) in {groups} group(s), "
+                  f"every batch row and step, N={w.dstate}: {tc} tokens*channels in {spent:.1f} s of "
+                  f"fp64 C oracle time on {used} pthreads",
+        "parity_err_y_on_sample": err,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--algo", default="auto", choices=["auto", "sequential", "chunked"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this scan shards along channels with no communication, "
+              "and multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from selective_state_space_42_amd.inputs import WORKLOADS, make_inputs
+    from selective_state_space_42_amd.scan import make_desc, ssm_scan_fwd, ssm_scan_workspace_bytes
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating {w.name} on {torch.cuda.get_device_name(dev)}")
+    inputs = make_inputs(w, device=dev)
+    torch.cuda.synchronize()
+    y = torch.empty_like(inputs["u"])
+    h_shape = (w.batch, w.dim, w.dstate, 2) if w.is_complex else (w.batch, w.dim, w.dstate)
+    h_last = torch.empty(h_shape, dtype=torch.float32, device=dev)
+    desc = make_desc(w.batch, w.seqlen, w.dim, w.dstate, inputs["u"].dtype, w.disc, w.is_complex, args.algo)
+    ws_bytes = ssm_scan_workspace_bytes(desc)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ssm_scan_fwd(inputs["u"], inputs["delta"], inputs["A"], inputs["Bm"], inputs["Cm"], inputs["Dskip"],
+                     inputs["theta"], inputs["lam"], disc=w.disc, y=y, h_last=h_last,
+                     workspace=ws if ws_bytes else None, algo=args.algo, stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} done")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+
+    tc = w.batch * w.seqlen * w.dim
+    alg_bytes = algorithmic_bytes(w)
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    algo_used = args.algo
+    if algo_used == "auto":
+        algo_used = "chunked" if ws_bytes > 0 else "sequential"
+    traffic = traffic_from_profile(w.name, algo_used)
+
+    out = {
+        "metric": METRIC, "value": tc / (ms * 1e-3), "unit": UNIT, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen, "dstate": w.dstate,
+                   "disc": w.disc, "complex": w.is_complex, "io_dtype": w.io_dtype, "algo": algo_used},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a channel sample")
+        out["cpu_baseline"] = cpu_baseline(inputs, w, y, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

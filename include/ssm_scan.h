@@ -1,0 +1,146 @@
+/*
+ * ssm_scan.h -- C ABI of libssmscan.so, the forward selective scan for
+ * AMD MI355X (gfx950).
+ *
+ * The operation (per batch b, channel d, state n; h_{-1} = 0):
+ *
+ *   alpha_t[n] = exp(delta_t A[d,n]) * e^{i theta_t[n]}      (complex state)
+ *              = exp(delta_t A[d,n])                          (real state)
+ *   h_t[n]     = alpha_t[n] h_{t-1}[n] + bterm_t[n]
+ *   y_t        = Re( sum_n C_t[n] h_t[n] ) + D[d] u_t
+ *
+ * with the b-term of the chosen discretisation (q_t[n] = B_t[n] u_t):
+ *   ZOH                  bterm = (exp(delta A) - 1)/A * q_t      (delta q_t if A = 0)
+ *   exponential Euler    bterm = delta_t q_t
+ *   exp.-trapezoidal     bterm = lambda_t delta_t q_t
+ *                              + (1 - lambda_t) delta_t alpha_t q_{t-1},  q_{-1} = 0
+ *
+ * Sources: the recurrence and its associative combine follow the
+ * fengwang.github.io essay on the complex parallel scan (section on the
+ * mathematics of the parallel scan); the three discretisations follow the
+ * discretisation table of the ai.tomabc.com Mamba-3 paper story, and its
+ * complex-state section for the rotation e^{i theta_t} with A real; the ZOH
+ * form also appears in section 2.1 of the blog.lonae.com essay on the dual
+ * spectral theory of SSMs and section 2.2 of the metaphor-xennon Mamba-3
+ * notes; the output uses the post-update state as in the mamba2_ssd loop of
+ * the blog.lonae.com essay (section 3.2).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device,
+ *    dense row-major in the index order given, with no strides.  Complex
+ *    values are interleaved (re, im).
+ *  - The caller allocates and owns every buffer, including the workspace.
+ *    The library allocates no device memory, keeps no pointer after the call
+ *    returns, and never synchronises the host with the device.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *    Buffers must stay valid until that work completes.  Faults during
+ *    execution surface at the caller's next synchronisation of the stream.
+ *  - Outputs must not alias inputs.  Calls that share a workspace must not
+ *    overlap in time (they would race on its flags).
+ *  - Every argument is validated before any HIP call; an invalid call
+ *    returns a non-zero status and enqueues nothing.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_SCAN_ABI_VERSION 1
+
+/* Element type of u, delta, B, C, theta, lambda and y.  A, D and h_last are
+ * always fp32; all arithmetic is fp32 (bf16 inputs are widened exactly, y is
+ * rounded to nearest-even on the way out). */
+typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
+
+typedef enum {
+    SSM_DISC_ZOH = 0,             /* real state only */
+    SSM_DISC_EXP_EULER = 1,
+    SSM_DISC_EXP_TRAPEZOIDAL = 2  /* needs lambda */
+} ssm_disc_t;
+
+/* Kernel family.  AUTO picks by shape: SEQUENTIAL sweeps the whole sequence
+ * per channel (needs many channels to fill the GPU); CHUNKED splits the
+ * sequence into tiles and carries the state between tiles with a decoupled
+ * look-back (for long sequences / few channels).  Both give the same result
+ * up to rounding. */
+typedef enum { SSM_ALGO_AUTO = 0, SSM_ALGO_SEQUENTIAL = 1, SSM_ALGO_CHUNKED = 2 } ssm_algo_t;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_INVALID_ARGUMENT = 1,   /* null required pointer, bad size, overflow,
+                                       misalignment, forbidden NULL/non-NULL combination */
+    SSM_ERR_UNSUPPORTED = 2,        /* complex ZOH, dstate > 64 (> 16 for CHUNKED),
+                                       unknown enum value */
+    SSM_ERR_WORKSPACE_TOO_SMALL = 3,
+    SSM_ERR_HIP = 4                 /* a HIP call failed; see ssm_scan_last_hip_error() */
+} ssm_status_t;
+
+typedef struct {
+    int64_t batch;   /* B >= 1 */
+    int64_t seqlen;  /* L >= 1 */
+    int64_t dim;     /* D >= 1, channels */
+    int64_t dstate;  /* N, 1 <= N <= 64 */
+    int32_t io_dtype;   /* ssm_dtype_t */
+    int32_t disc;       /* ssm_disc_t */
+    int32_t is_complex; /* 0: real state, B, C real; 1: complex state, B, C complex */
+    int32_t algo;       /* ssm_algo_t */
+} ssm_scan_desc_t;
+
+/* Bytes of workspace ssm_scan_fwd needs for `desc` (0 when the chosen kernel
+ * needs none).  Returns 0 for an invalid descriptor as well; ssm_scan_fwd
+ * reports that case. */
+size_t ssm_scan_workspace_bytes(const ssm_scan_desc_t *desc);
+
+/*
+ * Forward selective scan.
+ *
+ *   u       [B][L][D]          io dtype   input x_t of each channel
+ *   delta   [B][L][D]          io dtype   step sizes Delta_t (> 0 expected, not checked)
+ *   A       [D][N]             fp32       diagonal state matrix (real)
+ *   B       [B][L][N]          io dtype   real input projection, or
+ *           [B][L][N][2]                  complex (is_complex = 1)
+ *   C       same layout as B              output projection (no conjugate)
+ *   D       [D] fp32 or NULL              skip term; NULL means 0
+ *   theta   [B][L][D][N] io dtype or NULL rotation angle (radians) of the complex
+ *                                         state; must be NULL when is_complex = 0;
+ *                                         NULL with is_complex = 1 means theta = 0
+ *   lambda  [B][L][D] io dtype            trapezoid weight; required for
+ *                                         EXP_TRAPEZOIDAL, must be NULL otherwise
+ *   y       [B][L][D] io dtype            output (written)
+ *   h_last  [B][D][N] fp32, or            final state h_{L-1} (written);
+ *           [B][D][N][2], or NULL         NULL means not written
+ *   workspace, workspace_bytes            device scratch of at least
+ *                                         ssm_scan_workspace_bytes(desc) bytes,
+ *                                         256-byte aligned; may be NULL when that
+ *                                         is 0.  Its contents need no
+ *                                         initialisation and are not preserved.
+ *   stream                                hipStream_t (NULL = default stream)
+ *
+ * Alignment: every pointer must be aligned to its element size (4 bytes for
+ * fp32, 2 for bf16, 8 for complex fp32 h_last).  Returns an ssm_status_t.
+ */
+int ssm_scan_fwd(const ssm_scan_desc_t *desc, const void *u, const void *delta, const float *A,
+                 const void *B, const void *C, const float *D, const void *theta,
+                 const void *lambda, void *y, float *h_last, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *ssm_scan_status_string(int status);
+
+/* The hipError_t of the last failed HIP call made by this thread inside the
+ * library (0 if none). */
+int ssm_scan_last_hip_error(void);
+
+/* SSM_SCAN_ABI_VERSION of the loaded library. */
+int ssm_scan_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,48 @@
+"""Build libssmscan.so (HIP, gfx950) in-tree with hipcc.
+
+    python -m selective_state_space_42_amd.build
+
+Every HIP source is compiled with packed-fp32 instruction selection turned
+off (-target-feature -packed-fp32-ops): scalar fp32 arithmetic only.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libssmscan.so")
+SOURCES = [os.path.join(CSRC, "ssm_scan.hip")]
+HEADERS = [os.path.join(ROOT, "include", "ssm_scan.h")] + [
+    os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".h")]
+ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc_cmd(out: str = LIB, extra=()):
+    return [
+        "hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-command-line-argument",
+        "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+        *extra, "-o", out, *SOURCES,
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = hipcc_cmd(tmp)
+    if verbose:
+        print(" ".join(cmd))
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building libssmscan.so")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

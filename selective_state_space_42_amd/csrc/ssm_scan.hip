@@ -1,0 +1,157 @@
+// ssm_scan.hip -- host side of libssmscan.so: argument validation, kernel
+// choice, workspace sizing and launches behind the C ABI of include/ssm_scan.h.
+//
+// Validation happens before any HIP call, so every error path can be
+// exercised without a GPU.  The library allocates nothing and never
+// synchronises the host; all work is enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "ssm_scan.h"
+#include "device_common.h"
+#include "kernel_sequential.h"
+#include "kernel_chunked.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return SSM_OK;
+    g_last_hip_error = static_cast<int>(e);
+    return SSM_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int next_pow2(int64_t v) {
+    int r = 1;
+    while (r < v) r <<= 1;
+    return r;
+}
+
+// Shape and mode checks shared by ssm_scan_workspace_bytes and ssm_scan_fwd.
+int check_desc(const ssm_scan_desc_t* d) {
+    if (!d) return SSM_ERR_INVALID_ARGUMENT;
+    if (d->batch < 1 || d->seqlen < 1 || d->dim < 1 || d->dstate < 1) return SSM_ERR_INVALID_ARGUMENT;
+    if (d->io_dtype != SSM_DTYPE_F32 && d->io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
+    if (d->disc < SSM_DISC_ZOH || d->disc > SSM_DISC_EXP_TRAPEZOIDAL) return SSM_ERR_UNSUPPORTED;
+    if (d->is_complex != 0 && d->is_complex != 1) return SSM_ERR_UNSUPPORTED;
+    if (d->algo < SSM_ALGO_AUTO || d->algo > SSM_ALGO_CHUNKED) return SSM_ERR_UNSUPPORTED;
+    if (d->is_complex && d->disc == SSM_DISC_ZOH) return SSM_ERR_UNSUPPORTED;
+    if (d->dstate > 64) return SSM_ERR_UNSUPPORTED;
+    // B*L*D*N*2 complex words of 4 bytes must fit an int64 byte offset.
+    int64_t v = d->batch, r;
+    if (__builtin_mul_overflow(v, d->seqlen, &r)) return SSM_ERR_INVALID_ARGUMENT;
+    if (__builtin_mul_overflow(r, d->dim, &r)) return SSM_ERR_INVALID_ARGUMENT;
+    if (__builtin_mul_overflow(r, d->dstate, &r)) return SSM_ERR_INVALID_ARGUMENT;
+    if (__builtin_mul_overflow(r, int64_t(8), &r)) return SSM_ERR_INVALID_ARGUMENT;
+    return SSM_OK;
+}
+
+// Kernel family for a valid descriptor.
+int choose_algo(const ssm_scan_desc_t* d) {
+    if (d->algo != SSM_ALGO_AUTO) return d->algo;
+    if (d->dstate > ssm::kChunkLanes) return SSM_ALGO_SEQUENTIAL;
+    return ssm::chunked_preferred(d->batch, d->seqlen, d->dim) ? SSM_ALGO_CHUNKED : SSM_ALGO_SEQUENTIAL;
+}
+
+template <typename T>
+int launch_sequential(const ssm_scan_desc_t* d, const ssm::SeqParams& p, hipStream_t s) {
+    const int64_t waves = (d->batch * d->dim + (64 / p.lpc) - 1) / (64 / p.lpc);
+    const int64_t blocks = (waves + 3) / 4;
+    if (blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+    if (d->is_complex) {
+        if (d->disc == SSM_DISC_EXP_EULER)
+            hipLaunchKernelGGL((ssm::scan_sequential_kernel<T, ssm::kEuler, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((ssm::scan_sequential_kernel<T, ssm::kTrap, true>), grid, block, 0, s, p);
+    } else {
+        if (d->disc == SSM_DISC_ZOH)
+            hipLaunchKernelGGL((ssm::scan_sequential_kernel<T, ssm::kZOH, false>), grid, block, 0, s, p);
+        else if (d->disc == SSM_DISC_EXP_EULER)
+            hipLaunchKernelGGL((ssm::scan_sequential_kernel<T, ssm::kEuler, false>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((ssm::scan_sequential_kernel<T, ssm::kTrap, false>), grid, block, 0, s, p);
+    }
+    return hip_status(hipGetLastError());
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_abi_version(void) { return SSM_SCAN_ABI_VERSION; }
+
+int ssm_scan_last_hip_error(void) { return g_last_hip_error; }
+
+const char* ssm_scan_status_string(int status) {
+    switch (status) {
+        case SSM_OK: return "ok";
+        case SSM_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case SSM_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SSM_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case SSM_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t ssm_scan_workspace_bytes(const ssm_scan_desc_t* desc) {
+    if (check_desc(desc) != SSM_OK) return 0;
+    if (choose_algo(desc) != SSM_ALGO_CHUNKED) return 0;
+    if (desc->dstate > ssm::kChunkLanes) return 0;
+    return ssm::chunked_workspace_bytes(desc->batch, desc->seqlen, desc->dim);
+}
+
+int ssm_scan_fwd(const ssm_scan_desc_t* desc, const void* u, const void* delta, const float* A,
+                 const void* B, const void* C, const float* D, const void* theta, const void* lambda,
+                 void* y, float* h_last, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_desc(desc);
+    if (st != SSM_OK) return st;
+    const bool trap = desc->disc == SSM_DISC_EXP_TRAPEZOIDAL;
+    if (!u || !delta || !A || !B || !C || !y) return SSM_ERR_INVALID_ARGUMENT;
+    if (trap != (lambda != nullptr)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!desc->is_complex && theta) return SSM_ERR_INVALID_ARGUMENT;
+    const size_t es = desc->io_dtype == SSM_DTYPE_F32 ? 4 : 2;
+    const void* io_ptrs[] = {u, delta, B, C, theta, lambda, y};
+    for (const void* q : io_ptrs)
+        if (q && !aligned(q, es)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!aligned(A, 4) || (D && !aligned(D, 4))) return SSM_ERR_INVALID_ARGUMENT;
+    if (h_last && !aligned(h_last, desc->is_complex ? 8 : 4)) return SSM_ERR_INVALID_ARGUMENT;
+
+    const int algo = choose_algo(desc);
+    if (algo == SSM_ALGO_CHUNKED && desc->dstate > ssm::kChunkLanes) return SSM_ERR_UNSUPPORTED;
+    const size_t need = algo == SSM_ALGO_CHUNKED
+                            ? ssm::chunked_workspace_bytes(desc->batch, desc->seqlen, desc->dim)
+                            : 0;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned(workspace, 256)) return SSM_ERR_INVALID_ARGUMENT;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (algo == SSM_ALGO_CHUNKED) {
+        ssm::ChunkParams p{};
+        p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.theta = theta;
+        p.lambda = lambda; p.y = y; p.h_last = h_last;
+        p.batch = desc->batch; p.seqlen = desc->seqlen; p.dim = desc->dim; p.dstate = desc->dstate;
+        p.workspace = workspace;
+        st = desc->io_dtype == SSM_DTYPE_F32
+                 ? ssm::launch_chunked<float>(desc->disc, desc->is_complex != 0, p, s)
+                 : ssm::launch_chunked<uint16_t>(desc->disc, desc->is_complex != 0, p, s);
+        return st < 0 ? hip_status(static_cast<hipError_t>(-st)) : st;
+    }
+
+    ssm::SeqParams p{};
+    p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.theta = theta;
+    p.lambda = lambda; p.y = y; p.h_last = h_last;
+    p.batch = desc->batch; p.seqlen = desc->seqlen; p.dim = desc->dim; p.dstate = desc->dstate;
+    p.lpc = next_pow2(desc->dstate);
+    return desc->io_dtype == SSM_DTYPE_F32 ? launch_sequential<float>(desc, p, s)
+                                           : launch_sequential<uint16_t>(desc, p, s);
+}
+
+}  // extern "C"

@@ -164,7 +164,7 @@ def channel_sample(inputs: dict, d_index) -> dict:
         A=host(inputs["A"].index_select(0, idx)),
         Bm=host(inputs["Bm"]),
         Cm=host(inputs["Cm"]),
-        Dskip=host(inputs["Dskip"].index_select(0, idx)),
+        Dskip=None if inputs["Dskip"] is None else host(inputs["Dskip"].index_select(0, idx)),
         theta=None if inputs["theta"] is None else host(inputs["theta"].index_select(2, idx)),
         lam=None if inputs["lam"] is None else host(inputs["lam"].index_select(2, idx)),
     )

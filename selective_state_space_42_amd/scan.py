@@ -1,0 +1,118 @@
+"""Thin Python binding of libssmscan.so (argument marshalling only).
+
+The names mirror the C ABI in include/ssm_scan.h.  Every step of the scan runs
+in the HIP kernels of the library; torch only provides device memory and the
+stream.  There is no fallback: if the library is missing or its call fails,
+these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssmscan.so")
+
+SSM_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+SSM_DISC = {"zoh": 0, "euler": 1, "trap": 2}
+SSM_ALGO = {"auto": 0, "sequential": 1, "chunked": 2}
+ABI_VERSION = 1
+
+
+class ScanDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("disc", ctypes.c_int32),
+        ("is_complex", ctypes.c_int32), ("algo", ctypes.c_int32),
+    ]
+
+
+class ScanError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = ssm_scan_status_string(status)
+        if status == 4:
+            msg += f" (hipError_t {_lib().ssm_scan_last_hip_error()})"
+        super().__init__(f"{where}: status {status}: {msg}")
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m selective_state_space_42_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)  # torch is imported first, so its HIP runtime is the one in use
+    vp = ctypes.c_void_p
+    lib.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 11 + [ctypes.c_size_t, vp]
+    lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
+    lib.ssm_scan_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssm_scan_status_string.argtypes = [ctypes.c_int]
+    lib.ssm_scan_status_string.restype = ctypes.c_char_p
+    lib.ssm_scan_abi_version.argtypes = []
+    lib.ssm_scan_abi_version.restype = ctypes.c_int
+    lib.ssm_scan_last_hip_error.argtypes = []
+    lib.ssm_scan_last_hip_error.restype = ctypes.c_int
+    if lib.ssm_scan_abi_version() != ABI_VERSION:
+        raise RuntimeError("libssmscan.so ABI version mismatch")
+    _LIB = lib
+    return lib
+
+
+def make_desc(batch, seqlen, dim, dstate, io_dtype, disc, is_complex, algo="auto") -> ScanDesc:
+    return ScanDesc(int(batch), int(seqlen), int(dim), int(dstate), int(SSM_DTYPE.get(io_dtype, io_dtype)),
+                    int(SSM_DISC.get(disc, disc)), int(bool(is_complex)), int(SSM_ALGO.get(algo, algo)))
+
+
+def ssm_scan_abi_version() -> int:
+    return _lib().ssm_scan_abi_version()
+
+
+def ssm_scan_status_string(status: int) -> str:
+    return _lib().ssm_scan_status_string(int(status)).decode()
+
+
+def ssm_scan_workspace_bytes(desc: ScanDesc) -> int:
+    return int(_lib().ssm_scan_workspace_bytes(ctypes.byref(desc)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def ssm_scan_fwd(u, delta, A, B, C, D=None, theta=None, lam=None, *, disc: str, y=None, h_last=None,
+                 want_h_last: bool = True, workspace=None, algo: str = "auto", stream=None):
+    """Run the scan on torch device tensors; returns (y, h_last).
+
+    Layouts as in include/ssm_scan.h: u, delta, lam (B,L,D); A (D,N) fp32;
+    B, C (B,L,N) real or (B,L,N,2) complex; D (D,) fp32; theta (B,L,D,N).
+    The state is complex when B has a trailing dimension of 2.  y, h_last and
+    the workspace are allocated with torch when not given.
+    """
+    Bsz, L, Dm = u.shape
+    N = A.shape[1]
+    is_complex = B.dim() == 4
+    desc = make_desc(Bsz, L, Dm, N, u.dtype, disc, is_complex, algo)
+    if y is None:
+        y = torch.empty_like(u)
+    if h_last is None and want_h_last:
+        shape = (Bsz, Dm, N, 2) if is_complex else (Bsz, Dm, N)
+        h_last = torch.empty(shape, dtype=torch.float32, device=u.device)
+    need = ssm_scan_workspace_bytes(desc)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream if u.is_cuda else 0
+    st = _lib().ssm_scan_fwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                             _ptr(theta), _ptr(lam), _ptr(y), _ptr(h_last), _ptr(workspace), ws_bytes,
+                             ctypes.c_void_p(stream))
+    if st != 0:
+        raise ScanError(st, "ssm_scan_fwd")
+    return y, h_last
