@@ -1,11 +1,73 @@
-// kernel_chunked.h -- chunked scan with a decoupled look-back carry (in progress).
+// kernel_chunked.h -- the chunked scan: register-resident tiles along the
+// sequence, combined by a decoupled look-back.
+//
+// Work decomposition
+//   lane      = (channel c, state pair p): 8 lanes per channel, states
+//               n = 2p, 2p+1 in each lane, 8 consecutive channels per wave.
+//   wave      = 24 consecutive steps of those 8 channels.
+//   tile (WG) = 4 waves = 96 consecutive steps x 8 channels.
+// Tiles along the sequence are chained by the associative combine of the
+// operator pairs (a, b) -> (a2 a1, a2 b1 + b2) (fengwang.github.io essay on
+// the complex parallel scan, section on the mathematics of the parallel
+// scan; the chunk-and-merge formulation is section 3 of the intelliparadigm
+// article on selective scan).  Each tile is processed in two passes over
+// registers:
+//   pass 1  discretise every step (one exp and, for a complex state, one
+//           sin/cos per element), keep alpha_t in VGPRs, run the recurrence
+//           from a zero state to get the wave's aggregate (P = prod alpha,
+//           h_loc); combine the 4 wave aggregates in LDS; publish the tile
+//           aggregate; look back over predecessor tiles for the carry-in.
+//   pass 2  rerun the recurrence from the true incoming state using the
+//           stored alpha_t (no transcendental is evaluated twice) and form
+//           y_t = Re(sum_n C_t[n] h_t[n]) + D u_t; the sum over n is reduced
+//           through LDS, 8 steps at a time.
+// The (B, L, D, N) state never reaches memory.
+//
+// Exponential-trapezoidal form.  With beta'_t = (1 - lambda_t) delta_t the
+// recurrence h_t = alpha_t h_{t-1} + lambda_t delta_t q_t
+// + beta'_t alpha_t q_{t-1} (q_t = B_t u_t) is carried in the shifted state
+// g_t = h_t + beta'_{t+1} q_t, which obeys the exponential-Euler form
+//   g_t = alpha_t g_{t-1} + w_t B_t,   w_t = (lambda_t delta_t + beta'_{t+1}) u_t,
+// and y_t = Re(sum_n C_t g_t) + (D - beta'_{t+1} K_t) u_t with
+// K_t = Re(sum_n C_t[n] B_t[n]); beta'_L = 0 so g_{L-1} = h_{L-1}.  This is the
+// two-band (decay mask times two-band mask) structure the ai.tomabc.com
+// Mamba-3 story describes for the exponential-trapezoidal discretisation.
+//
+// Cross-tile protocol (per channel group, tiles in sequence order):
+//   flag 0 = nothing, 1 = aggregate (P, h_loc) published, 2 = inclusive state
+//   published.  Tiles take tickets from one of 8 counters (one per XCD slot,
+//   blockIdx % 8) so that a tile only ever waits on tiles that started earlier
+//   (forward progress).  Flags and payloads move only through relaxed
+//   agent-scope atomics, which bypass the per-XCD L2 (coherent across XCDs);
+//   the publisher waits for its payload stores to complete (s_waitcnt
+//   vmcnt(0)) before storing the flag, and readers load the payload only after
+//   seeing the flag.  This avoids whole-L2 write-back/invalidate fences.
+// A prep kernel zeroes flags and counters, converts B and C to fp32 rows of
+// (B re, B im, C re, C im) per (b, t, n) (zero padded to whole tiles and to
+// 16 states) and, for the trapezoid, computes K_t.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
+#include "device_math.h"
 
 namespace ssm {
 
-constexpr int kChunkLanes = 16;  // lanes per channel of the chunked kernel (max dstate)
+constexpr int kChunkLanes = 16;  // states covered by one channel's lanes (max dstate)
+
+namespace chunk {
+constexpr int kLPC = 8;            // lanes per channel
+constexpr int kNPL = 2;            // states per lane
+constexpr int kCPW = 64 / kLPC;    // channels per wave and per tile
+constexpr int kWaves = 4;          // waves per workgroup, consecutive in time
+constexpr int kTW = 24;            // steps per wave (a multiple of 8)
+constexpr int kTT = kWaves * kTW;  // steps per tile
+constexpr int kThreads = kWaves * 64;
+constexpr int kSlots = 8;          // ticket counters (one per XCD)
+constexpr int kPayloadF2 = 3 * 64 * kNPL;  // float2 per tile: aggregate P, aggregate h, inclusive h
+enum : uint32_t { kFlagEmpty = 0, kFlagAggregate = 1, kFlagInclusive = 2 };
+}  // namespace chunk
 
 struct ChunkParams {
     const void* u;
@@ -20,12 +82,757 @@ struct ChunkParams {
     float* h_last;
     int64_t batch, seqlen, dim, dstate;
     void* workspace;
+    int32_t theta_pairs;  // 1: dstate even and theta aligned to two elements
+    int32_t rows_dma;     // 1: dim even and u, delta, lambda 4-byte aligned (rows move as dwords)
 };
 
-inline bool chunked_preferred(int64_t, int64_t, int64_t) { return false; }
-inline size_t chunked_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+struct ChunkLayout {
+    int64_t n_dblk;    // channel groups per batch row, ceil(D / kCPW)
+    int64_t groups;    // batch * n_dblk
+    int64_t n_tt;      // tiles along the sequence
+    int64_t l_pad;     // n_tt * kTT
+    int64_t slot_groups[chunk::kSlots];
+    int64_t max_slot_tiles;
+    uint64_t off_flags, off_payload, off_bc, off_k, total;
+};
+
+inline uint64_t round256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+// Channel groups of 8 are bundled by 8 (64 channels, one 128-byte row of the
+// per-token arrays in bf16); bundle s goes to ticket slot s % 8.
+inline ChunkLayout chunk_layout(int64_t B, int64_t L, int64_t D) {
+    using namespace chunk;
+    ChunkLayout l{};
+    l.n_dblk = (D + kCPW - 1) / kCPW;
+    l.groups = B * l.n_dblk;
+    l.n_tt = (L + kTT - 1) / kTT;
+    l.l_pad = l.n_tt * kTT;
+    const int64_t full = l.groups / 8, rem = l.groups % 8;
+    int64_t mx = 0;
+    for (int s = 0; s < kSlots; ++s) {
+        int64_t cnt = 8 * (full / kSlots + (s < full % kSlots ? 1 : 0));
+        if (rem > 0 && s == full % kSlots) cnt += rem;
+        l.slot_groups[s] = cnt;
+        mx = cnt > mx ? cnt : mx;
+    }
+    l.max_slot_tiles = mx * l.n_tt;
+    uint64_t off = 256;  // ticket counters
+    l.off_flags = off;
+    off += round256(uint64_t(l.groups * l.n_tt) * 4);
+    l.off_payload = off;
+    off += round256(uint64_t(l.groups * l.n_tt) * kPayloadF2 * 8);
+    l.off_bc = off;
+    off += round256(uint64_t(B * l.l_pad) * kChunkLanes * 16);
+    l.off_k = off;
+    off += round256(uint64_t(B * l.l_pad) * 4);
+    l.total = off;
+    return l;
+}
+
+inline size_t chunked_workspace_bytes(int64_t B, int64_t L, int64_t D) { return chunk_layout(B, L, D).total; }
+
+// The chunked kernel fills the GPU whatever the channel count; the sequential
+// kernel is kept for dstate > 16 and as an independent formulation.
+inline bool chunked_preferred(int64_t, int64_t, int64_t) { return true; }
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+__device__ __forceinline__ void st_agent(float2* p, float2 v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_agent(const float2* p) {
+    return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT));
+}
+
+struct Cx {
+    float re, im;
+};
+__device__ __forceinline__ Cx cmul(Cx a, Cx b) { return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re}; }
+__device__ __forceinline__ Cx cfma(Cx a, Cx b, Cx c) {  // a*b + c
+    return {a.re * b.re - a.im * b.im + c.re, a.re * b.im + a.im * b.re + c.im};
+}
+__device__ __forceinline__ Cx to_cx(float2 v) { return {v.x, v.y}; }
+__device__ __forceinline__ float2 to_f2(Cx v) { return make_float2(v.re, v.im); }
+
+// ---------------------------------------------------------------- prep kernel
+
+template <typename T, bool CPLX, bool TRAP>
+__global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkParams p, ChunkLayout lay) {
+    using E = Elem<T>;
+    char* ws = static_cast<char*>(p.workspace);
+    uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws);
+    uint32_t* flags = reinterpret_cast<uint32_t*>(ws + lay.off_flags);
+    float4* bc = reinterpret_cast<float4*>(ws + lay.off_bc);
+    float* kt = reinterpret_cast<float*>(ws + lay.off_k);
+    const T* Bm = static_cast<const T*>(p.B);
+    const T* Cm = static_cast<const T*>(p.C);
+
+    const int64_t gtid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    if (gtid < chunk::kSlots) ctrl[gtid] = 0;
+    const int64_t nflags = lay.groups * lay.n_tt;
+    for (int64_t i = gtid; i < nflags; i += stride) flags[i] = chunk::kFlagEmpty;
+
+    // rows of kChunkLanes entries; stride is a multiple of 16 so each row's
+    // 16 lanes stay together for the K_t reduction
+    const int64_t items = p.batch * lay.l_pad * kChunkLanes;
+    for (int64_t i = gtid; i < items; i += stride) {
+        const int64_t row = i / kChunkLanes;
+        const int n = static_cast<int>(i % kChunkLanes);
+        const int64_t b = row / lay.l_pad, t = row % lay.l_pad;
+        float br = 0.f, bi = 0.f, cr = 0.f, ci = 0.f;
+        if (t < p.seqlen && n < p.dstate) {
+            const int64_t k = (b * p.seqlen + t) * p.dstate + n;
+            if constexpr (CPLX) {
+                br = E::load(Bm, 2 * k);
+                bi = E::load(Bm, 2 * k + 1);
+                cr = E::load(Cm, 2 * k);
+                ci = E::load(Cm, 2 * k + 1);
+            } else {
+                br = E::load(Bm, k);
+                cr = E::load(Cm, k);
+            }
+        }
+        bc[i] = make_float4(br, bi, cr, ci);
+        if constexpr (TRAP) {
+            float part = cr * br - ci * bi;  // Re(C B)
+            for (int off = 8; off > 0; off >>= 1) part += __shfl_xor(part, off, 16);
+            if (n == 0) kt[row] = part;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- main kernel
+
+// Coordinates of one tile (uniform across the workgroup).
+struct Tile {
+    int64_t tt;   // tile index along the sequence
+    int64_t g;    // channel group
+    int64_t b;    // batch row
+    int64_t d0;   // first channel
+    int64_t t0;   // first step
+    int nch;      // channels of the group that exist (<= kCPW)
+};
+
+__device__ __forceinline__ Tile decode_tile(uint32_t local, uint32_t per_tt, int slot, const ChunkLayout& lay,
+                                            int64_t D) {
+    using namespace chunk;
+    Tile t;
+    const uint32_t tt = local / per_tt, r = local % per_tt;
+    const uint32_t g = ((r / 8) * kSlots + slot) * 8 + (r % 8);
+    const uint32_t ndb = static_cast<uint32_t>(lay.n_dblk);
+    t.tt = tt;
+    t.g = g;
+    t.b = g / ndb;
+    t.d0 = int64_t(g % ndb) * kCPW;
+    t.t0 = int64_t(tt) * kTT;
+    t.nch = static_cast<int>(D - t.d0 < kCPW ? D - t.d0 : kCPW);
+    return t;
+}
+
+// theta of one lane for one wave's steps, as loaded: bf16 keeps the (n, n+1)
+// pair packed in one register; fp32 keeps two values.
+template <typename T>
+struct ThetaRegs;
+template <>
+struct ThetaRegs<uint16_t> {
+    uint32_t w[chunk::kTW];
+    __device__ __forceinline__ float get(int s, int j) const { return j ? bf16_hi(w[s]) : bf16_lo(w[s]); }
+    __device__ __forceinline__ void pin(int s) { ssm::pin(w[s]); }
+};
+template <>
+struct ThetaRegs<float> {
+    float v[chunk::kTW][2];
+    __device__ __forceinline__ float get(int s, int j) const { return v[s][j]; }
+    __device__ __forceinline__ void pin(int s) {
+        ssm::pin(v[s][0]);
+        ssm::pin(v[s][1]);
+    }
+};
+
+// ---- staging of one tile
+//
+// Registers carried from the issue of a tile's loads to their use.
+template <typename T>
+struct TileRegs {
+    float a_ld[chunk::kNPL];  // A of this lane's states
+    ThetaRegs<T> th;          // theta of this lane's states, this wave's steps
+    float dskip;              // D of this thread's staging channel (tid % kCPW)
+};
+
+// Raw per-step rows in LDS, exactly as stored in memory: for each of the
+// arrays u, delta, lambda, rows t0 .. t0 + kTT (one row past the tile, for
+// the trapezoid's next-step terms) of the group's kCPW channels.  They arrive
+// by buffer-to-LDS DMA in dwords, 64 per wave instruction.
+template <typename T>
+struct RawRows {
+    static constexpr int kRowDw = chunk::kCPW * int(sizeof(T)) / 4;       // dwords per row
+    static constexpr int kInstr = ((chunk::kTT + 1) * kRowDw + 63) / 64;  // DMA instructions per array
+    static constexpr int kArrayDw = kInstr * 64;                          // padded array size
+    static constexpr int kKInstr = (chunk::kTT + 63) / 64;                // K_t rows (fp32)
+};
+
+// Issue every global load of tile `t`: A and theta into registers (theta as
+// stored, decoded in pass 1), B/C rows and the raw per-step rows (and K_t)
+// into LDS by DMA.  Buffer resources cover exactly the valid data, so lanes
+// and steps outside read 0 and no load needs a branch or a mask.  With
+// p.rows_dma == 0 (odd D or unaligned pointers) the raw rows are instead
+// loaded element by element in commit_tile().
+template <typename T, int DISC, bool CPLX>
+__device__ __forceinline__ void issue_tile(TileRegs<T>& r, const ChunkParams& p, const ChunkLayout& lay,
+                                           const Tile& t, int tid, int c, int pr, int s0, int wave,
+                                           float4* s_bc_dst, uint32_t* s_raw, float* s_k) {
+    using namespace chunk;
+    using BE = Buf<T>;
+    using RR = RawRows<T>;
+    constexpr uint32_t es = BE::kSize;
+    constexpr bool kFast = std::is_same_v<T, uint16_t>;
+    constexpr bool kTR = DISC == kTrap;
+    const T* theta = static_cast<const T*>(p.theta);
+    const float4* bc = reinterpret_cast<const float4*>(static_cast<const char*>(p.workspace) + lay.off_bc);
+    const float* kt = reinterpret_cast<const float*>(static_cast<const char*>(p.workspace) + lay.off_k);
+    const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
+    const int lane = tid & 63;
+    const bool cok = c < t.nch;
+    {
+        const rsrc_t rA = make_rsrc(p.A + t.d0 * N, static_cast<uint32_t>(t.nch * N * 4));
+#pragma unroll
+        for (int j = 0; j < kNPL; ++j) {
+            const int n = pr * kNPL + j;
+            r.a_ld[j] = Buf<float>::load(rA, cok && n < N ? static_cast<uint32_t>((c * N + n) * 4) : kOutOfRange);
+        }
+        const rsrc_t rDs = make_rsrc(p.Dskip ? p.Dskip + t.d0 : p.A, p.Dskip ? static_cast<uint32_t>(t.nch * 4) : 0u);
+        r.dskip = Buf<float>::load(rDs, static_cast<uint32_t>(tid % kCPW) * 4);
+    }
+    if constexpr (CPLX) {
+        const int64_t ws0 = t.t0 + s0;  // this wave's first step
+        const int64_t vsteps = L - ws0 < 0 ? 0 : (L - ws0 > kTW ? kTW : L - ws0);
+        const uint32_t row = static_cast<uint32_t>(D * N) * es;
+        const rsrc_t rT = make_rsrc(theta + ((t.b * L + (vsteps ? ws0 : 0)) * D + t.d0) * N,
+                                    theta ? static_cast<uint32_t>(vsteps) * row : 0u);
+        const int n0 = pr * kNPL;
+        const uint32_t lo0 = cok && n0 < N ? static_cast<uint32_t>(c * N + n0) * es : kOutOfRange;
+        const uint32_t lo1 = cok && n0 + 1 < N ? static_cast<uint32_t>(c * N + n0 + 1) * es : kOutOfRange;
+#pragma unroll
+        for (int s = 0; s < kTW; ++s) {
+            if constexpr (kFast) {
+                if (p.theta_pairs) {  // N even: (n, n+1) adjacent and 4-byte aligned
+                    r.th.w[s] = __builtin_amdgcn_raw_buffer_load_b32(rT, lo0 + s * row, 0, 0);
+                } else {
+                    const uint32_t a = __builtin_amdgcn_raw_buffer_load_b16(rT, lo0 + s * row, 0, 0);
+                    const uint32_t bb = __builtin_amdgcn_raw_buffer_load_b16(rT, lo1 + s * row, 0, 0);
+                    r.th.w[s] = a | (bb << 16);
+                }
+            } else {
+                if (p.theta_pairs) {
+                    BE::load_pair(rT, lo0 + s * row, &r.th.v[s][0], &r.th.v[s][1]);
+                } else {
+                    r.th.v[s][0] = BE::load(rT, lo0 + s * row);
+                    r.th.v[s][1] = BE::load(rT, lo1 + s * row);
+                }
+            }
+        }
+    }
+    // B/C rows: wave w's 64 lanes fill 64 consecutive float4 entries per instruction
+    {
+        const float4* src = bc + (t.b * lay.l_pad + t.t0) * kChunkLanes;
+#pragma unroll
+        for (int k = 0; k < kTT * kChunkLanes / kThreads; ++k) {
+            const int i0 = k * kThreads + wave * 64;
+            __builtin_amdgcn_global_load_lds(src + i0 + lane,
+                                             (__attribute__((address_space(3))) void*)(s_bc_dst + i0), 16, 0, 0);
+        }
+    }
+    if (p.rows_dma) {
+        // rows t0 .. t0 + rows - 1 exist (rows >= 1); D even, so every row of
+        // the group starts on a dword and holds whole dwords
+        const int64_t rows = L - t.t0 > kTT + 1 ? kTT + 1 : L - t.t0;
+        const uint32_t bytes = static_cast<uint32_t>((rows - 1) * D + t.nch) * es;
+        const int64_t base = (t.b * L + t.t0) * D + t.d0;
+        const T* arrs[3] = {static_cast<const T*>(p.u), static_cast<const T*>(p.delta),
+                            static_cast<const T*>(p.lambda)};
+        constexpr int kArrays = kTR ? 3 : 2;
+        constexpr int kTotal = kArrays * RR::kInstr + (kTR ? RR::kKInstr : 0);
+        const rsrc_t rK = make_rsrc(kt + t.b * lay.l_pad + t.t0, kTT * 4);
+#pragma unroll
+        for (int q = 0; q < (kTotal + kWaves - 1) / kWaves; ++q) {
+            const int g = q * kWaves + wave;  // this wave's DMA instruction (uniform)
+            if (g < kArrays * RR::kInstr) {
+                const int ar = g / RR::kInstr, iq = g % RR::kInstr;
+                const int f = iq * 64 + lane;  // dword of the padded array
+                const int rw = f / RR::kRowDw, dw = f % RR::kRowDw;
+                const uint32_t voff = rw <= kTT ? static_cast<uint32_t>(rw * D) * es + dw * 4 : kOutOfRange;
+                const rsrc_t rs = make_rsrc(arrs[ar] + base, bytes);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void*)(s_raw + ar * RR::kArrayDw + iq * 64), 4, voff, 0, 0,
+                    0);
+            } else if (g < kTotal) {
+                const int iq = g - kArrays * RR::kInstr;
+                const int f = iq * 64 + lane;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rK, (__attribute__((address_space(3))) void*)(s_k + iq * 64), 4,
+                    f < kTT ? static_cast<uint32_t>(f) * 4 : kOutOfRange, 0, 0, 0);
+            }
+        }
+    }
+}
+
+// Write the staged per-step terms of the current tile: (delta, w) and e per
+// step and channel, from the raw rows in LDS (after they have landed and a
+// workgroup barrier).  Without DMA the raw rows are first loaded element by
+// element here (synchronously; followed by a barrier inside).
+template <typename T, int DISC>
+__device__ __forceinline__ void commit_tile(const TileRegs<T>& r, const ChunkParams& p, const ChunkLayout& lay,
+                                            const Tile& t, int tid, uint32_t* s_raw, float* s_k,
+                                            float2 (*s_dw)[chunk::kCPW], float (*s_e)[chunk::kCPW]) {
+    using namespace chunk;
+    using BE = Buf<T>;
+    using RR = RawRows<T>;
+    constexpr uint32_t es = BE::kSize;
+    constexpr bool kTR = DISC == kTrap;
+    const int64_t L = p.seqlen, D = p.dim;
+    // [array][row][kCPW] stored bit patterns, arrays RR::kArrayDw dwords apart
+    using RawT = std::conditional_t<sizeof(T) == 2, uint16_t, uint32_t>;
+    RawT* raw = reinterpret_cast<RawT*>(s_raw);
+    constexpr int kArrayEl = RR::kArrayDw * 4 / int(sizeof(T));
+    const int cc = tid % kCPW;
+    if (!p.rows_dma) {
+        const int64_t rows = L - t.t0 > kTT + 1 ? kTT + 1 : L - t.t0;
+        const uint32_t bytes = static_cast<uint32_t>((rows - 1) * D + t.nch) * es;
+        const int64_t base = (t.b * L + t.t0) * D + t.d0;
+        const T* arrs[3] = {static_cast<const T*>(p.u), static_cast<const T*>(p.delta),
+                            static_cast<const T*>(p.lambda)};
+        constexpr int kArrays = kTR ? 3 : 2;
+        const float* kt = reinterpret_cast<const float*>(static_cast<const char*>(p.workspace) + lay.off_k);
+        for (int i = tid; i < (kTT + 1) * kCPW; i += kThreads) {
+            const int rw = i / kCPW, ch = i % kCPW;
+            const uint32_t off = ch < t.nch ? static_cast<uint32_t>(rw * D + ch) * es : kOutOfRange;
+#pragma unroll
+            for (int ar = 0; ar < kArrays; ++ar)
+                raw[ar * kArrayEl + i] = static_cast<RawT>(BE::load_raw(make_rsrc(arrs[ar] + base, bytes), off));
+        }
+        if constexpr (kTR)
+            for (int i = tid; i < kTT; i += kThreads) s_k[i] = kt[t.b * lay.l_pad + t.t0 + i];
+        __syncthreads();
+    }
+    float dsk = r.dskip;
+    pin(dsk);
+#pragma unroll
+    for (int k = 0; k < kTT * kCPW / kThreads; ++k) {
+        const int i = tid + k * kThreads;
+        const int st = i / kCPW;
+        const bool ok = t.t0 + st < L && cc < t.nch;
+        const float x = BE::widen(raw[0 * kArrayEl + i]);
+        const float dt = BE::widen(raw[1 * kArrayEl + i]);
+        float w, e;
+        if constexpr (DISC == kZOH) {
+            w = x;
+            e = dsk * x;
+        } else if constexpr (DISC == kEuler) {
+            w = dt * x;
+            e = dsk * x;
+        } else {
+            const bool okn = t.t0 + st + 1 < L;
+            const float lam = BE::widen(raw[2 * kArrayEl + i]);
+            const float dn = BE::widen(raw[1 * kArrayEl + i + kCPW]);
+            const float ln = BE::widen(raw[2 * kArrayEl + i + kCPW]);
+            const float bnext = okn ? (1.f - ln) * dn : 0.f;  // beta'_{t+1}
+            w = (lam * dt + bnext) * x;
+            e = (dsk - bnext * s_k[st]) * x;
+        }
+        s_dw[st][cc] = ok ? make_float2(dt, w) : make_float2(0.f, 0.f);
+        s_e[st][cc] = ok ? e : 0.f;
+    }
+}
+
+// Sum of delta over each wave's steps, per channel (after commit_tile and a
+// barrier): one thread per (wave, channel).
+__device__ __forceinline__ void sum_deltas(int tid, const float2 (*s_dw)[chunk::kCPW], float (*s_sdt)[chunk::kCPW]) {
+    using namespace chunk;
+    if (tid < kWaves * kCPW) {
+        const int w = tid / kCPW, ch = tid % kCPW;
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < kTW; ++s) acc += s_dw[w * kTW + s][ch].x;
+        s_sdt[w][ch] = acc;
+    }
+}
+
+// Persistent workgroups: each takes tickets from its slot's counter until the
+// slot's tiles are exhausted.  The pipeline per workgroup is
+//   [tile k: commit staged values to LDS | pass 1]
+//   [issue the global loads of tile k+1 into registers | look-back of k |
+//    pass 2 of k]
+// so tile k+1's memory latency overlaps tile k's look-back and pass 2.  A
+// tile only waits on tiles with smaller tickets of the same slot; each such
+// tile is held by a running workgroup that is processing it or will process it
+// right after its current (even smaller) ticket, so the smallest unfinished
+// ticket always makes progress.
+template <typename T, int DISC, bool CPLX>
+__global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkParams p, ChunkLayout lay) {
+    using namespace chunk;
+    using BE = Buf<T>;
+    constexpr uint32_t es = BE::kSize;
+    constexpr bool kFast = std::is_same_v<T, uint16_t>;
+    using M = std::conditional_t<kFast, FastMath, AccurateMath>;
+    constexpr bool kZ = DISC == kZOH;
+    constexpr bool kTR = DISC == kTrap;
+    static_assert(kTT * kChunkLanes % kThreads == 0 && kTT * kCPW % kThreads == 0, "tile shape");
+
+    __shared__ float4 s_bcb[2][kTT][kChunkLanes];  // (B re, B im, C re, C im), double-buffered by tile
+    __shared__ float2 s_dw[kTT][kCPW];         // (delta, w) per step and channel
+    __shared__ float s_e[kTT][kCPW];           // e per step and channel (output's u term)
+    __shared__ uint32_t s_raw[3 * RawRows<T>::kArrayDw];  // raw u, delta, lambda rows
+    __shared__ float s_k[RawRows<T>::kKInstr * 64];        // K_t rows
+    __shared__ float s_sdt[kWaves][kCPW];                   // sum of delta over each wave's steps
+    // pass-1 wave aggregates (P, h); once the incoming states are formed the
+    // same space holds pass 2's y partials (kWaves x 8 steps x 64 lanes)
+    constexpr int kAggF2 = kWaves * 64 * kNPL;
+    static_assert(2 * kAggF2 * 2 == kWaves * 8 * 64, "aggregate and partial buffers share space");
+    __shared__ alignas(16) float s_x[kWaves * 8 * 64];
+    float2* s_aggP = reinterpret_cast<float2*>(s_x);           // [wave][lane][j]
+    float2* s_aggH = reinterpret_cast<float2*>(s_x) + kAggF2;  // [wave][lane][j]
+    float* s_red = s_x;                                         // [wave][step % 8][lane]
+    __shared__ float2 s_carry[kWaves][64][kNPL];  // incoming state of each wave's steps
+    __shared__ uint32_t s_ticket;
+
+    const T* u = static_cast<const T*>(p.u);
+    const T* delta = static_cast<const T*>(p.delta);
+    const T* theta = static_cast<const T*>(p.theta);
+    const T* lambda = static_cast<const T*>(p.lambda);
+    T* y = static_cast<T*>(p.y);
+    char* ws = static_cast<char*>(p.workspace);
+    uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws);
+    uint32_t* flags = reinterpret_cast<uint32_t*>(ws + lay.off_flags);
+    float2* payload = reinterpret_cast<float2*>(ws + lay.off_payload);
+    const float4* bc = reinterpret_cast<const float4*>(ws + lay.off_bc);
+    const float* kt = reinterpret_cast<const float*>(ws + lay.off_k);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int lane = tid & 63;
+    const int c = lane / kLPC;
+    const int pr = lane % kLPC;
+    const int s0 = wave * kTW;  // this wave's first step within a tile
+    const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
+    const int slot = blockIdx.x % kSlots;
+    const uint32_t per_tt = static_cast<uint32_t>(lay.slot_groups[slot]);
+    const uint32_t slot_tiles = per_tt * static_cast<uint32_t>(lay.n_tt);
+
+    TileRegs<T> r;  // one tile's register-carried loads
+
+    // ---- prologue: first ticket, its loads, the ticket after it
+    if (tid == 0) s_ticket = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    uint32_t cur = __builtin_amdgcn_readfirstlane(s_ticket);
+    if (cur >= slot_tiles) return;
+    // The ticket after the current one is requested by lane 0 of wave 1 (wave 0
+    // is busy with the look-back then) and published through LDS a tile later.
+    uint32_t next_ticket = 0;  // thread kTicketThread only
+    constexpr int kTicketThread = 64;
+    if (tid == kTicketThread)
+        next_ticket = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    Tile tc = decode_tile(cur, per_tt, slot, lay, D);
+    int buf = 0;
+    issue_tile<T, DISC, CPLX>(r, p, lay, tc, tid, c, pr, s0, wave, &s_bcb[0][0][0], s_raw, s_k);
+
+    for (;;) {
+        // ---- 1. stage the current tile
+        wait_stores();  // this wave's DMA (B/C rows, raw rows) has landed in LDS (vmcnt(0))
+        __syncthreads();
+        commit_tile<T, DISC>(r, p, lay, tc, tid, s_raw, s_k, s_dw, s_e);
+        __syncthreads();
+        if constexpr (kFast) sum_deltas(tid, s_dw, s_sdt);  // read after the pass-1 barrier
+        float4 (*s_bc)[kChunkLanes] = s_bcb[buf];
+
+        // ---- 2. pass 1: discretise, keep alpha in registers, local aggregate
+        const bool cok = c < tc.nch;
+        const int64_t d = tc.d0 + (cok ? c : 0);
+        bool nok[kNPL];
+        float a_prep[kNPL], a_raw[kNPL], inv_a[kNPL];
+#pragma unroll
+        for (int s = 0; s < kTW; ++s) r.th.pin(s);
+#pragma unroll
+        for (int j = 0; j < kNPL; ++j) {
+            nok[j] = cok && pr * kNPL + j < N;
+            pin(r.a_ld[j]);
+            a_raw[j] = r.a_ld[j];
+            a_prep[j] = M::prep_A(a_raw[j]);
+            inv_a[j] = a_raw[j] != 0.f ? 1.f / a_raw[j] : 0.f;
+        }
+        float al_r[kTW][kNPL], al_i[kTW][kNPL];  // alpha_t (al_i holds b_t on the real path)
+        Cx gl[kNPL], P[kNPL];
+        float sth[kNPL];
+#pragma unroll
+        for (int j = 0; j < kNPL; ++j) {
+            gl[j] = {0.f, 0.f};
+            P[j] = {1.f, 0.f};
+            sth[j] = 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < kTW; ++s) {
+            const float2 tc4 = s_dw[s0 + s][c];  // (delta, w)
+#pragma unroll
+            for (int j = 0; j < kNPL; ++j) {
+                const float4 bcq = s_bc[s0 + s][pr * kNPL + j];
+                const float rho = M::exp_dA(tc4.x, a_prep[j]);
+                if constexpr (CPLX) {
+                    const float thv = r.th.get(s, j);
+                    float sn, cs;
+                    M::sincos(thv, &sn, &cs);
+                    const Cx al = {rho * cs, rho * sn};
+                    al_r[s][j] = al.re;
+                    al_i[s][j] = al.im;
+                    gl[j] = cfma(al, gl[j], Cx{tc4.y * bcq.x, tc4.y * bcq.y});
+                    if constexpr (kFast) sth[j] += thv;
+                    else P[j] = cmul(al, P[j]);
+                } else {
+                    float bt;
+                    if constexpr (kZ) bt = zoh_gamma(tc4.x, a_raw[j], inv_a[j]) * tc4.y * bcq.x;
+                    else bt = tc4.y * bcq.x;
+                    al_r[s][j] = rho;
+                    al_i[s][j] = bt;
+                    gl[j].re = rho * gl[j].re + bt;
+                    if constexpr (!kFast) P[j].re = rho * P[j].re;
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kNPL; ++j) {
+            // fast path: publish sum(theta); wave 0 forms prod alpha from it
+            if constexpr (kFast) P[j] = {sth[j], 0.f};
+            s_aggP[(wave * 64 + lane) * kNPL + j] = to_f2(P[j]);
+            s_aggH[(wave * 64 + lane) * kNPL + j] = to_f2(gl[j]);
+        }
+        if (tid == kTicketThread) s_ticket = next_ticket;
+        __syncthreads();
+
+        // ---- 3/4. wave 0: tile aggregate, look-back, inclusive state, then its
+        // share of the next tile's loads.  Waves 1-3: the ticket after next and
+        // their loads of the next tile right away.  (vmcnt retires in order, so
+        // wave 0 must not have loads in flight while it waits on its
+        // look-back traffic.)
+        const uint32_t nx = __builtin_amdgcn_readfirstlane(s_ticket);
+        const bool has_next = nx < slot_tiles;
+        const Tile tn = has_next ? decode_tile(nx, per_tt, slot, lay, D) : tc;
+        if (wave != 0) {
+            if (tid == kTicketThread)
+                next_ticket = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (has_next) issue_tile<T, DISC, CPLX>(r, p, lay, tn, tid, c, pr, s0, wave, &s_bcb[buf ^ 1][0][0], s_raw, s_k);
+        }
+        if (wave == 0) {
+            float2* pay_base = payload + (tc.g * lay.n_tt) * kPayloadF2;
+            uint32_t* flag = flags + tc.g * lay.n_tt;
+            const int64_t tt = tc.tt;
+            Cx Pt[kNPL], Ht[kNPL], carry[kNPL];
+#pragma unroll
+            for (int j = 0; j < kNPL; ++j) {
+                Pt[j] = {1.f, 0.f};
+                Ht[j] = {0.f, 0.f};
+                carry[j] = {0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    float2* pw = &s_aggP[(w * 64 + lane) * kNPL + j];
+                    Cx Pw = to_cx(*pw);
+                    if constexpr (kFast) {  // prod alpha = exp(A sum delta) e^{i sum theta}
+                        const float mod = M::exp_dA(s_sdt[w][c], a_prep[j]);
+                        if constexpr (CPLX) {
+                            float sn, cs;
+                            M::sincos(Pw.re, &sn, &cs);
+                            Pw = {mod * cs, mod * sn};
+                        } else {
+                            Pw = {mod, 0.f};
+                        }
+                        *pw = to_f2(Pw);  // kept for the incoming states below
+                    }
+                    Ht[j] = cfma(Pw, Ht[j], to_cx(s_aggH[(w * 64 + lane) * kNPL + j]));
+                    Pt[j] = cmul(Pw, Pt[j]);
+                }
+            }
+            float2* mine = pay_base + tt * kPayloadF2;
+            if (tt > 0) {
+#pragma unroll
+                for (int j = 0; j < kNPL; ++j) {
+                    st_agent(mine + (0 * 64 + lane) * kNPL + j, to_f2(Pt[j]));
+                    st_agent(mine + (1 * 64 + lane) * kNPL + j, to_f2(Ht[j]));
+                }
+                wait_stores();
+                if (lane == 0)
+                    __hip_atomic_store(&flag[tt], kFlagAggregate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+                Cx Pacc[kNPL], Hacc[kNPL];
+#pragma unroll
+                for (int j = 0; j < kNPL; ++j) {
+                    Pacc[j] = {1.f, 0.f};
+                    Hacc[j] = {0.f, 0.f};
+                }
+                for (int64_t k = tt - 1; k >= 0; --k) {
+                    uint32_t f;
+                    for (;;) {
+                        f = __hip_atomic_load(&flag[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        f = __builtin_amdgcn_readfirstlane(f);
+                        if (f != kFlagEmpty) break;
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                    const float2* pk = pay_base + k * kPayloadF2;
+                    if (f == kFlagInclusive) {
+#pragma unroll
+                        for (int j = 0; j < kNPL; ++j)
+                            carry[j] = cfma(Pacc[j], to_cx(ld_agent(pk + (2 * 64 + lane) * kNPL + j)), Hacc[j]);
+                        break;
+                    }
+#pragma unroll
+                    for (int j = 0; j < kNPL; ++j) {
+                        const Cx Pk = to_cx(ld_agent(pk + (0 * 64 + lane) * kNPL + j));
+                        const Cx Hk = to_cx(ld_agent(pk + (1 * 64 + lane) * kNPL + j));
+                        Hacc[j] = cfma(Pacc[j], Hk, Hacc[j]);
+                        Pacc[j] = cmul(Pacc[j], Pk);
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kNPL; ++j) {
+                const Cx inc = cfma(Pt[j], carry[j], Ht[j]);
+                st_agent(mine + (2 * 64 + lane) * kNPL + j, to_f2(inc));
+                Cx hin = carry[j];  // incoming state of each wave's steps
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    s_carry[w][lane][j] = to_f2(hin);
+                    hin = cfma(to_cx(s_aggP[(w * 64 + lane) * kNPL + j]), hin,
+                               to_cx(s_aggH[(w * 64 + lane) * kNPL + j]));
+                }
+                if (tt == lay.n_tt - 1 && p.h_last && nok[j]) {
+                    const int64_t hs = (tc.b * D + d) * N + pr * kNPL + j;
+                    if constexpr (CPLX) {
+                        p.h_last[2 * hs] = inc.re;
+                        p.h_last[2 * hs + 1] = inc.im;
+                    } else {
+                        p.h_last[hs] = inc.re;
+                    }
+                }
+            }
+            wait_stores();
+            if (lane == 0)
+                __hip_atomic_store(&flag[tt], kFlagInclusive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (has_next) issue_tile<T, DISC, CPLX>(r, p, lay, tn, tid, c, pr, s0, wave, &s_bcb[buf ^ 1][0][0], s_raw, s_k);
+        }
+        __syncthreads();
+
+        // ---- 5. incoming state of this wave's steps (formed by wave 0)
+        Cx h[kNPL];
+#pragma unroll
+        for (int j = 0; j < kNPL; ++j) h[j] = to_cx(s_carry[wave][lane][j]);
+
+        // ---- 6. pass 2: recurrence from the incoming state, outputs (y through
+        // a resource covering this wave's valid steps; stores past it drop)
+        {
+            const int64_t yw0 = tc.t0 + s0;
+            const int64_t ysteps = L - yw0 < 0 ? 0 : (L - yw0 > kTW ? kTW : L - yw0);
+            const uint32_t y_row = static_cast<uint32_t>(D) * es;
+            const rsrc_t rY = make_rsrc(y + (tc.b * L + (ysteps ? yw0 : 0)) * D + tc.d0,
+                                        ysteps ? static_cast<uint32_t>((ysteps - 1) * D + tc.nch) * es : 0u);
+            const uint32_t y_lane = cok ? static_cast<uint32_t>(c) * es : kOutOfRange;
+#pragma unroll
+            for (int s = 0; s < kTW; ++s) {
+                const float2 tc4 = s_dw[s0 + s][c];  // (delta, w)
+                float part = 0.f;
+#pragma unroll
+                for (int j = 0; j < kNPL; ++j) {
+                    const float4 bcq = s_bc[s0 + s][pr * kNPL + j];
+                    if constexpr (CPLX) {
+                        h[j] = cfma(Cx{al_r[s][j], al_i[s][j]}, h[j], Cx{tc4.y * bcq.x, tc4.y * bcq.y});
+                        part += bcq.z * h[j].re - bcq.w * h[j].im;  // Re(C h)
+                    } else {
+                        h[j].re = al_r[s][j] * h[j].re + al_i[s][j];
+                        part += bcq.z * h[j].re;
+                    }
+                }
+                s_red[(wave * 8 + (s & 7)) * 64 + lane] = part;
+                if ((s & 7) == 7) {
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    const int sb = s - 7 + pr;  // step this lane finishes
+                    const float4 v0 = *reinterpret_cast<const float4*>(&s_red[(wave * 8 + pr) * 64 + c * kLPC]);
+                    const float4 v1 = *reinterpret_cast<const float4*>(&s_red[(wave * 8 + pr) * 64 + c * kLPC + 4]);
+                    const float yv =
+                        ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w)) + s_e[s0 + sb][c];
+                    BE::store(rY, y_lane + static_cast<uint32_t>(sb) * y_row, yv);
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                }
+            }
+        }
+        __syncthreads();  // LDS is rewritten by the next tile
+        if (!has_next) break;
+        tc = tn;
+        buf ^= 1;
+    }
+}
+
+// Resident workgroups of `kernel` per CU, queried once per instantiation.
+template <typename K>
+int chunk_blocks_per_cu(K kernel) {
+    static int cached = 0;
+    if (cached == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, chunk::kThreads, 0) != hipSuccess || n < 1) n = 1;
+        cached = n;
+    }
+    return cached;
+}
+
+template <typename T, int DISC, bool CPLX>
+hipError_t launch_chunk_pair(const ChunkParams& p, const ChunkLayout& lay, dim3 pgrid, hipStream_t s) {
+    using namespace chunk;
+    auto kernel = chunk_scan_kernel<T, DISC, CPLX>;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t resident = int64_t(chunk_blocks_per_cu(kernel)) * cus;
+    int64_t grid = int64_t(kSlots) * lay.max_slot_tiles;
+    const int64_t cap = (resident / kSlots) * kSlots;
+    if (cap >= kSlots && grid > cap) grid = cap;
+    hipLaunchKernelGGL((chunk_prep_kernel<T, CPLX, DISC == kTrap>), pgrid, dim3(256), 0, s, p, lay);
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, p, lay);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- launch
 
 template <typename T>
-int launch_chunked(int, bool, const ChunkParams&, hipStream_t) { return SSM_ERR_UNSUPPORTED; }
+int launch_chunked(int disc, bool cplx, const ChunkParams& p, hipStream_t s) {
+    using namespace chunk;
+    const ChunkLayout lay = chunk_layout(p.batch, p.seqlen, p.dim);
+    if (int64_t(kSlots) * lay.max_slot_tiles > UINT32_MAX || lay.groups > INT32_MAX)
+        return 2;  // SSM_ERR_UNSUPPORTED: tickets and group indices are 32-bit
+    // buffer windows and per-lane byte offsets are 32-bit: keep every window
+    // (and an out-of-range lane offset plus a window) below 2^31
+    const uint64_t es = sizeof(T), lim = uint64_t(1) << 30;
+    if (uint64_t(p.dim) * p.dstate * es * kTW > lim || uint64_t(kTT + 2) * p.dim * es > lim ||
+        uint64_t(p.dim) * p.dstate * 4 > lim)
+        return 2;
+    const int64_t items = p.batch * lay.l_pad * kChunkLanes;
+    const int64_t nfl = lay.groups * lay.n_tt;
+    int64_t pblocks = ((items > nfl ? items : nfl) + 255) / 256;
+    if (pblocks > 16384) pblocks = 16384;
+    const dim3 pg(static_cast<unsigned>(pblocks));
+    hipError_t e;
+    if (cplx) {
+        e = disc == kEuler ? launch_chunk_pair<T, kEuler, true>(p, lay, pg, s)
+                           : launch_chunk_pair<T, kTrap, true>(p, lay, pg, s);
+    } else {
+        e = disc == kZOH     ? launch_chunk_pair<T, kZOH, false>(p, lay, pg, s)
+            : disc == kEuler ? launch_chunk_pair<T, kEuler, false>(p, lay, pg, s)
+                             : launch_chunk_pair<T, kTrap, false>(p, lay, pg, s);
+    }
+    return e == hipSuccess ? 0 : -static_cast<int>(e);
+}
 
 }  // namespace ssm
