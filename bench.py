@@ -118,6 +118,25 @@ def cpu_baseline(inputs, w, y_gpu, target_s: float):
     }
 
 
+def copy_calibration(torch, dev, nbytes: int, steps: int, warmup: int):
+    """A plain copy of known size: reads and writes `nbytes` per launch."""
+    n = (nbytes + 15) // 16 * 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": steps + warmup,
+                      "ms_per_copy": ms, "GBps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +146,9 @@ def main():
     ap.add_argument("--algo", default="auto", choices=["auto", "sequential", "chunked"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of the scan, time a plain device-to-device copy of BYTES bytes "
+                         "(the known-size kernel that HBM byte counters are scaled against)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -142,6 +164,9 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        copy_calibration(torch, dev, args.copy_calibration, args.steps, args.warmup)
+        return
     log(f"generating {w.name} on {torch.cuda.get_device_name(dev)}")
     inputs = make_inputs(w, device=dev)
     torch.cuda.synchronize()
