@@ -65,7 +65,10 @@ constexpr int kTW = 24;            // steps per wave (a multiple of 8)
 constexpr int kTT = kWaves * kTW;  // steps per tile
 constexpr int kThreads = kWaves * 64;
 constexpr int kSlots = 8;          // ticket counters (one per XCD)
+constexpr int kDmaWaves = kWaves - 1;  // waves 1.. issue the tile's LDS copies; wave 0 looks back
 constexpr int kPayloadF2 = 3 * 64 * kNPL;  // float2 per tile: aggregate P, aggregate h, inclusive h
+constexpr int kLookWindow = 16;            // predecessor flags read at once by the look-back
+constexpr int kLookBatch = 1;              // predecessor payloads loaded at once
 enum : uint32_t { kFlagEmpty = 0, kFlagAggregate = 1, kFlagInclusive = 2 };
 }  // namespace chunk
 
@@ -83,7 +86,8 @@ struct ChunkParams {
     int64_t batch, seqlen, dim, dstate;
     void* workspace;
     int32_t theta_pairs;  // 1: dstate even and theta aligned to two elements
-    int32_t rows_dma;     // 1: dim even and u, delta, lambda 4-byte aligned (rows move as dwords)
+    int32_t rows_dma;     // 1: dim * element size a multiple of 16 and u, delta, lambda 16-byte aligned
+                          //    (rows move by DMA in 16-byte chunks)
 };
 
 struct ChunkLayout {
@@ -139,13 +143,20 @@ inline bool chunked_preferred(int64_t, int64_t, int64_t) { return true; }
 
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-__device__ __forceinline__ void st_agent(float2* p, float2 v) {
-    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+// Agent-scope relaxed 8-byte accesses at a wave-uniform base plus a 32-bit
+// per-lane byte offset (so the address is one scalar base and one VGPR).
+__device__ __forceinline__ void st_agent(float2* base, uint32_t off, float2 v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(base) + off), __builtin_bit_cast(uint64_t, v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float2 ld_agent(const float2* p) {
-    return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT));
+__device__ __forceinline__ float2 ld_agent(const float2* base, uint32_t off) {
+    return __builtin_bit_cast(
+        float2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(reinterpret_cast<const char*>(base) + off),
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// byte offset of (section, lane, state j) in a tile's payload
+__device__ __forceinline__ uint32_t pay_off(int section, int lane, int j) {
+    return static_cast<uint32_t>(((section * 64 + lane) * chunk::kNPL + j) * 8);
 }
 
 struct Cx {
@@ -208,14 +219,15 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkParams p, ChunkLay
 
 // ---------------------------------------------------------------- main kernel
 
-// Coordinates of one tile (uniform across the workgroup).
+// Coordinates of one tile (uniform across the workgroup).  32-bit fields keep
+// the scalar registers a persistent loop carries few.
 struct Tile {
-    int64_t tt;   // tile index along the sequence
-    int64_t g;    // channel group
-    int64_t b;    // batch row
-    int64_t d0;   // first channel
-    int64_t t0;   // first step
+    uint32_t tt;  // tile index along the sequence
+    uint32_t g;   // channel group
+    uint32_t b;   // batch row
+    uint32_t d0;  // first channel
     int nch;      // channels of the group that exist (<= kCPW)
+    __device__ __forceinline__ int64_t t0() const { return int64_t(tt) * chunk::kTT; }  // first step
 };
 
 __device__ __forceinline__ Tile decode_tile(uint32_t local, uint32_t per_tt, int slot, const ChunkLayout& lay,
@@ -228,8 +240,7 @@ __device__ __forceinline__ Tile decode_tile(uint32_t local, uint32_t per_tt, int
     t.tt = tt;
     t.g = g;
     t.b = g / ndb;
-    t.d0 = int64_t(g % ndb) * kCPW;
-    t.t0 = int64_t(tt) * kTT;
+    t.d0 = (g % ndb) * kCPW;
     t.nch = static_cast<int>(D - t.d0 < kCPW ? D - t.d0 : kCPW);
     return t;
 }
@@ -267,36 +278,31 @@ struct TileRegs {
 // Raw per-step rows in LDS, exactly as stored in memory: for each of the
 // arrays u, delta, lambda, rows t0 .. t0 + kTT (one row past the tile, for
 // the trapezoid's next-step terms) of the group's kCPW channels.  They arrive
-// by buffer-to-LDS DMA in dwords, 64 per wave instruction.
+// by buffer-to-LDS DMA in 16-byte chunks, 64 per wave instruction.
 template <typename T>
 struct RawRows {
-    static constexpr int kRowDw = chunk::kCPW * int(sizeof(T)) / 4;       // dwords per row
-    static constexpr int kInstr = ((chunk::kTT + 1) * kRowDw + 63) / 64;  // DMA instructions per array
-    static constexpr int kArrayDw = kInstr * 64;                          // padded array size
-    static constexpr int kKInstr = (chunk::kTT + 63) / 64;                // K_t rows (fp32)
+    static constexpr int kRowDw = chunk::kCPW * int(sizeof(T)) / 4;   // dwords per row
+    static constexpr int kChunks = (chunk::kTT + 1) * kRowDw / 4;     // 16-byte chunks per array
+    static constexpr int kInstr = (kChunks + 63) / 64;                // DMA instructions per array
+    static constexpr int kArrayDw = kChunks * 4;                      // array size in dwords
+    static constexpr int kKChunks = chunk::kTT / 4;                   // K_t rows (fp32) in chunks
+    static_assert(kRowDw % 4 == 0 && chunk::kTT % 4 == 0 && kKChunks <= 64, "chunked rows");
 };
 
-// Issue every global load of tile `t`: A and theta into registers (theta as
-// stored, decoded in pass 1), B/C rows and the raw per-step rows (and K_t)
-// into LDS by DMA.  Buffer resources cover exactly the valid data, so lanes
-// and steps outside read 0 and no load needs a branch or a mask.  With
-// p.rows_dma == 0 (odd D or unaligned pointers) the raw rows are instead
-// loaded element by element in commit_tile().
-template <typename T, int DISC, bool CPLX>
-__device__ __forceinline__ void issue_tile(TileRegs<T>& r, const ChunkParams& p, const ChunkLayout& lay,
-                                           const Tile& t, int tid, int c, int pr, int s0, int wave,
-                                           float4* s_bc_dst, uint32_t* s_raw, float* s_k) {
+// Issue the loads a wave keeps in registers for tile `t`: A of its states,
+// D of its staging channel and theta of its states over its steps (theta as
+// stored, decoded in pass 1).  Buffer resources cover exactly the valid data,
+// so lanes and steps outside read 0 and no load needs a branch or a mask.
+// At least kOwnLoadsMin vector-memory instructions are issued.
+template <typename T, bool CPLX>
+__device__ __forceinline__ void issue_own(TileRegs<T>& r, const ChunkParams& p, const Tile& t, int tid, int c,
+                                          int pr, int s0) {
     using namespace chunk;
     using BE = Buf<T>;
-    using RR = RawRows<T>;
     constexpr uint32_t es = BE::kSize;
     constexpr bool kFast = std::is_same_v<T, uint16_t>;
-    constexpr bool kTR = DISC == kTrap;
     const T* theta = static_cast<const T*>(p.theta);
-    const float4* bc = reinterpret_cast<const float4*>(static_cast<const char*>(p.workspace) + lay.off_bc);
-    const float* kt = reinterpret_cast<const float*>(static_cast<const char*>(p.workspace) + lay.off_k);
     const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
-    const int lane = tid & 63;
     const bool cok = c < t.nch;
     {
         const rsrc_t rA = make_rsrc(p.A + t.d0 * N, static_cast<uint32_t>(t.nch * N * 4));
@@ -309,7 +315,7 @@ __device__ __forceinline__ void issue_tile(TileRegs<T>& r, const ChunkParams& p,
         r.dskip = Buf<float>::load(rDs, static_cast<uint32_t>(tid % kCPW) * 4);
     }
     if constexpr (CPLX) {
-        const int64_t ws0 = t.t0 + s0;  // this wave's first step
+        const int64_t ws0 = t.t0() + s0;  // this wave's first step
         const int64_t vsteps = L - ws0 < 0 ? 0 : (L - ws0 > kTW ? kTW : L - ws0);
         const uint32_t row = static_cast<uint32_t>(D * N) * es;
         const rsrc_t rT = make_rsrc(theta + ((t.b * L + (vsteps ? ws0 : 0)) * D + t.d0) * N,
@@ -337,45 +343,68 @@ __device__ __forceinline__ void issue_tile(TileRegs<T>& r, const ChunkParams& p,
             }
         }
     }
-    // B/C rows: wave w's 64 lanes fill 64 consecutive float4 entries per instruction
+}
+
+// Lower bound on the vector-memory instructions issue_own() issues (theta
+// rows for a complex state, else the D load).
+template <bool CPLX>
+constexpr int kOwnLoadsMin = CPLX ? chunk::kTW : 1;
+
+// Issue one DMA wave's share (dw in [0, kDmaWaves)) of tile `t`'s
+// buffer-to-LDS copies: the B/C rows and, with p.rows_dma, the raw per-step
+// rows and K_t.  With p.rows_dma == 0 (other D or unaligned pointers) the raw
+// rows are instead loaded element by element in commit_tile().
+template <typename T, int DISC>
+__device__ __forceinline__ void issue_dma(const ChunkParams& p, const ChunkLayout& lay, const Tile& t, int lane,
+                                          int dw, float4* s_bc_dst, uint32_t* s_raw, float* s_k) {
+    using namespace chunk;
+    using RR = RawRows<T>;
+    constexpr uint32_t es = sizeof(T);
+    constexpr bool kTR = DISC == kTrap;
+    const float4* bc = reinterpret_cast<const float4*>(static_cast<const char*>(p.workspace) + lay.off_bc);
+    const float* kt = reinterpret_cast<const float*>(static_cast<const char*>(p.workspace) + lay.off_k);
+    const int64_t L = p.seqlen, D = p.dim;
+    // B/C rows: each instruction fills 64 consecutive float4 entries
     {
-        const float4* src = bc + (t.b * lay.l_pad + t.t0) * kChunkLanes;
+        const float4* src = bc + (t.b * lay.l_pad + t.t0()) * kChunkLanes;
+        constexpr int kInstr = kTT * kChunkLanes / 64;
+        static_assert(kInstr % kDmaWaves == 0, "B/C rows split evenly over the DMA waves");
 #pragma unroll
-        for (int k = 0; k < kTT * kChunkLanes / kThreads; ++k) {
-            const int i0 = k * kThreads + wave * 64;
+        for (int k = 0; k < kInstr / kDmaWaves; ++k) {
+            const int i0 = (k * kDmaWaves + dw) * 64;
             __builtin_amdgcn_global_load_lds(src + i0 + lane,
                                              (__attribute__((address_space(3))) void*)(s_bc_dst + i0), 16, 0, 0);
         }
     }
     if (p.rows_dma) {
-        // rows t0 .. t0 + rows - 1 exist (rows >= 1); D even, so every row of
-        // the group starts on a dword and holds whole dwords
-        const int64_t rows = L - t.t0 > kTT + 1 ? kTT + 1 : L - t.t0;
+        // rows t0 .. t0 + rows - 1 exist (rows >= 1).  D * sizeof(T) and the
+        // pointers are multiples of 16 bytes, so every 16-byte chunk of a row
+        // lies wholly inside or wholly outside the resource's window.
+        const int64_t rows = L - t.t0() > kTT + 1 ? kTT + 1 : L - t.t0();
         const uint32_t bytes = static_cast<uint32_t>((rows - 1) * D + t.nch) * es;
-        const int64_t base = (t.b * L + t.t0) * D + t.d0;
+        const int64_t base = (t.b * L + t.t0()) * D + t.d0;
         const T* arrs[3] = {static_cast<const T*>(p.u), static_cast<const T*>(p.delta),
                             static_cast<const T*>(p.lambda)};
         constexpr int kArrays = kTR ? 3 : 2;
-        constexpr int kTotal = kArrays * RR::kInstr + (kTR ? RR::kKInstr : 0);
-        const rsrc_t rK = make_rsrc(kt + t.b * lay.l_pad + t.t0, kTT * 4);
+        constexpr int kTotal = kArrays * RR::kInstr + (kTR ? 1 : 0);
+        constexpr int kRowChunks = RR::kRowDw / 4;
 #pragma unroll
-        for (int q = 0; q < (kTotal + kWaves - 1) / kWaves; ++q) {
-            const int g = q * kWaves + wave;  // this wave's DMA instruction (uniform)
+        for (int q = 0; q < (kTotal + kDmaWaves - 1) / kDmaWaves; ++q) {
+            const int g = q * kDmaWaves + dw;  // this wave's DMA instruction (uniform)
             if (g < kArrays * RR::kInstr) {
                 const int ar = g / RR::kInstr, iq = g % RR::kInstr;
-                const int f = iq * 64 + lane;  // dword of the padded array
-                const int rw = f / RR::kRowDw, dw = f % RR::kRowDw;
-                const uint32_t voff = rw <= kTT ? static_cast<uint32_t>(rw * D) * es + dw * 4 : kOutOfRange;
+                const int f = iq * 64 + lane;  // chunk of the array
+                const int rw = f / kRowChunks, part = f % kRowChunks;
                 const rsrc_t rs = make_rsrc(arrs[ar] + base, bytes);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void*)(s_raw + ar * RR::kArrayDw + iq * 64), 4, voff, 0, 0,
-                    0);
+                if (f < RR::kChunks)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rs, (__attribute__((address_space(3))) void*)(s_raw + ar * RR::kArrayDw + iq * 256), 16,
+                        static_cast<uint32_t>(rw * D) * es + part * 16, 0, 0, 0);
             } else if (g < kTotal) {
-                const int iq = g - kArrays * RR::kInstr;
-                const int f = iq * 64 + lane;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rK, (__attribute__((address_space(3))) void*)(s_k + iq * 64), 4,
-                    f < kTT ? static_cast<uint32_t>(f) * 4 : kOutOfRange, 0, 0, 0);
+                const rsrc_t rK = make_rsrc(kt + t.b * lay.l_pad + t.t0(), kTT * 4);
+                if (lane < RR::kKChunks)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (__attribute__((address_space(3))) void*)(s_k), 16,
+                                                             static_cast<uint32_t>(lane) * 16, 0, 0, 0);
             }
         }
     }
@@ -401,9 +430,9 @@ __device__ __forceinline__ void commit_tile(const TileRegs<T>& r, const ChunkPar
     constexpr int kArrayEl = RR::kArrayDw * 4 / int(sizeof(T));
     const int cc = tid % kCPW;
     if (!p.rows_dma) {
-        const int64_t rows = L - t.t0 > kTT + 1 ? kTT + 1 : L - t.t0;
+        const int64_t rows = L - t.t0() > kTT + 1 ? kTT + 1 : L - t.t0();
         const uint32_t bytes = static_cast<uint32_t>((rows - 1) * D + t.nch) * es;
-        const int64_t base = (t.b * L + t.t0) * D + t.d0;
+        const int64_t base = (t.b * L + t.t0()) * D + t.d0;
         const T* arrs[3] = {static_cast<const T*>(p.u), static_cast<const T*>(p.delta),
                             static_cast<const T*>(p.lambda)};
         constexpr int kArrays = kTR ? 3 : 2;
@@ -416,7 +445,7 @@ __device__ __forceinline__ void commit_tile(const TileRegs<T>& r, const ChunkPar
                 raw[ar * kArrayEl + i] = static_cast<RawT>(BE::load_raw(make_rsrc(arrs[ar] + base, bytes), off));
         }
         if constexpr (kTR)
-            for (int i = tid; i < kTT; i += kThreads) s_k[i] = kt[t.b * lay.l_pad + t.t0 + i];
+            for (int i = tid; i < kTT; i += kThreads) s_k[i] = kt[t.b * lay.l_pad + t.t0() + i];
         __syncthreads();
     }
     float dsk = r.dskip;
@@ -425,7 +454,7 @@ __device__ __forceinline__ void commit_tile(const TileRegs<T>& r, const ChunkPar
     for (int k = 0; k < kTT * kCPW / kThreads; ++k) {
         const int i = tid + k * kThreads;
         const int st = i / kCPW;
-        const bool ok = t.t0 + st < L && cc < t.nch;
+        const bool ok = t.t0() + st < L && cc < t.nch;
         const float x = BE::widen(raw[0 * kArrayEl + i]);
         const float dt = BE::widen(raw[1 * kArrayEl + i]);
         float w, e;
@@ -436,7 +465,7 @@ __device__ __forceinline__ void commit_tile(const TileRegs<T>& r, const ChunkPar
             w = dt * x;
             e = dsk * x;
         } else {
-            const bool okn = t.t0 + st + 1 < L;
+            const bool okn = t.t0() + st + 1 < L;
             const float lam = BE::widen(raw[2 * kArrayEl + i]);
             const float dn = BE::widen(raw[1 * kArrayEl + i + kCPW]);
             const float ln = BE::widen(raw[2 * kArrayEl + i + kCPW]);
@@ -449,16 +478,107 @@ __device__ __forceinline__ void commit_tile(const TileRegs<T>& r, const ChunkPar
     }
 }
 
-// Sum of delta over each wave's steps, per channel (after commit_tile and a
-// barrier): one thread per (wave, channel).
-__device__ __forceinline__ void sum_deltas(int tid, const float2 (*s_dw)[chunk::kCPW], float (*s_sdt)[chunk::kCPW]) {
+// Wait until at most N vector-memory instructions of this wave are
+// outstanding.  vmcnt retires in issue order, so this waits for everything
+// issued before the last N.  The empty asm statements keep the compiler from
+// moving memory operations across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm_below() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+    asm volatile("" ::: "memory");
+}
+
+// Tile aggregate (P, h) of one lane's states from the waves' aggregates in
+// LDS, folded in step order: (P, h) <- (P_w P, P_w h + h_w).
+__device__ __forceinline__ void tile_aggregate(const float2* s_aggP, const float2* s_aggH, int lane, Cx* Pt,
+                                               Cx* Ht) {
     using namespace chunk;
-    if (tid < kWaves * kCPW) {
-        const int w = tid / kCPW, ch = tid % kCPW;
-        float acc = 0.f;
 #pragma unroll
-        for (int s = 0; s < kTW; ++s) acc += s_dw[w * kTW + s][ch].x;
-        s_sdt[w][ch] = acc;
+    for (int j = 0; j < kNPL; ++j) {
+        Pt[j] = {1.f, 0.f};
+        Ht[j] = {0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const Cx Pw = to_cx(s_aggP[(w * 64 + lane) * kNPL + j]);
+            Ht[j] = cfma(Pw, Ht[j], to_cx(s_aggH[(w * 64 + lane) * kNPL + j]));
+            Pt[j] = cmul(Pw, Pt[j]);
+        }
+    }
+}
+
+// Carry-in (state after the last step before tile tt) of one chain, by one
+// wave: read the flags of up to kLookWindow predecessors at once (one lane
+// each), fold the aggregates of those that precede the nearest inclusive
+// state (nearest first), then that inclusive state.  An empty flag before the
+// nearest inclusive state stops the fold there; the rest is retried after a
+// short sleep.  Tile 0 of a chain always publishes an inclusive state and
+// every predecessor belongs to a running workgroup (see the kernel), so the
+// loop ends.
+__device__ __forceinline__ void look_back(const uint32_t* flag, const float2* pay_base, int64_t tt, int lane,
+                                          Cx* carry) {
+    using namespace chunk;
+    Cx Pacc[kNPL], Hacc[kNPL];
+#pragma unroll
+    for (int j = 0; j < kNPL; ++j) {
+        Pacc[j] = {1.f, 0.f};
+        Hacc[j] = {0.f, 0.f};
+    }
+    int64_t k0 = tt - 1;  // nearest predecessor not folded yet
+    for (;;) {
+        const int64_t k = k0 - lane;
+        const bool valid = lane < kLookWindow && k >= 0;
+        uint32_t f = kFlagEmpty;
+        if (valid) f = __hip_atomic_load(&flag[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t inc = __ballot(valid && f == kFlagInclusive);
+        const uint64_t emp = __ballot(valid && f == kFlagEmpty);
+        const int ni = inc ? __builtin_ctzll(inc) : 64;  // nearest inclusive
+        const int ne = emp ? __builtin_ctzll(emp) : 64;  // nearest empty
+        const bool found = ni < ne;                      // ni < kLookWindow then
+        const int nagg = found ? ni : (ne < kLookWindow ? ne : kLookWindow);
+        // fold nagg aggregates (and the inclusive state if found), loading
+        // kLookBatch predecessors' payloads at a time
+        int h0 = 0;
+        do {
+            const int nb = nagg - h0 < kLookBatch ? nagg - h0 : kLookBatch;
+            const bool last = h0 + nb == nagg;
+            float2 Pv[kLookBatch][kNPL], Hv[kLookBatch][kNPL], Iv[kNPL];
+#pragma unroll
+            for (int q = 0; q < kLookBatch; ++q) {
+                if (q < nb) {
+                    const float2* pk = pay_base + (k0 - h0 - q) * kPayloadF2;
+#pragma unroll
+                    for (int j = 0; j < kNPL; ++j) {
+                        Pv[q][j] = ld_agent(pk, pay_off(0, lane, j));
+                        Hv[q][j] = ld_agent(pk, pay_off(1, lane, j));
+                    }
+                }
+            }
+            if (last && found) {
+                const float2* pk = pay_base + (k0 - ni) * kPayloadF2;
+#pragma unroll
+                for (int j = 0; j < kNPL; ++j) Iv[j] = ld_agent(pk, pay_off(2, lane, j));
+            }
+#pragma unroll
+            for (int q = 0; q < kLookBatch; ++q) {
+                if (q < nb) {
+#pragma unroll
+                    for (int j = 0; j < kNPL; ++j) {
+                        Hacc[j] = cfma(Pacc[j], to_cx(Hv[q][j]), Hacc[j]);
+                        Pacc[j] = cmul(Pacc[j], to_cx(Pv[q][j]));
+                    }
+                }
+            }
+            if (last && found) {
+#pragma unroll
+                for (int j = 0; j < kNPL; ++j) carry[j] = cfma(Pacc[j], to_cx(Iv[j]), Hacc[j]);
+                return;
+            }
+            h0 += nb;
+        } while (h0 < nagg);
+        k0 -= nagg;
+        if (ne < kLookWindow && ne == nagg) __builtin_amdgcn_s_sleep(2);  // waiting on a predecessor
     }
 }
 
@@ -487,8 +607,7 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
     __shared__ float2 s_dw[kTT][kCPW];         // (delta, w) per step and channel
     __shared__ float s_e[kTT][kCPW];           // e per step and channel (output's u term)
     __shared__ uint32_t s_raw[3 * RawRows<T>::kArrayDw];  // raw u, delta, lambda rows
-    __shared__ float s_k[RawRows<T>::kKInstr * 64];        // K_t rows
-    __shared__ float s_sdt[kWaves][kCPW];                   // sum of delta over each wave's steps
+    __shared__ float s_k[kTT];                              // K_t rows
     // pass-1 wave aggregates (P, h); once the incoming states are formed the
     // same space holds pass 2's y partials (kWaves x 8 steps x 64 lanes)
     constexpr int kAggF2 = kWaves * 64 * kNPL;
@@ -538,15 +657,15 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
         next_ticket = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     Tile tc = decode_tile(cur, per_tt, slot, lay, D);
     int buf = 0;
-    issue_tile<T, DISC, CPLX>(r, p, lay, tc, tid, c, pr, s0, wave, &s_bcb[0][0][0], s_raw, s_k);
+    issue_own<T, CPLX>(r, p, tc, tid, c, pr, s0);
+    if (wave != 0) issue_dma<T, DISC>(p, lay, tc, lane, wave - 1, &s_bcb[0][0][0], s_raw, s_k);
 
     for (;;) {
         // ---- 1. stage the current tile
-        wait_stores();  // this wave's DMA (B/C rows, raw rows) has landed in LDS (vmcnt(0))
+        wait_stores();  // this wave's loads and DMA (B/C rows, raw rows) have landed (vmcnt(0))
         __syncthreads();
         commit_tile<T, DISC>(r, p, lay, tc, tid, s_raw, s_k, s_dw, s_e);
         __syncthreads();
-        if constexpr (kFast) sum_deltas(tid, s_dw, s_sdt);  // read after the pass-1 barrier
         float4 (*s_bc)[kChunkLanes] = s_bcb[buf];
 
         // ---- 2. pass 1: discretise, keep alpha in registers, local aggregate
@@ -566,7 +685,7 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
         }
         float al_r[kTW][kNPL], al_i[kTW][kNPL];  // alpha_t (al_i holds b_t on the real path)
         Cx gl[kNPL], P[kNPL];
-        float sth[kNPL];
+        float sth[kNPL], sdt = 0.f;
 #pragma unroll
         for (int j = 0; j < kNPL; ++j) {
             gl[j] = {0.f, 0.f};
@@ -576,6 +695,7 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
 #pragma unroll
         for (int s = 0; s < kTW; ++s) {
             const float2 tc4 = s_dw[s0 + s][c];  // (delta, w)
+            if constexpr (kFast) sdt += tc4.x;
 #pragma unroll
             for (int j = 0; j < kNPL; ++j) {
                 const float4 bcq = s_bc[s0 + s][pr * kNPL + j];
@@ -601,103 +721,69 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
                 }
             }
         }
+        // the wave's aggregate (P, h); on the fast path P = prod alpha is formed
+        // from the sums as exp(A sum delta) e^{i sum theta}
 #pragma unroll
         for (int j = 0; j < kNPL; ++j) {
-            // fast path: publish sum(theta); wave 0 forms prod alpha from it
-            if constexpr (kFast) P[j] = {sth[j], 0.f};
+            if constexpr (kFast) {
+                const float mod = M::exp_dA(sdt, a_prep[j]);
+                if constexpr (CPLX) {
+                    float sn, cs;
+                    M::sincos(sth[j], &sn, &cs);
+                    P[j] = {mod * cs, mod * sn};
+                } else {
+                    P[j] = {mod, 0.f};
+                }
+            }
             s_aggP[(wave * 64 + lane) * kNPL + j] = to_f2(P[j]);
             s_aggH[(wave * 64 + lane) * kNPL + j] = to_f2(gl[j]);
         }
         if (tid == kTicketThread) s_ticket = next_ticket;
         __syncthreads();
 
-        // ---- 3/4. wave 0: tile aggregate, look-back, inclusive state, then its
-        // share of the next tile's loads.  Waves 1-3: the ticket after next and
-        // their loads of the next tile right away.  (vmcnt retires in order, so
-        // wave 0 must not have loads in flight while it waits on its
-        // look-back traffic.)
+        // ---- 3. cross-tile carry.  Wave 0: look back, form the inclusive state
+        // and every wave's incoming state.  Wave 1: publish the tile aggregate.
+        // Waves 1..: the ticket after next, their loads of the next tile and
+        // its LDS copies.  (vmcnt retires in order, so wave 0 issues no loads
+        // before its look-back traffic has returned.)
         const uint32_t nx = __builtin_amdgcn_readfirstlane(s_ticket);
         const bool has_next = nx < slot_tiles;
         const Tile tn = has_next ? decode_tile(nx, per_tt, slot, lay, D) : tc;
+        float2* pay_base = payload + (tc.g * lay.n_tt) * kPayloadF2;
+        uint32_t* flag = flags + tc.g * lay.n_tt;
+        const int64_t tt = tc.tt;
+        float2* mine = pay_base + tt * kPayloadF2;
         if (wave != 0) {
-            if (tid == kTicketThread)
-                next_ticket = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (has_next) issue_tile<T, DISC, CPLX>(r, p, lay, tn, tid, c, pr, s0, wave, &s_bcb[buf ^ 1][0][0], s_raw, s_k);
-        }
-        if (wave == 0) {
-            float2* pay_base = payload + (tc.g * lay.n_tt) * kPayloadF2;
-            uint32_t* flag = flags + tc.g * lay.n_tt;
-            const int64_t tt = tc.tt;
-            Cx Pt[kNPL], Ht[kNPL], carry[kNPL];
-#pragma unroll
-            for (int j = 0; j < kNPL; ++j) {
-                Pt[j] = {1.f, 0.f};
-                Ht[j] = {0.f, 0.f};
-                carry[j] = {0.f, 0.f};
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) {
-                    float2* pw = &s_aggP[(w * 64 + lane) * kNPL + j];
-                    Cx Pw = to_cx(*pw);
-                    if constexpr (kFast) {  // prod alpha = exp(A sum delta) e^{i sum theta}
-                        const float mod = M::exp_dA(s_sdt[w][c], a_prep[j]);
-                        if constexpr (CPLX) {
-                            float sn, cs;
-                            M::sincos(Pw.re, &sn, &cs);
-                            Pw = {mod * cs, mod * sn};
-                        } else {
-                            Pw = {mod, 0.f};
-                        }
-                        *pw = to_f2(Pw);  // kept for the incoming states below
-                    }
-                    Ht[j] = cfma(Pw, Ht[j], to_cx(s_aggH[(w * 64 + lane) * kNPL + j]));
-                    Pt[j] = cmul(Pw, Pt[j]);
-                }
-            }
-            float2* mine = pay_base + tt * kPayloadF2;
-            if (tt > 0) {
+            if (wave == 1 && tt > 0) {
+                Cx Pt[kNPL], Ht[kNPL];
+                tile_aggregate(s_aggP, s_aggH, lane, Pt, Ht);
 #pragma unroll
                 for (int j = 0; j < kNPL; ++j) {
-                    st_agent(mine + (0 * 64 + lane) * kNPL + j, to_f2(Pt[j]));
-                    st_agent(mine + (1 * 64 + lane) * kNPL + j, to_f2(Ht[j]));
+                    st_agent(mine, pay_off(0, lane, j), to_f2(Pt[j]));
+                    st_agent(mine, pay_off(1, lane, j), to_f2(Ht[j]));
                 }
                 wait_stores();
-                if (lane == 0)
-                    __hip_atomic_store(&flag[tt], kFlagAggregate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-                Cx Pacc[kNPL], Hacc[kNPL];
-#pragma unroll
-                for (int j = 0; j < kNPL; ++j) {
-                    Pacc[j] = {1.f, 0.f};
-                    Hacc[j] = {0.f, 0.f};
-                }
-                for (int64_t k = tt - 1; k >= 0; --k) {
-                    uint32_t f;
-                    for (;;) {
-                        f = __hip_atomic_load(&flag[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        f = __builtin_amdgcn_readfirstlane(f);
-                        if (f != kFlagEmpty) break;
-                        __builtin_amdgcn_s_sleep(2);
-                    }
-                    const float2* pk = pay_base + k * kPayloadF2;
-                    if (f == kFlagInclusive) {
-#pragma unroll
-                        for (int j = 0; j < kNPL; ++j)
-                            carry[j] = cfma(Pacc[j], to_cx(ld_agent(pk + (2 * 64 + lane) * kNPL + j)), Hacc[j]);
-                        break;
-                    }
-#pragma unroll
-                    for (int j = 0; j < kNPL; ++j) {
-                        const Cx Pk = to_cx(ld_agent(pk + (0 * 64 + lane) * kNPL + j));
-                        const Cx Hk = to_cx(ld_agent(pk + (1 * 64 + lane) * kNPL + j));
-                        Hacc[j] = cfma(Pacc[j], Hk, Hacc[j]);
-                        Pacc[j] = cmul(Pacc[j], Pk);
-                    }
-                }
+                if (lane == 0) __hip_atomic_store(&flag[tt], kFlagAggregate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+            if (tid == kTicketThread)
+                next_ticket = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (has_next) {
+                issue_own<T, CPLX>(r, p, tn, tid, c, pr, s0);
+                issue_dma<T, DISC>(p, lay, tn, lane, wave - 1, &s_bcb[buf ^ 1][0][0], s_raw, s_k);
+            }
+        } else {
+            Cx Pt[kNPL], Ht[kNPL], carry[kNPL];
+            tile_aggregate(s_aggP, s_aggH, lane, Pt, Ht);
+            // re-read the wave aggregates from LDS after the look-back rather
+            // than holding them in registers across it
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < kNPL; ++j) carry[j] = {0.f, 0.f};
+            if (tt > 0) look_back(flag, pay_base, tt, lane, carry);
 #pragma unroll
             for (int j = 0; j < kNPL; ++j) {
                 const Cx inc = cfma(Pt[j], carry[j], Ht[j]);
-                st_agent(mine + (2 * 64 + lane) * kNPL + j, to_f2(inc));
+                st_agent(mine, pay_off(2, lane, j), to_f2(inc));
                 Cx hin = carry[j];  // incoming state of each wave's steps
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w) {
@@ -715,22 +801,30 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
                     }
                 }
             }
-            wait_stores();
-            if (lane == 0)
-                __hip_atomic_store(&flag[tt], kFlagInclusive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (has_next) issue_tile<T, DISC, CPLX>(r, p, lay, tn, tid, c, pr, s0, wave, &s_bcb[buf ^ 1][0][0], s_raw, s_k);
         }
         __syncthreads();
+        if (wave == 0) {
+            // the next tile's loads go out behind the inclusive stores; once at
+            // most that many instructions are outstanding the stores are
+            // complete and the flag may be raised
+            if (has_next) {
+                issue_own<T, CPLX>(r, p, tn, tid, c, pr, s0);
+                wait_vm_below<kOwnLoadsMin<CPLX>>();
+            } else {
+                wait_stores();
+            }
+            if (lane == 0) __hip_atomic_store(&flag[tt], kFlagInclusive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
 
-        // ---- 5. incoming state of this wave's steps (formed by wave 0)
+        // ---- 4. incoming state of this wave's steps (formed by wave 0)
         Cx h[kNPL];
 #pragma unroll
         for (int j = 0; j < kNPL; ++j) h[j] = to_cx(s_carry[wave][lane][j]);
 
-        // ---- 6. pass 2: recurrence from the incoming state, outputs (y through
+        // ---- 5. pass 2: recurrence from the incoming state, outputs (y through
         // a resource covering this wave's valid steps; stores past it drop)
         {
-            const int64_t yw0 = tc.t0 + s0;
+            const int64_t yw0 = tc.t0() + s0;
             const int64_t ysteps = L - yw0 < 0 ? 0 : (L - yw0 > kTW ? kTW : L - yw0);
             const uint32_t y_row = static_cast<uint32_t>(D) * es;
             const rsrc_t rY = make_rsrc(y + (tc.b * L + (ysteps ? yw0 : 0)) * D + tc.d0,

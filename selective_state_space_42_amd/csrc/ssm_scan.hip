@@ -140,7 +140,8 @@ int ssm_scan_fwd(const ssm_scan_desc_t* desc, const void* u, const void* delta, 
         p.batch = desc->batch; p.seqlen = desc->seqlen; p.dim = desc->dim; p.dstate = desc->dstate;
         p.workspace = workspace;
         p.theta_pairs = (desc->dstate % 2 == 0) && aligned(theta, 2 * es);
-        p.rows_dma = (desc->dim % 2 == 0) && aligned(u, 4) && aligned(delta, 4) && (!lambda || aligned(lambda, 4));
+        p.rows_dma = (desc->dim * static_cast<int64_t>(es)) % 16 == 0 && aligned(u, 16) && aligned(delta, 16) &&
+                     (!lambda || aligned(lambda, 16));
         st = desc->io_dtype == SSM_DTYPE_F32
                  ? ssm::launch_chunked<float>(desc->disc, desc->is_complex != 0, p, s)
                  : ssm::launch_chunked<uint16_t>(desc->disc, desc->is_complex != 0, p, s);
