@@ -208,7 +208,9 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkParams p, ChunkLay
                 cr = E::load(Cm, k);
             }
         }
-        bc[i] = make_float4(br, bi, cr, ci);
+        // stored state-pair-major (entry j * kLPC + p for state n = p * kNPL + j)
+        // so that a wave's reads of one entry per lane hit distinct LDS banks
+        bc[row * kChunkLanes + (n % chunk::kNPL) * chunk::kLPC + n / chunk::kNPL] = make_float4(br, bi, cr, ci);
         if constexpr (TRAP) {
             float part = cr * br - ci * bi;  // Re(C B)
             for (int off = 8; off > 0; off >>= 1) part += __shfl_xor(part, off, 16);
@@ -610,12 +612,16 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
     __shared__ float s_k[kTT];                              // K_t rows
     // pass-1 wave aggregates (P, h); once the incoming states are formed the
     // same space holds pass 2's y partials (kWaves x 8 steps x 64 lanes)
+    // y partials: rows of 64 lanes padded to kRedRow floats, so that the
+    // transposed reads (8 lanes of one channel, each from another row) fall
+    // in distinct banks
+    constexpr int kRedRow = 64 + 4;
     constexpr int kAggF2 = kWaves * 64 * kNPL;
-    static_assert(2 * kAggF2 * 2 == kWaves * 8 * 64, "aggregate and partial buffers share space");
-    __shared__ alignas(16) float s_x[kWaves * 8 * 64];
+    static_assert(2 * kAggF2 * 2 <= kWaves * 8 * kRedRow, "aggregate and partial buffers share space");
+    __shared__ alignas(16) float s_x[kWaves * 8 * kRedRow];
     float2* s_aggP = reinterpret_cast<float2*>(s_x);           // [wave][lane][j]
     float2* s_aggH = reinterpret_cast<float2*>(s_x) + kAggF2;  // [wave][lane][j]
-    float* s_red = s_x;                                         // [wave][step % 8][lane]
+    float* s_red = s_x;                                         // [wave][step % 8][lane (padded)]
     __shared__ float2 s_carry[kWaves][64][kNPL];  // incoming state of each wave's steps
     __shared__ uint32_t s_ticket;
 
@@ -698,7 +704,7 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
             if constexpr (kFast) sdt += tc4.x;
 #pragma unroll
             for (int j = 0; j < kNPL; ++j) {
-                const float4 bcq = s_bc[s0 + s][pr * kNPL + j];
+                const float4 bcq = s_bc[s0 + s][j * kLPC + pr];
                 const float rho = M::exp_dA(tc4.x, a_prep[j]);
                 if constexpr (CPLX) {
                     const float thv = r.th.get(s, j);
@@ -743,9 +749,9 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
 
         // ---- 3. cross-tile carry.  Wave 0: look back, form the inclusive state
         // and every wave's incoming state.  Wave 1: publish the tile aggregate.
-        // Waves 1..: the ticket after next, their loads of the next tile and
-        // its LDS copies.  (vmcnt retires in order, so wave 0 issues no loads
-        // before its look-back traffic has returned.)
+        // Waves 1..: the ticket after next and the next tile's LDS copies.
+        // (vmcnt retires in order, so wave 0 issues no loads before its
+        // look-back traffic has returned.)
         const uint32_t nx = __builtin_amdgcn_readfirstlane(s_ticket);
         const bool has_next = nx < slot_tiles;
         const Tile tn = has_next ? decode_tile(nx, per_tt, slot, lay, D) : tc;
@@ -767,10 +773,7 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
             }
             if (tid == kTicketThread)
                 next_ticket = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (has_next) {
-                issue_own<T, CPLX>(r, p, tn, tid, c, pr, s0);
-                issue_dma<T, DISC>(p, lay, tn, lane, wave - 1, &s_bcb[buf ^ 1][0][0], s_raw, s_k);
-            }
+            if (has_next) issue_dma<T, DISC>(p, lay, tn, lane, wave - 1, &s_bcb[buf ^ 1][0][0], s_raw, s_k);
         } else {
             Cx Pt[kNPL], Ht[kNPL], carry[kNPL];
             tile_aggregate(s_aggP, s_aggH, lane, Pt, Ht);
@@ -803,16 +806,17 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
             }
         }
         __syncthreads();
+        // Every wave's register loads of the next tile come from this one site
+        // (one set of destination registers, so pass 2 never waits on them).
+        // On wave 0 they go out behind the inclusive stores; once at most that
+        // many instructions are outstanding the stores are complete and the
+        // flag may be raised.
+        if (has_next) issue_own<T, CPLX>(r, p, tn, tid, c, pr, s0);
         if (wave == 0) {
-            // the next tile's loads go out behind the inclusive stores; once at
-            // most that many instructions are outstanding the stores are
-            // complete and the flag may be raised
-            if (has_next) {
-                issue_own<T, CPLX>(r, p, tn, tid, c, pr, s0);
+            if (has_next)
                 wait_vm_below<kOwnLoadsMin<CPLX>>();
-            } else {
+            else
                 wait_stores();
-            }
             if (lane == 0) __hip_atomic_store(&flag[tt], kFlagInclusive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 
@@ -836,7 +840,7 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
                 float part = 0.f;
 #pragma unroll
                 for (int j = 0; j < kNPL; ++j) {
-                    const float4 bcq = s_bc[s0 + s][pr * kNPL + j];
+                    const float4 bcq = s_bc[s0 + s][j * kLPC + pr];
                     if constexpr (CPLX) {
                         h[j] = cfma(Cx{al_r[s][j], al_i[s][j]}, h[j], Cx{tc4.y * bcq.x, tc4.y * bcq.y});
                         part += bcq.z * h[j].re - bcq.w * h[j].im;  // Re(C h)
@@ -845,14 +849,14 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
                         part += bcq.z * h[j].re;
                     }
                 }
-                s_red[(wave * 8 + (s & 7)) * 64 + lane] = part;
+                s_red[(wave * 8 + (s & 7)) * kRedRow + lane] = part;
                 if ((s & 7) == 7) {
                     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                     __builtin_amdgcn_wave_barrier();
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                     const int sb = s - 7 + pr;  // step this lane finishes
-                    const float4 v0 = *reinterpret_cast<const float4*>(&s_red[(wave * 8 + pr) * 64 + c * kLPC]);
-                    const float4 v1 = *reinterpret_cast<const float4*>(&s_red[(wave * 8 + pr) * 64 + c * kLPC + 4]);
+                    const float4 v0 = *reinterpret_cast<const float4*>(&s_red[(wave * 8 + pr) * kRedRow + c * kLPC]);
+                    const float4 v1 = *reinterpret_cast<const float4*>(&s_red[(wave * 8 + pr) * kRedRow + c * kLPC + 4]);
                     const float yv =
                         ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w)) + s_e[s0 + sb][c];
                     BE::store(rY, y_lane + static_cast<uint32_t>(sb) * y_row, yv);
