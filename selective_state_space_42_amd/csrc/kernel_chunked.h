@@ -325,19 +325,22 @@ __device__ __forceinline__ void issue_own(TileRegs<T>& r, const ChunkParams& p, 
         const int n0 = pr * kNPL;
         const uint32_t lo0 = cok && n0 < N ? static_cast<uint32_t>(c * N + n0) * es : kOutOfRange;
         const uint32_t lo1 = cok && n0 + 1 < N ? static_cast<uint32_t>(c * N + n0 + 1) * es : kOutOfRange;
+        // one branch for the whole wave-tile, so the loads issue back to back
+        if (p.theta_pairs) {  // N even: (n, n+1) adjacent and one element pair apart
 #pragma unroll
-        for (int s = 0; s < kTW; ++s) {
-            if constexpr (kFast) {
-                if (p.theta_pairs) {  // N even: (n, n+1) adjacent and 4-byte aligned
+            for (int s = 0; s < kTW; ++s) {
+                if constexpr (kFast)
                     r.th.w[s] = __builtin_amdgcn_raw_buffer_load_b32(rT, lo0 + s * row, 0, 0);
-                } else {
+                else
+                    BE::load_pair(rT, lo0 + s * row, &r.th.v[s][0], &r.th.v[s][1]);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < kTW; ++s) {
+                if constexpr (kFast) {
                     const uint32_t a = __builtin_amdgcn_raw_buffer_load_b16(rT, lo0 + s * row, 0, 0);
                     const uint32_t bb = __builtin_amdgcn_raw_buffer_load_b16(rT, lo1 + s * row, 0, 0);
                     r.th.w[s] = a | (bb << 16);
-                }
-            } else {
-                if (p.theta_pairs) {
-                    BE::load_pair(rT, lo0 + s * row, &r.th.v[s][0], &r.th.v[s][1]);
                 } else {
                     r.th.v[s][0] = BE::load(rT, lo0 + s * row);
                     r.th.v[s][1] = BE::load(rT, lo1 + s * row);
