@@ -10,7 +10,7 @@ already resident in HBM.  Rank 0 prints one JSON line:
   value      tokens*channels/s = B*L*D / (seconds per step)
   roofline   algorithmic HBM bytes per launch / kernel time vs 8.0 TB/s
              (algorithmic bytes: every input read once, every output written
-             once, as in DESIGN.md); `traffic` comes from the committed
+             once); `traffic` comes from the committed
              rocprofv3 counter summary when it was taken on the current
              kernel sources, else null
   cpu_baseline  the fp64 oracle timed on the host's cores over a bounded

@@ -587,6 +587,59 @@ __device__ __forceinline__ void look_back(const uint32_t* flag, const float2* pa
     }
 }
 
+// Pass 1 over one wave's steps: discretise every step, keep alpha_t in
+// registers (al_i holds b_t on the real path), run the recurrence from a zero
+// state (g) and sum delta and theta for the wave's decay product.  SC selects
+// the sin/cos evaluation.  The sums are kept where they stay exact enough:
+// with hardware sin/cos theta is summed as its reduced revolutions (bounded
+// by the step count), otherwise delta and theta are summed in fp64.
+template <typename T, int DISC, bool CPLX, int SC, typename Acc>
+__device__ __forceinline__ void pass1(const TileRegs<T>& r, const float2 (*s_dw)[chunk::kCPW],
+                                      const float4 (*s_bc)[kChunkLanes], int s0, int c, int pr, const float* a_prep,
+                                      const float* a_raw, const float* inv_a, float (&al_r)[chunk::kTW][chunk::kNPL],
+                                      float (&al_i)[chunk::kTW][chunk::kNPL], Cx* gl, Acc* sth, Acc& sdt) {
+    using namespace chunk;
+#pragma unroll
+    for (int s = 0; s < kTW; ++s) {
+        const float2 tc4 = s_dw[s0 + s][c];  // (delta, w)
+        sdt += static_cast<Acc>(tc4.x);
+#pragma unroll
+        for (int j = 0; j < kNPL; ++j) {
+            const float4 bcq = s_bc[s0 + s][j * kLPC + pr];
+            if constexpr (CPLX) {
+                const float rho = exp_dA(tc4.x, a_prep[j]);
+                const float thv = r.th.get(s, j);
+                float sn, cs;
+                if constexpr (SC == kSinCosHw) {
+                    const float rev = __builtin_amdgcn_fractf(thv * kInv2Pi);
+                    sin_cos_rev(rev, &sn, &cs);
+                    sth[j] += rev;
+                } else {
+                    sin_cos<SC>(thv, &sn, &cs);
+                    sth[j] += static_cast<Acc>(thv);
+                }
+                const Cx al = {rho * cs, rho * sn};
+                al_r[s][j] = al.re;
+                al_i[s][j] = al.im;
+                gl[j] = cfma(al, gl[j], Cx{tc4.y * bcq.x, tc4.y * bcq.y});
+            } else {
+                float rho, bt;
+                if constexpr (DISC == kZOH) {  // weight expm1(delta A)/A (delta at A = 0); decay 1 + expm1
+                    const float em1 = expm1f(tc4.x * a_raw[j]);
+                    rho = 1.f + em1;
+                    bt = (a_raw[j] != 0.f ? em1 * inv_a[j] : tc4.x) * tc4.y * bcq.x;
+                } else {
+                    rho = exp_dA(tc4.x, a_prep[j]);
+                    bt = tc4.y * bcq.x;
+                }
+                al_r[s][j] = rho;
+                al_i[s][j] = bt;
+                gl[j].re = rho * gl[j].re + bt;
+            }
+        }
+    }
+}
+
 // Persistent workgroups: each takes tickets from its slot's counter until the
 // slot's tiles are exhausted.  The pipeline per workgroup is
 //   [tile k: commit staged values to LDS | pass 1]
@@ -603,7 +656,6 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
     using BE = Buf<T>;
     constexpr uint32_t es = BE::kSize;
     constexpr bool kFast = std::is_same_v<T, uint16_t>;
-    using M = std::conditional_t<kFast, FastMath, AccurateMath>;
     constexpr bool kZ = DISC == kZOH;
     constexpr bool kTR = DISC == kTrap;
     static_assert(kTT * kChunkLanes % kThreads == 0 && kTT * kCPW % kThreads == 0, "tile shape");
@@ -689,62 +741,51 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
             nok[j] = cok && pr * kNPL + j < N;
             pin(r.a_ld[j]);
             a_raw[j] = r.a_ld[j];
-            a_prep[j] = M::prep_A(a_raw[j]);
+            a_prep[j] = prep_A(a_raw[j]);
             inv_a[j] = a_raw[j] != 0.f ? 1.f / a_raw[j] : 0.f;
         }
         float al_r[kTW][kNPL], al_i[kTW][kNPL];  // alpha_t (al_i holds b_t on the real path)
-        Cx gl[kNPL], P[kNPL];
-        float sth[kNPL], sdt = 0.f;
+        Cx gl[kNPL];
+        using Acc = std::conditional_t<kFast, float, double>;  // sums of delta and theta
+        Acc sth[kNPL], sdt = 0;
 #pragma unroll
         for (int j = 0; j < kNPL; ++j) {
             gl[j] = {0.f, 0.f};
-            P[j] = {1.f, 0.f};
-            sth[j] = 0.f;
+            sth[j] = 0;
         }
+        if constexpr (kFast || !CPLX) {
+            pass1<T, DISC, CPLX, kFast ? kSinCosHw : kSinCosPoly>(r, s_dw, s_bc, s0, c, pr, a_prep, a_raw, inv_a, al_r,
+                                                                  al_i, gl, sth, sdt);
+        } else {
+            // fp32 complex state: the polynomial sin/cos when every |theta| of
+            // this wave's steps is at most pi/4 (one uniform test per tile)
+            float m = 0.f;
 #pragma unroll
-        for (int s = 0; s < kTW; ++s) {
-            const float2 tc4 = s_dw[s0 + s][c];  // (delta, w)
-            if constexpr (kFast) sdt += tc4.x;
+            for (int s = 0; s < kTW; ++s)
 #pragma unroll
-            for (int j = 0; j < kNPL; ++j) {
-                const float4 bcq = s_bc[s0 + s][j * kLPC + pr];
-                const float rho = M::exp_dA(tc4.x, a_prep[j]);
-                if constexpr (CPLX) {
-                    const float thv = r.th.get(s, j);
-                    float sn, cs;
-                    M::sincos(thv, &sn, &cs);
-                    const Cx al = {rho * cs, rho * sn};
-                    al_r[s][j] = al.re;
-                    al_i[s][j] = al.im;
-                    gl[j] = cfma(al, gl[j], Cx{tc4.y * bcq.x, tc4.y * bcq.y});
-                    if constexpr (kFast) sth[j] += thv;
-                    else P[j] = cmul(al, P[j]);
-                } else {
-                    float bt;
-                    if constexpr (kZ) bt = zoh_gamma(tc4.x, a_raw[j], inv_a[j]) * tc4.y * bcq.x;
-                    else bt = tc4.y * bcq.x;
-                    al_r[s][j] = rho;
-                    al_i[s][j] = bt;
-                    gl[j].re = rho * gl[j].re + bt;
-                    if constexpr (!kFast) P[j].re = rho * P[j].re;
-                }
-            }
+                for (int j = 0; j < kNPL; ++j) m = fmaxf(m, fabsf(r.th.get(s, j)));
+            if (__any(!(m <= kPiOver4)))
+                pass1<T, DISC, CPLX, kSinCosWide>(r, s_dw, s_bc, s0, c, pr, a_prep, a_raw, inv_a, al_r, al_i, gl, sth,
+                                                 sdt);
+            else
+                pass1<T, DISC, CPLX, kSinCosPoly>(r, s_dw, s_bc, s0, c, pr, a_prep, a_raw, inv_a, al_r, al_i, gl, sth,
+                                                  sdt);
         }
-        // the wave's aggregate (P, h); on the fast path P = prod alpha is formed
-        // from the sums as exp(A sum delta) e^{i sum theta}
+        // the wave's aggregate (P, h): P = prod alpha = exp(A sum delta) e^{i sum theta}
 #pragma unroll
         for (int j = 0; j < kNPL; ++j) {
-            if constexpr (kFast) {
-                const float mod = M::exp_dA(sdt, a_prep[j]);
-                if constexpr (CPLX) {
-                    float sn, cs;
-                    M::sincos(sth[j], &sn, &cs);
-                    P[j] = {mod * cs, mod * sn};
-                } else {
-                    P[j] = {mod, 0.f};
-                }
+            const float mod = kFast ? exp_dA(static_cast<float>(sdt), a_prep[j])
+                                    : static_cast<float>(exp(sdt * static_cast<double>(a_raw[j])));
+            Cx P = {mod, 0.f};
+            if constexpr (CPLX) {
+                float sn, cs;
+                if constexpr (kFast)
+                    sin_cos_rev(__builtin_amdgcn_fractf(static_cast<float>(sth[j])), &sn, &cs);
+                else
+                    sin_cos_wide(static_cast<double>(sth[j]), &sn, &cs);
+                P = {mod * cs, mod * sn};
             }
-            s_aggP[(wave * 64 + lane) * kNPL + j] = to_f2(P[j]);
+            s_aggP[(wave * 64 + lane) * kNPL + j] = to_f2(P);
             s_aggH[(wave * 64 + lane) * kNPL + j] = to_f2(gl[j]);
         }
         if (tid == kTicketThread) s_ticket = next_ticket;

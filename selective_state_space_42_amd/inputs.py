@@ -54,9 +54,9 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads.  Distributions for the complex workloads follow the
-# readings recorded in the design doc (delta/u/Dskip as the Mamba-1-style workload
-# where the complex ones leave them unstated; re/im variance 1/2).
+# The five workloads.  Where the complex workloads leave delta, u and Dskip
+# unstated they take the Mamba-1-style workload's distributions; "re/im ~
+# N(0, 1/2)" is read as variance 1/2 for each part.
 WORKLOADS = {
     "real_zoh_b1_d4_l64_n4": Workload(
         "real_zoh_b1_d4_l64_n4", 1, 4, 64, 4, "zoh", False, "f32", -2.0, 0.5, "neg_index", 1.0),

@@ -89,6 +89,16 @@ def test_long_sequence_many_tiles(algo):
     _run(w, algo, d_index=list(range(16)))
 
 
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("scale", [0.5, 8.0, 3000.0])
+@pytest.mark.parametrize("mode", ["complex_euler_f32", "complex_trap_bf16"])
+def test_wide_rotation_angles(mode, scale, algo):
+    """theta = scale * U(-pi, pi): angles past pi/4 (the fp32 path's reduced
+    range) and past many revolutions."""
+    w = MODES[mode].scaled(name=f"{mode}_theta{scale:g}", batch=2, dim=19, seqlen=300, theta_scale=scale)
+    _run(w, algo)
+
+
 GOLDEN = sorted(glob.glob(os.path.join(os.path.dirname(__file__), "golden", "*.npz")))
 
 
