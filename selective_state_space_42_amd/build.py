@@ -3,7 +3,10 @@
     python -m selective_state_space_42_amd.build
 
 Every HIP source is compiled with packed-fp32 instruction selection turned
-off (-target-feature -packed-fp32-ops): scalar fp32 arithmetic only.
+off (-target-feature -packed-fp32-ops): scalar fp32 arithmetic only.  The
+atomic optimizer is off too: it rewrites a single lane's ticket fetch-add into
+a wave-wide form that consumes the returned value at once, so the wave would
+wait a full memory round trip for a ticket it only needs a tile later.
 """
 from __future__ import annotations
 
@@ -25,6 +28,7 @@ def hipcc_cmd(out: str = LIB, extra=()):
     return [
         "hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-Wno-unused-command-line-argument",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         *extra, "-o", out, *SOURCES,

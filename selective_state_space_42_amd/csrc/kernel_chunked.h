@@ -373,12 +373,12 @@ __device__ __forceinline__ void issue_dma(const ChunkParams& p, const ChunkLayou
     {
         const float4* src = bc + (t.b * lay.l_pad + t.t0()) * kChunkLanes;
         constexpr int kInstr = kTT * kChunkLanes / 64;
-        static_assert(kInstr % kDmaWaves == 0, "B/C rows split evenly over the DMA waves");
 #pragma unroll
-        for (int k = 0; k < kInstr / kDmaWaves; ++k) {
-            const int i0 = (k * kDmaWaves + dw) * 64;
-            __builtin_amdgcn_global_load_lds(src + i0 + lane,
-                                             (__attribute__((address_space(3))) void*)(s_bc_dst + i0), 16, 0, 0);
+        for (int k = 0; k < (kInstr + kDmaWaves - 1) / kDmaWaves; ++k) {
+            const int q = k * kDmaWaves + dw;  // this wave's instruction (uniform)
+            if (kInstr % kDmaWaves == 0 || q < kInstr)
+                __builtin_amdgcn_global_load_lds(src + q * 64 + lane,
+                                                 (__attribute__((address_space(3))) void*)(s_bc_dst + q * 64), 16, 0, 0);
         }
     }
     if (p.rows_dma) {
