@@ -599,13 +599,32 @@ __device__ __forceinline__ void pass1(const TileRegs<T>& r, const float2 (*s_dw)
                                       const float* a_raw, const float* inv_a, float (&al_r)[chunk::kTW][chunk::kNPL],
                                       float (&al_i)[chunk::kTW][chunk::kNPL], Cx* gl, Acc* sth, Acc& sdt) {
     using namespace chunk;
+    // the next step's LDS operands are read one step ahead
+    float2 nx_dw = s_dw[s0][c];
+    float2 nx_b[kNPL];
+#pragma unroll
+    for (int j = 0; j < kNPL; ++j) {
+        const float4 q = s_bc[s0][j * kLPC + pr];
+        nx_b[j] = make_float2(q.x, q.y);
+    }
 #pragma unroll
     for (int s = 0; s < kTW; ++s) {
-        const float2 tc4 = s_dw[s0 + s][c];  // (delta, w)
+        const float2 tc4 = nx_dw;  // (delta, w)
+        float2 cb[kNPL];
+#pragma unroll
+        for (int j = 0; j < kNPL; ++j) cb[j] = nx_b[j];
+        if (s + 1 < kTW) {
+            nx_dw = s_dw[s0 + s + 1][c];
+#pragma unroll
+            for (int j = 0; j < kNPL; ++j) {
+                const float4 q = s_bc[s0 + s + 1][j * kLPC + pr];
+                nx_b[j] = make_float2(q.x, q.y);
+            }
+        }
         sdt += static_cast<Acc>(tc4.x);
 #pragma unroll
         for (int j = 0; j < kNPL; ++j) {
-            const float4 bcq = s_bc[s0 + s][j * kLPC + pr];
+            const float4 bcq = make_float4(cb[j].x, cb[j].y, 0.f, 0.f);
             if constexpr (CPLX) {
                 const float rho = exp_dA(tc4.x, a_prep[j]);
                 const float thv = r.th.get(s, j);
@@ -637,6 +656,7 @@ __device__ __forceinline__ void pass1(const TileRegs<T>& r, const float2 (*s_dw)
                 gl[j].re = rho * gl[j].re + bt;
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -878,13 +898,26 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
             const rsrc_t rY = make_rsrc(y + (tc.b * L + (ysteps ? yw0 : 0)) * D + tc.d0,
                                         ysteps ? static_cast<uint32_t>((ysteps - 1) * D + tc.nch) * es : 0u);
             const uint32_t y_lane = cok ? static_cast<uint32_t>(c) * es : kOutOfRange;
+            // the next step's LDS operands are read one step ahead
+            float2 nx_dw = s_dw[s0][c];
+            float4 nx_b[kNPL];
+#pragma unroll
+            for (int j = 0; j < kNPL; ++j) nx_b[j] = s_bc[s0][j * kLPC + pr];
 #pragma unroll
             for (int s = 0; s < kTW; ++s) {
-                const float2 tc4 = s_dw[s0 + s][c];  // (delta, w)
+                const float2 tc4 = nx_dw;  // (delta, w)
+                float4 cb[kNPL];
+#pragma unroll
+                for (int j = 0; j < kNPL; ++j) cb[j] = nx_b[j];
+                if (s + 1 < kTW) {
+                    nx_dw = s_dw[s0 + s + 1][c];
+#pragma unroll
+                    for (int j = 0; j < kNPL; ++j) nx_b[j] = s_bc[s0 + s + 1][j * kLPC + pr];
+                }
                 float part = 0.f;
 #pragma unroll
                 for (int j = 0; j < kNPL; ++j) {
-                    const float4 bcq = s_bc[s0 + s][j * kLPC + pr];
+                    const float4 bcq = cb[j];
                     if constexpr (CPLX) {
                         h[j] = cfma(Cx{al_r[s][j], al_i[s][j]}, h[j], Cx{tc4.y * bcq.x, tc4.y * bcq.y});
                         part += bcq.z * h[j].re - bcq.w * h[j].im;  // Re(C h)
@@ -908,6 +941,7 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
                     __builtin_amdgcn_wave_barrier();
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         __syncthreads();  // LDS is rewritten by the next tile
