@@ -643,9 +643,9 @@ __device__ __forceinline__ void pass1(const TileRegs<T>& r, const float2 (*s_dw)
                 gl[j] = cfma(al, gl[j], Cx{tc4.y * bcq.x, tc4.y * bcq.y});
             } else {
                 float rho, bt;
-                if constexpr (DISC == kZOH) {  // weight expm1(delta A)/A (delta at A = 0); decay 1 + expm1
-                    const float em1 = expm1f(tc4.x * a_raw[j]);
-                    rho = 1.f + em1;
+                if constexpr (DISC == kZOH) {  // weight (e^{delta A} - 1)/A (delta at A = 0)
+                    float em1;
+                    exp_expm1(tc4.x * a_raw[j], tc4.x * a_prep[j], &rho, &em1);
                     bt = (a_raw[j] != 0.f ? em1 * inv_a[j] : tc4.x) * tc4.y * bcq.x;
                 } else {
                     rho = exp_dA(tc4.x, a_prep[j]);
