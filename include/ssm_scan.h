@@ -63,11 +63,13 @@ typedef enum {
     SSM_DISC_EXP_TRAPEZOIDAL = 2  /* needs lambda */
 } ssm_disc_t;
 
-/* Kernel family.  AUTO picks by shape: SEQUENTIAL sweeps the whole sequence
- * per channel (needs many channels to fill the GPU); CHUNKED splits the
- * sequence into tiles and carries the state between tiles with a decoupled
- * look-back (for long sequences / few channels).  Both give the same result
- * up to rounding. */
+/* Kernel family.  SEQUENTIAL sweeps the whole sequence per channel (one
+ * channel's states across lanes; needs many channels to fill the GPU; any
+ * N <= 64).  CHUNKED splits the sequence into tiles of 96 steps x 8 channels,
+ * keeps each tile's state in registers and carries it between tiles with a
+ * decoupled look-back (fills the GPU at any shape; N <= 16).  AUTO uses
+ * CHUNKED when N <= 16, else SEQUENTIAL.  Both give the same result up to
+ * rounding. */
 typedef enum { SSM_ALGO_AUTO = 0, SSM_ALGO_SEQUENTIAL = 1, SSM_ALGO_CHUNKED = 2 } ssm_algo_t;
 
 typedef enum {
@@ -75,7 +77,9 @@ typedef enum {
     SSM_ERR_INVALID_ARGUMENT = 1,   /* null required pointer, bad size, overflow,
                                        misalignment, forbidden NULL/non-NULL combination */
     SSM_ERR_UNSUPPORTED = 2,        /* complex ZOH, dstate > 64 (> 16 for CHUNKED),
-                                       unknown enum value */
+                                       unknown enum value, or (CHUNKED) a shape whose
+                                       per-tile windows exceed 32-bit offsets:
+                                       24*D*N*esize, 98*D*esize or 4*D*N above 2^30 */
     SSM_ERR_WORKSPACE_TOO_SMALL = 3,
     SSM_ERR_HIP = 4                 /* a HIP call failed; see ssm_scan_last_hip_error() */
 } ssm_status_t;
@@ -93,7 +97,9 @@ typedef struct {
 
 /* Bytes of workspace ssm_scan_fwd needs for `desc` (0 when the chosen kernel
  * needs none).  Returns 0 for an invalid descriptor as well; ssm_scan_fwd
- * reports that case. */
+ * reports that case.  For CHUNKED it is about 3 KiB per tile (96 steps x 8
+ * channels: the look-back payloads) plus 260 bytes per (batch, step) for the
+ * fp32 B/C rows; e.g. 4.6 GB for B=1, L=2^20, D=1024. */
 size_t ssm_scan_workspace_bytes(const ssm_scan_desc_t *desc);
 
 /*
@@ -122,7 +128,10 @@ size_t ssm_scan_workspace_bytes(const ssm_scan_desc_t *desc);
  *   stream                                hipStream_t (NULL = default stream)
  *
  * Alignment: every pointer must be aligned to its element size (4 bytes for
- * fp32, 2 for bf16, 8 for complex fp32 h_last).  Returns an ssm_status_t.
+ * fp32, 2 for bf16, 8 for complex fp32 h_last).  CHUNKED stages u, delta and
+ * lambda by 16-byte DMA when D * element size is a multiple of 16 and those
+ * pointers are 16-byte aligned; other shapes take a slower element-wise
+ * staging path with the same results.  Returns an ssm_status_t.
  */
 int ssm_scan_fwd(const ssm_scan_desc_t *desc, const void *u, const void *delta, const float *A,
                  const void *B, const void *C, const float *D, const void *theta,

@@ -141,7 +141,13 @@ inline bool chunked_preferred(int64_t, int64_t, int64_t) { return true; }
 
 // ---------------------------------------------------------------- helpers
 
-__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// vmcnt(0); the empty asm statements keep the compiler from moving memory
+// operations across the wait
+__device__ __forceinline__ void wait_stores() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
+}
 
 // Agent-scope relaxed 8-byte accesses at a wave-uniform base plus a 32-bit
 // per-lane byte offset (so the address is one scalar base and one VGPR).
