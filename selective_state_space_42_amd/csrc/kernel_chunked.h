@@ -463,9 +463,11 @@ __device__ __forceinline__ void commit_tile(const TileRegs<T>& r, const ChunkPar
     pin(dsk);
 #pragma unroll
     for (int k = 0; k < kTT * kCPW / kThreads; ++k) {
+        // No validity test: rows past the sequence end arrive as zeros (and
+        // K_t is zero there), so their terms come out zero; entries of
+        // channels past the group's end are never read by a lane that stores.
         const int i = tid + k * kThreads;
         const int st = i / kCPW;
-        const bool ok = t.t0() + st < L && cc < t.nch;
         const float x = BE::widen(raw[0 * kArrayEl + i]);
         const float dt = BE::widen(raw[1 * kArrayEl + i]);
         float w, e;
@@ -476,16 +478,15 @@ __device__ __forceinline__ void commit_tile(const TileRegs<T>& r, const ChunkPar
             w = dt * x;
             e = dsk * x;
         } else {
-            const bool okn = t.t0() + st + 1 < L;
             const float lam = BE::widen(raw[2 * kArrayEl + i]);
             const float dn = BE::widen(raw[1 * kArrayEl + i + kCPW]);
             const float ln = BE::widen(raw[2 * kArrayEl + i + kCPW]);
-            const float bnext = okn ? (1.f - ln) * dn : 0.f;  // beta'_{t+1}
+            const float bnext = (1.f - ln) * dn;  // beta'_{t+1} (zero past the end)
             w = (lam * dt + bnext) * x;
             e = (dsk - bnext * s_k[st]) * x;
         }
-        s_dw[st][cc] = ok ? make_float2(dt, w) : make_float2(0.f, 0.f);
-        s_e[st][cc] = ok ? e : 0.f;
+        s_dw[st][cc] = make_float2(dt, w);
+        s_e[st][cc] = e;
     }
 }
 
@@ -920,16 +921,18 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
 #pragma unroll
                     for (int j = 0; j < kNPL; ++j) nx_b[j] = s_bc[s0 + s + 1][j * kLPC + pr];
                 }
-                float part = 0.f;
+                // Re(sum_j C h) of this lane's states as one chain of fmas
+                float part;
 #pragma unroll
                 for (int j = 0; j < kNPL; ++j) {
                     const float4 bcq = cb[j];
                     if constexpr (CPLX) {
                         h[j] = cfma(Cx{al_r[s][j], al_i[s][j]}, h[j], Cx{tc4.y * bcq.x, tc4.y * bcq.y});
-                        part += bcq.z * h[j].re - bcq.w * h[j].im;  // Re(C h)
+                        part = j ? __builtin_fmaf(bcq.z, h[j].re, part) : bcq.z * h[j].re;
+                        part = __builtin_fmaf(-bcq.w, h[j].im, part);
                     } else {
                         h[j].re = al_r[s][j] * h[j].re + al_i[s][j];
-                        part += bcq.z * h[j].re;
+                        part = j ? __builtin_fmaf(bcq.z, h[j].re, part) : bcq.z * h[j].re;
                     }
                 }
                 s_red[(wave * 8 + (s & 7)) * kRedRow + lane] = part;
