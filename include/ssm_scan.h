@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 1
+#define SSM_SCAN_ABI_VERSION 2
 
 /* Element type of u, delta, B, C, theta, lambda and y.  A, D and h_last are
  * always fp32; all arithmetic is fp32 (bf16 inputs are widened exactly, y is
@@ -137,6 +137,68 @@ int ssm_scan_fwd(const ssm_scan_desc_t *desc, const void *u, const void *delta, 
                  const void *B, const void *C, const float *D, const void *theta,
                  const void *lambda, void *y, float *h_last, void *workspace,
                  size_t workspace_bytes, void *stream);
+
+/*
+ * Continuation of a scan: the same operation over a sequence that began
+ * before step 0.  A long sequence can be processed in pieces, or a prompt
+ * scanned and its state handed to ssm_scan_step for decoding.  The state is
+ * the whole memory a recurrent model carries, so a state left by one call
+ * serves as the prefix of the next (the production
+ * checklist of the blog.lonae.com essay, on reusing the state; the
+ * ai.tomabc.com Mamba-3 story's motivation section, on the fixed-size state
+ * of recurrent inference).  Arguments as for ssm_scan_fwd, plus:
+ *
+ *   h0      [B][D][N] fp32, or [B][D][N][2]    state before step 0 (h_{-1});
+ *           (is_complex = 1), or NULL            NULL means 0
+ *   q0      same layout as h0, or NULL          q_{-1} = B_{-1} u_{-1}, the input
+ *                                               term of the step before step 0,
+ *                                               which the trapezoid's beta_0
+ *                                               multiplies; EXP_TRAPEZOIDAL only
+ *                                               (must be NULL otherwise); NULL means 0
+ *   q_last  same layout as h0, or NULL          q_{L-1} = B_{L-1} u_{L-1} (written);
+ *                                               EXP_TRAPEZOIDAL only
+ *
+ * Passing h_last and q_last of one call as h0 and q0 of the next gives the
+ * result of a single call over the concatenated sequence (up to rounding).
+ * h0 and q0 must not alias h_last, q_last or any other output.  Each state
+ * pointer must be aligned to one state element (8 bytes complex, 4 real).
+ * ssm_scan_fwd is this call with h0, q0 and q_last NULL.  Returns an
+ * ssm_status_t.
+ */
+int ssm_scan_fwd_ex(const ssm_scan_desc_t *desc, const void *u, const void *delta, const float *A,
+                    const void *B, const void *C, const float *D, const void *theta,
+                    const void *lambda, const float *h0, const float *q0, void *y, float *h_last,
+                    float *q_last, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One step of the recurrence with the state kept in device memory and
+ * updated in place: the decode step of autoregressive generation, where each
+ * new token advances the fixed-size state once (the ai.tomabc.com Mamba-3
+ * story's table of inference arithmetic intensity treats this sequential
+ * step; it reads and writes the whole state per token, so it is bound by
+ * memory traffic).  desc->seqlen must be 1; desc->algo is ignored.  The
+ * tensors are those of ssm_scan_fwd with the length-1 time axis dropped:
+ *
+ *   u, delta, lambda  [B][D] io dtype     inputs of this step (lambda: EXP_TRAPEZOIDAL
+ *                                         only, NULL otherwise)
+ *   A [D][N] fp32, D [D] fp32 or NULL     as for ssm_scan_fwd
+ *   B, C   [B][N] or [B][N][2] io dtype   projections of this step
+ *   theta  [B][D][N] io dtype or NULL     rotation of this step (complex state)
+ *   h      [B][D][N] or [B][D][N][2] fp32 read as h_{t-1}, overwritten with h_t
+ *                                         (required)
+ *   q      same layout as h, fp32         EXP_TRAPEZOIDAL: read as q_{t-1} = B_{t-1} u_{t-1}
+ *                                         and overwritten with q_t = B_t u_t
+ *                                         (required); must be NULL otherwise
+ *   y      [B][D] io dtype                output of this step (written)
+ *
+ * h and q of ssm_scan_fwd_ex's h_last and q_last continue a scanned prompt;
+ * zeros start from an empty history.  N may be up to 64.  No workspace.
+ * h and q must not alias each other or any other argument.  Returns an
+ * ssm_status_t.
+ */
+int ssm_scan_step(const ssm_scan_desc_t *desc, const void *u, const void *delta, const float *A,
+                  const void *B, const void *C, const float *D, const void *theta, const void *lambda,
+                  float *h, float *q, void *y, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *ssm_scan_status_string(int status);

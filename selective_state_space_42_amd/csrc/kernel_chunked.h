@@ -83,6 +83,9 @@ struct ChunkParams {
     const void* lambda;
     void* y;
     float* h_last;
+    const float* h0;  // state before step 0, layout of h_last (NULL: zero)
+    const float* q0;  // trapezoid: q_{-1} = B_{-1} u_{-1}, layout of h_last (NULL: zero)
+    float* q_last;    // trapezoid: q_{L-1} = B_{L-1} u_{L-1} (written when not NULL)
     int64_t batch, seqlen, dim, dstate;
     void* workspace;
     int32_t theta_pairs;  // 1: dstate even and theta aligned to two elements
@@ -221,6 +224,28 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkParams p, ChunkLay
             float part = cr * br - ci * bi;  // Re(C B)
             for (int off = 8; off > 0; off >>= 1) part += __shfl_xor(part, off, 16);
             if (n == 0) kt[row] = part;
+        }
+    }
+
+    // q_{L-1} = B_{L-1} u_{L-1} per (b, d, n): the trapezoid's input term that a
+    // continuation of the sequence needs (bf16 products are exact in fp32)
+    if constexpr (TRAP) {
+        if (p.q_last) {
+            const T* u = static_cast<const T*>(p.u);
+            const int64_t nq = p.batch * p.dim * p.dstate;
+            for (int64_t i = gtid; i < nq; i += stride) {
+                const int64_t n = i % p.dstate, bd = i / p.dstate;
+                const int64_t b = bd / p.dim, d = bd % p.dim;
+                const int64_t t = p.seqlen - 1;
+                const float x = E::load(u, (b * p.seqlen + t) * p.dim + d);
+                const int64_t k = (b * p.seqlen + t) * p.dstate + n;
+                if constexpr (CPLX) {
+                    p.q_last[2 * i] = E::load(Bm, 2 * k) * x;
+                    p.q_last[2 * i + 1] = E::load(Bm, 2 * k + 1) * x;
+                } else {
+                    p.q_last[i] = E::load(Bm, k) * x;
+                }
+            }
         }
     }
 }
@@ -853,7 +878,32 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
             asm volatile("" ::: "memory");
 #pragma unroll
             for (int j = 0; j < kNPL; ++j) carry[j] = {0.f, 0.f};
-            if (tt > 0) look_back(flag, pay_base, tt, lane, carry);
+            if (tt > 0) {
+                look_back(flag, pay_base, tt, lane, carry);
+            } else if (p.h0 || (kTR && p.q0)) {
+                // the state before step 0; the trapezoid carries the shifted
+                // state, g_{-1} = h_{-1} + beta'_0 q_{-1} with beta'_0 = (1 - lambda_0) delta_0
+                using E = Elem<T>;
+                float bp0 = 0.f;
+                if constexpr (kTR) {
+                    if (p.q0 && cok) {
+                        const int64_t i0 = tc.b * L * D + d;
+                        bp0 = (1.f - E::load(lambda, i0)) * E::load(delta, i0);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < kNPL; ++j) {
+                    if (!nok[j]) continue;
+                    const int64_t hs = (tc.b * D + d) * N + pr * kNPL + j;
+                    Cx g0 = {0.f, 0.f};
+                    if (p.h0) g0 = CPLX ? Cx{p.h0[2 * hs], p.h0[2 * hs + 1]} : Cx{p.h0[hs], 0.f};
+                    if (kTR && p.q0) {
+                        const Cx q = CPLX ? Cx{p.q0[2 * hs], p.q0[2 * hs + 1]} : Cx{p.q0[hs], 0.f};
+                        g0 = {g0.re + bp0 * q.re, g0.im + bp0 * q.im};
+                    }
+                    carry[j] = g0;
+                }
+            }
 #pragma unroll
             for (int j = 0; j < kNPL; ++j) {
                 const Cx inc = cfma(Pt[j], carry[j], Ht[j]);

@@ -29,6 +29,9 @@ struct SeqParams {
     const void* lambda;
     void* y;
     float* h_last;
+    const float* h0;  // state before step 0, layout of h_last (NULL: zero)
+    const float* q0;  // trapezoid: q_{-1}, layout of h_last (NULL: zero)
+    float* q_last;    // trapezoid: q_{L-1} (written when not NULL)
     int64_t batch, seqlen, dim, dstate;
     int32_t lpc;  // lanes per channel: power of two, dstate <= lpc <= 64
 };
@@ -58,8 +61,17 @@ __global__ void __launch_bounds__(256) scan_sequential_kernel(SeqParams p) {
     const float a = ok ? p.A[d * N + n] : 0.0f;
     const float dskip = (ch_ok && p.Dskip) ? p.Dskip[d] : 0.0f;
 
+    const int64_t sidx = (b * D + d) * N + n;  // (b, d, n) in the layout of h_last
     float hr = 0.0f, hi = 0.0f;    // state h[n]
     float qpr = 0.0f, qpi = 0.0f;  // previous step's q = B u (trapezoid only)
+    if (ok && p.h0) {
+        hr = CPLX ? p.h0[2 * sidx] : p.h0[sidx];
+        hi = CPLX ? p.h0[2 * sidx + 1] : 0.0f;
+    }
+    if (DISC == kTrap && ok && p.q0) {
+        qpr = CPLX ? p.q0[2 * sidx] : p.q0[sidx];
+        qpi = CPLX ? p.q0[2 * sidx + 1] : 0.0f;
+    }
 
     for (int64_t t = 0; t < L; ++t) {
         const int64_t tc = (b * L + t) * D + d;
@@ -124,12 +136,19 @@ __global__ void __launch_bounds__(256) scan_sequential_kernel(SeqParams p) {
     }
 
     if (ok && p.h_last) {
-        const int64_t s = (b * D + d) * N + n;
         if constexpr (CPLX) {
-            p.h_last[2 * s] = hr;
-            p.h_last[2 * s + 1] = hi;
+            p.h_last[2 * sidx] = hr;
+            p.h_last[2 * sidx + 1] = hi;
         } else {
-            p.h_last[s] = hr;
+            p.h_last[sidx] = hr;
+        }
+    }
+    if (DISC == kTrap && ok && p.q_last) {  // q_{L-1}, the input term a continuation needs
+        if constexpr (CPLX) {
+            p.q_last[2 * sidx] = qpr;
+            p.q_last[2 * sidx + 1] = qpi;
+        } else {
+            p.q_last[sidx] = qpr;
         }
     }
 }

@@ -13,6 +13,7 @@
 #include "device_common.h"
 #include "kernel_sequential.h"
 #include "kernel_chunked.h"
+#include "kernel_step.h"
 
 namespace {
 
@@ -80,6 +81,45 @@ int launch_sequential(const ssm_scan_desc_t* d, const ssm::SeqParams& p, hipStre
     return hip_status(hipGetLastError());
 }
 
+template <typename T>
+int launch_step(const ssm_scan_desc_t* d, const ssm::StepParams& p, hipStream_t s) {
+    const int64_t waves = (d->batch * d->dim + (64 / p.lpc) - 1) / (64 / p.lpc);
+    const int64_t blocks = (waves + 3) / 4;
+    if (blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+    if (d->is_complex) {
+        if (d->disc == SSM_DISC_EXP_EULER)
+            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kEuler, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kTrap, true>), grid, block, 0, s, p);
+    } else {
+        if (d->disc == SSM_DISC_ZOH)
+            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kZOH, false>), grid, block, 0, s, p);
+        else if (d->disc == SSM_DISC_EXP_EULER)
+            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kEuler, false>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kTrap, false>), grid, block, 0, s, p);
+    }
+    return hip_status(hipGetLastError());
+}
+
+// Pointer checks shared by the scan and the step: required inputs present,
+// lambda exactly for the trapezoid, theta only for a complex state, every
+// pointer aligned to its element.
+int check_inputs(const ssm_scan_desc_t* desc, const void* u, const void* delta, const float* A, const void* B,
+                 const void* C, const float* D, const void* theta, const void* lambda, const void* y) {
+    const bool trap = desc->disc == SSM_DISC_EXP_TRAPEZOIDAL;
+    if (!u || !delta || !A || !B || !C || !y) return SSM_ERR_INVALID_ARGUMENT;
+    if (trap != (lambda != nullptr)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!desc->is_complex && theta) return SSM_ERR_INVALID_ARGUMENT;
+    const size_t es = desc->io_dtype == SSM_DTYPE_F32 ? 4 : 2;
+    const void* io_ptrs[] = {u, delta, B, C, theta, lambda, y};
+    for (const void* q : io_ptrs)
+        if (q && !aligned(q, es)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!aligned(A, 4) || (D && !aligned(D, 4))) return SSM_ERR_INVALID_ARGUMENT;
+    return SSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,18 +149,25 @@ size_t ssm_scan_workspace_bytes(const ssm_scan_desc_t* desc) {
 int ssm_scan_fwd(const ssm_scan_desc_t* desc, const void* u, const void* delta, const float* A,
                  const void* B, const void* C, const float* D, const void* theta, const void* lambda,
                  void* y, float* h_last, void* workspace, size_t workspace_bytes, void* stream) {
+    return ssm_scan_fwd_ex(desc, u, delta, A, B, C, D, theta, lambda, nullptr, nullptr, y, h_last, nullptr,
+                           workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_fwd_ex(const ssm_scan_desc_t* desc, const void* u, const void* delta, const float* A,
+                    const void* B, const void* C, const float* D, const void* theta, const void* lambda,
+                    const float* h0, const float* q0, void* y, float* h_last, float* q_last, void* workspace,
+                    size_t workspace_bytes, void* stream) {
     int st = check_desc(desc);
     if (st != SSM_OK) return st;
+    st = check_inputs(desc, u, delta, A, B, C, D, theta, lambda, y);
+    if (st != SSM_OK) return st;
     const bool trap = desc->disc == SSM_DISC_EXP_TRAPEZOIDAL;
-    if (!u || !delta || !A || !B || !C || !y) return SSM_ERR_INVALID_ARGUMENT;
-    if (trap != (lambda != nullptr)) return SSM_ERR_INVALID_ARGUMENT;
-    if (!desc->is_complex && theta) return SSM_ERR_INVALID_ARGUMENT;
+    if (!trap && (q0 || q_last)) return SSM_ERR_INVALID_ARGUMENT;
+    const size_t ss = desc->is_complex ? 8 : 4;  // one state element
+    const void* st_ptrs[] = {h0, q0, h_last, q_last};
+    for (const void* q : st_ptrs)
+        if (q && !aligned(q, ss)) return SSM_ERR_INVALID_ARGUMENT;
     const size_t es = desc->io_dtype == SSM_DTYPE_F32 ? 4 : 2;
-    const void* io_ptrs[] = {u, delta, B, C, theta, lambda, y};
-    for (const void* q : io_ptrs)
-        if (q && !aligned(q, es)) return SSM_ERR_INVALID_ARGUMENT;
-    if (!aligned(A, 4) || (D && !aligned(D, 4))) return SSM_ERR_INVALID_ARGUMENT;
-    if (h_last && !aligned(h_last, desc->is_complex ? 8 : 4)) return SSM_ERR_INVALID_ARGUMENT;
 
     const int algo = choose_algo(desc);
     if (algo == SSM_ALGO_CHUNKED && desc->dstate > ssm::kChunkLanes) return SSM_ERR_UNSUPPORTED;
@@ -137,6 +184,7 @@ int ssm_scan_fwd(const ssm_scan_desc_t* desc, const void* u, const void* delta, 
         ssm::ChunkParams p{};
         p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.theta = theta;
         p.lambda = lambda; p.y = y; p.h_last = h_last;
+        p.h0 = h0; p.q0 = q0; p.q_last = q_last;
         p.batch = desc->batch; p.seqlen = desc->seqlen; p.dim = desc->dim; p.dstate = desc->dstate;
         p.workspace = workspace;
         p.theta_pairs = (desc->dstate % 2 == 0) && aligned(theta, 2 * es);
@@ -151,10 +199,33 @@ int ssm_scan_fwd(const ssm_scan_desc_t* desc, const void* u, const void* delta, 
     ssm::SeqParams p{};
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.theta = theta;
     p.lambda = lambda; p.y = y; p.h_last = h_last;
+    p.h0 = h0; p.q0 = q0; p.q_last = q_last;
     p.batch = desc->batch; p.seqlen = desc->seqlen; p.dim = desc->dim; p.dstate = desc->dstate;
     p.lpc = next_pow2(desc->dstate);
     return desc->io_dtype == SSM_DTYPE_F32 ? launch_sequential<float>(desc, p, s)
                                            : launch_sequential<uint16_t>(desc, p, s);
+}
+
+int ssm_scan_step(const ssm_scan_desc_t* desc, const void* u, const void* delta, const float* A, const void* B,
+                  const void* C, const float* D, const void* theta, const void* lambda, float* h, float* q,
+                  void* y, void* stream) {
+    int st = check_desc(desc);
+    if (st != SSM_OK) return st;
+    if (desc->seqlen != 1) return SSM_ERR_INVALID_ARGUMENT;
+    st = check_inputs(desc, u, delta, A, B, C, D, theta, lambda, y);
+    if (st != SSM_OK) return st;
+    const bool trap = desc->disc == SSM_DISC_EXP_TRAPEZOIDAL;
+    if (!h || trap != (q != nullptr)) return SSM_ERR_INVALID_ARGUMENT;
+    const size_t ss = desc->is_complex ? 8 : 4;
+    if (!aligned(h, ss) || (q && !aligned(q, ss))) return SSM_ERR_INVALID_ARGUMENT;
+
+    ssm::StepParams p{};
+    p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.theta = theta;
+    p.lambda = lambda; p.h = h; p.q = q; p.y = y;
+    p.batch = desc->batch; p.dim = desc->dim; p.dstate = desc->dstate;
+    p.lpc = next_pow2((desc->dstate + 1) / 2);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return desc->io_dtype == SSM_DTYPE_F32 ? launch_step<float>(desc, p, s) : launch_step<uint16_t>(desc, p, s);
 }
 
 }  // extern "C"

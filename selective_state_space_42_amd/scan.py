@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libssmscan.so")
 SSM_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 SSM_DISC = {"zoh": 0, "euler": 1, "trap": 2}
 SSM_ALGO = {"auto": 0, "sequential": 1, "chunked": 2}
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class ScanDesc(ctypes.Structure):
@@ -51,6 +51,10 @@ def _lib():
     vp = ctypes.c_void_p
     lib.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 11 + [ctypes.c_size_t, vp]
     lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_scan_fwd_ex.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 14 + [ctypes.c_size_t, vp]
+    lib.ssm_scan_fwd_ex.restype = ctypes.c_int
+    lib.ssm_scan_step.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 12
+    lib.ssm_scan_step.restype = ctypes.c_int
     lib.ssm_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
     lib.ssm_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_scan_status_string.argtypes = [ctypes.c_int]
@@ -116,3 +120,59 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, theta=None, lam=None, *, disc: str, 
     if st != 0:
         raise ScanError(st, "ssm_scan_fwd")
     return y, h_last
+
+
+def ssm_scan_fwd_ex(u, delta, A, B, C, D=None, theta=None, lam=None, h0=None, q0=None, *, disc: str, y=None,
+                    h_last=None, q_last=None, want_h_last: bool = True, want_q_last: bool = False,
+                    workspace=None, algo: str = "auto", stream=None):
+    """Continuation of a scan; returns (y, h_last, q_last).
+
+    As ssm_scan_fwd, plus h0 (the state before step 0) and, for the
+    trapezoid, q0 = B_{-1} u_{-1}; both have the layout of h_last and may be
+    None (zero).  q_last = B_{L-1} u_{L-1} is returned for the trapezoid when
+    want_q_last (else None).
+    """
+    Bsz, L, Dm = u.shape
+    N = A.shape[1]
+    is_complex = B.dim() == 4
+    desc = make_desc(Bsz, L, Dm, N, u.dtype, disc, is_complex, algo)
+    shape = (Bsz, Dm, N, 2) if is_complex else (Bsz, Dm, N)
+    if y is None:
+        y = torch.empty_like(u)
+    if h_last is None and want_h_last:
+        h_last = torch.empty(shape, dtype=torch.float32, device=u.device)
+    if q_last is None and want_q_last:
+        q_last = torch.empty(shape, dtype=torch.float32, device=u.device)
+    need = ssm_scan_workspace_bytes(desc)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream if u.is_cuda else 0
+    st = _lib().ssm_scan_fwd_ex(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                _ptr(theta), _ptr(lam), _ptr(h0), _ptr(q0), _ptr(y), _ptr(h_last), _ptr(q_last),
+                                _ptr(workspace), ws_bytes, ctypes.c_void_p(stream))
+    if st != 0:
+        raise ScanError(st, "ssm_scan_fwd_ex")
+    return y, h_last, q_last
+
+
+def ssm_scan_step(u, delta, A, B, C, D=None, theta=None, lam=None, *, h, q=None, disc: str, y=None, stream=None):
+    """One decode step, updating h (and q for the trapezoid) in place; returns y.
+
+    u, delta, lam (B,D); A (D,N) fp32; B, C (B,N) real or (B,N,2) complex;
+    D (D,) fp32; theta (B,D,N); h, q (B,D,N) or (B,D,N,2) fp32.
+    """
+    Bsz, Dm = u.shape
+    N = A.shape[1]
+    is_complex = B.dim() == 3
+    desc = make_desc(Bsz, 1, Dm, N, u.dtype, disc, is_complex)
+    if y is None:
+        y = torch.empty_like(u)
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream if u.is_cuda else 0
+    st = _lib().ssm_scan_step(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                              _ptr(theta), _ptr(lam), _ptr(h), _ptr(q), _ptr(y), ctypes.c_void_p(stream))
+    if st != 0:
+        raise ScanError(st, "ssm_scan_step")
+    return y

@@ -27,14 +27,14 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = scan._lib()
     names = declared_functions()
-    assert {"ssm_scan_fwd", "ssm_scan_workspace_bytes", "ssm_scan_status_string",
-            "ssm_scan_abi_version", "ssm_scan_last_hip_error"} <= set(names)
+    assert {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_step", "ssm_scan_workspace_bytes",
+            "ssm_scan_status_string", "ssm_scan_abi_version", "ssm_scan_last_hip_error"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_version_and_status_strings():
-    assert scan.ssm_scan_abi_version() == 1
+    assert scan.ssm_scan_abi_version() == 2
     for code, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported configuration"),
                        (3, "workspace too small"), (4, "HIP runtime error"), (99, "unknown status")]:
         assert scan.ssm_scan_status_string(code) == text
@@ -110,3 +110,45 @@ def test_workspace_rules():
     assert call(d, lam=P, theta=P, ws=0) == WS_SMALL
     assert call(d, lam=P, theta=P, ws=P, ws_bytes=need - 1) == WS_SMALL
     assert call(d, lam=P, theta=P, ws=P + 64, ws_bytes=need) == INVALID  # not 256-byte aligned
+
+
+def call_ex(desc, u=P, delta=P, A=P, B=P, C=P, D=0, theta=0, lam=0, h0=0, q0=0, y=P, h=0, q_last=0, ws=0,
+            ws_bytes=0):
+    lib = scan._lib()
+    args = [u, delta, A, B, C, D, theta, lam, h0, q0, y, h, q_last, ws]
+    return lib.ssm_scan_fwd_ex(ctypes.byref(desc), *[ctypes.c_void_p(a) if a else None for a in args], ws_bytes,
+                               None)
+
+
+def call_step(desc, u=P, delta=P, A=P, B=P, C=P, D=0, theta=0, lam=0, h=P, q=0, y=P):
+    lib = scan._lib()
+    dp = None if desc is None else ctypes.byref(desc)
+    args = [u, delta, A, B, C, D, theta, lam, h, q, y]
+    return lib.ssm_scan_step(dp, *[ctypes.c_void_p(a) if a else None for a in args], None)
+
+
+def test_continuation_argument_rules():
+    # q0 / q_last belong to the trapezoid only
+    assert call_ex(desc(disc="euler"), q0=P) == INVALID
+    assert call_ex(desc(disc="zoh"), q_last=P) == INVALID
+    # state pointers aligned to one state element
+    assert call_ex(desc(cplx=True), h0=P + 4) == INVALID
+    assert call_ex(desc(disc="trap", cplx=True), lam=P, q0=P + 4) == INVALID
+    assert call_ex(desc(disc="trap"), lam=P, q_last=P + 2) == INVALID
+    # the same pointer rules as the plain scan
+    assert call_ex(desc(), u=0) == INVALID
+    assert call_ex(desc(disc="trap")) == INVALID
+    assert call_ex(desc(N=65)) == UNSUPPORTED
+
+
+def test_step_argument_rules():
+    assert call_step(None) == INVALID
+    assert call_step(desc(L=2)) == INVALID                      # one step per call
+    assert call_step(desc(L=1), h=0) == INVALID                 # state required
+    assert call_step(desc(L=1, disc="trap"), lam=P) == INVALID  # trapezoid needs q
+    assert call_step(desc(L=1, disc="euler"), q=P) == INVALID   # q only for the trapezoid
+    assert call_step(desc(L=1, cplx=True), h=P + 4) == INVALID
+    assert call_step(desc(L=1, disc="trap"), lam=P, q=P + 2) == INVALID
+    assert call_step(desc(L=1), u=P + 2) == INVALID
+    assert call_step(desc(L=1, N=65)) == UNSUPPORTED
+    assert call_step(desc(L=1, disc="zoh", cplx=True)) == UNSUPPORTED

@@ -1,0 +1,159 @@
+"""GPU parity of the continuation entry point and the decode step.
+
+ssm_scan_fwd_ex takes the state before step 0 (h0) and the trapezoid's
+previous input term (q0 = B_{-1} u_{-1}) and returns q_last; ssm_scan_step
+advances a state kept in memory by one step.  Both are compared with the fp64
+oracle, whose own continuation is pinned bitwise to its one-shot result
+(tests/test_oracle_pins.py):
+
+  * a sequence scanned in two calls (the first call's h_last, q_last handed
+    to the second as h0, q0) equals the oracle's one-shot scan;
+  * random nonzero h0, q0 give the oracle's continued scan from those values;
+  * a prompt scanned by ssm_scan_fwd_ex followed by ssm_scan_step decode
+    steps equals the oracle's one-shot scan over prompt + decoded steps.
+
+Tolerances are those of the scan: 1e-5 for fp32 I/O, 2e-2 for bf16 I/O.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import TOL, rel_err, rel_err_complex
+from selective_state_space_42_amd.inputs import WORKLOADS, all_channels, make_inputs
+from selective_state_space_42_amd.scan import ssm_scan_fwd_ex, ssm_scan_step
+
+pytestmark = pytest.mark.gpu
+
+_R = WORKLOADS["real_zoh_b8_d1536_l2048_n16"]
+_C = WORKLOADS["complex_euler_b8_d2048_l4096_n16"]
+MODES = {
+    "real_zoh_f32": _R,
+    "real_euler_bf16": _R.scaled(disc="euler", io_dtype="bf16"),
+    "real_trap_f32": _R.scaled(disc="trap"),
+    "real_trap_bf16": _R.scaled(disc="trap", io_dtype="bf16"),
+    "complex_euler_f32": _C,
+    "complex_trap_f32": _C.scaled(disc="trap"),
+    "complex_trap_bf16": _C.scaled(disc="trap", io_dtype="bf16"),
+}
+KEYS = ("u", "delta", "A", "Bm", "Cm", "Dskip", "theta", "lam")
+
+
+def _time_slice(inp, a, b):
+    """Steps [a, b) of every per-step input, as contiguous tensors."""
+    out = dict(inp)
+    for k in ("u", "delta", "lam", "theta", "Bm", "Cm"):
+        if inp[k] is not None:
+            out[k] = inp[k][:, a:b].contiguous()
+    return out
+
+
+def _step_inputs(inp, t):
+    """The inputs of step t with the time axis dropped."""
+    out = dict(inp)
+    for k in ("u", "delta", "lam", "theta", "Bm", "Cm"):
+        if inp[k] is not None:
+            out[k] = inp[k][:, t].contiguous()
+    return out
+
+
+def _args(x):
+    return [x[k] for k in KEYS]
+
+
+def _host(t):
+    return None if t is None else t.detach().float().cpu().double().numpy()
+
+
+def _errs(w, y, h, ref_y, ref_h):
+    err_y = rel_err(_host(y), ref_y)
+    err_h = rel_err_complex(_host(h), ref_h) if w.is_complex else rel_err(_host(h), ref_h)
+    return err_y, err_h
+
+
+def _oracle(w, x, **kw):
+    return oracle.scan(x["u"], x["delta"], x["A"], x["Bm"], x["Cm"], x["Dskip"], x["theta"], x["lam"],
+                       disc=w.disc, is_complex=w.is_complex, return_q=True, **kw)
+
+
+@pytest.mark.parametrize("algo", ["sequential", "chunked"])
+@pytest.mark.parametrize("mode", list(MODES))
+def test_two_calls_equal_one_shot(mode, algo):
+    """L = 333 split at step 200 (inside a tile): y of both calls and the final h, q."""
+    w = MODES[mode].scaled(batch=2, dim=37, seqlen=333)
+    trap = w.disc == "trap"
+    inp = make_inputs(w, seed=7, device="cuda")
+    split = 200
+    first, second = _time_slice(inp, 0, split), _time_slice(inp, split, w.seqlen)
+    y1, h1, q1 = ssm_scan_fwd_ex(*_args(first), disc=w.disc, algo=algo, want_q_last=trap)
+    y2, h2, q2 = ssm_scan_fwd_ex(*_args(second), h0=h1, q0=q1, disc=w.disc, algo=algo, want_q_last=trap)
+    torch.cuda.synchronize()
+    ref_y, ref_h, ref_q = _oracle(w, all_channels(inp))
+    err_y, err_h = _errs(w, torch.cat([y1, y2], dim=1), h2, ref_y, ref_h)
+    err_q = 0.0
+    if trap:
+        err_q = rel_err_complex(_host(q2), ref_q) if w.is_complex else rel_err(_host(q2), ref_q)
+    tol = TOL[w.io_dtype]
+    print(f"{mode} algo={algo} err_y={err_y:.3e} err_h={err_h:.3e} err_q={err_q:.3e}", flush=True)
+    assert err_y <= tol and err_h <= tol and err_q <= tol, (err_y, err_h, err_q, tol)
+
+
+@pytest.mark.parametrize("algo", ["sequential", "chunked"])
+@pytest.mark.parametrize("mode", list(MODES))
+def test_nonzero_initial_state(mode, algo):
+    """Random h0 (and q0) against the oracle continued from the same values."""
+    w = MODES[mode].scaled(batch=2, dim=37, seqlen=150)
+    trap = w.disc == "trap"
+    inp = make_inputs(w, seed=9, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    shape = (w.batch, w.dim, w.dstate) + ((2,) if w.is_complex else ())
+    h0 = torch.randn(shape, generator=g, device="cuda")
+    q0 = torch.randn(shape, generator=g, device="cuda") if trap else None
+    y, h, q = ssm_scan_fwd_ex(*_args(inp), h0=h0, q0=q0, disc=w.disc, algo=algo, want_q_last=trap)
+    torch.cuda.synchronize()
+    ref_y, ref_h, ref_q = _oracle(w, all_channels(inp), h0=_host(h0), q0=_host(q0))
+    err_y, err_h = _errs(w, y, h, ref_y, ref_h)
+    tol = TOL[w.io_dtype]
+    print(f"{mode} algo={algo} err_y={err_y:.3e} err_h={err_h:.3e}", flush=True)
+    assert err_y <= tol and err_h <= tol, (err_y, err_h, tol)
+    if trap:
+        q_host = _host(q)
+        assert np.allclose(q_host, ref_q, rtol=1e-6, atol=0), "q_last = B_{L-1} u_{L-1}"
+
+
+@pytest.mark.parametrize("N", [16, 5, 64])
+@pytest.mark.parametrize("mode", list(MODES))
+def test_decode_after_prompt(mode, N):
+    """A 60-step prompt scanned, then 12 decode steps: equals one scan of 72 steps."""
+    w = MODES[mode].scaled(batch=3, dim=40, seqlen=72, dstate=N)
+    trap = w.disc == "trap"
+    inp = make_inputs(w, seed=11, device="cuda")
+    prompt = 60
+    y0, h, q = ssm_scan_fwd_ex(*_args(_time_slice(inp, 0, prompt)), disc=w.disc, want_q_last=trap)
+    ys = [y0]
+    for t in range(prompt, w.seqlen):
+        x = _step_inputs(inp, t)
+        ys.append(ssm_scan_step(*_args(x), h=h, q=q, disc=w.disc)[:, None, :])
+    torch.cuda.synchronize()
+    ref_y, ref_h, _ = _oracle(w, all_channels(inp))
+    err_y, err_h = _errs(w, torch.cat(ys, dim=1), h, ref_y, ref_h)
+    tol = TOL[w.io_dtype]
+    print(f"{mode} N={N} err_y={err_y:.3e} err_h={err_h:.3e}", flush=True)
+    assert err_y <= tol and err_h <= tol, (err_y, err_h, tol)
+
+
+@pytest.mark.parametrize("mode", ["real_trap_f32", "complex_trap_f32", "complex_trap_bf16", "complex_euler_f32"])
+def test_decode_from_empty_history(mode):
+    """Decoding from h = 0 (and q = 0) step by step equals the scan from step 0."""
+    w = MODES[mode].scaled(batch=2, dim=24, seqlen=20)
+    trap = w.disc == "trap"
+    inp = make_inputs(w, seed=13, device="cuda")
+    shape = (w.batch, w.dim, w.dstate) + ((2,) if w.is_complex else ())
+    h = torch.zeros(shape, device="cuda")
+    q = torch.zeros(shape, device="cuda") if trap else None
+    ys = [ssm_scan_step(*_args(_step_inputs(inp, t)), h=h, q=q, disc=w.disc)[:, None, :] for t in range(w.seqlen)]
+    torch.cuda.synchronize()
+    ref_y, ref_h, _ = _oracle(w, all_channels(inp))
+    err_y, err_h = _errs(w, torch.cat(ys, dim=1), h, ref_y, ref_h)
+    tol = TOL[w.io_dtype]
+    assert err_y <= tol and err_h <= tol, (err_y, err_h, tol)
