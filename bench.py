@@ -18,7 +18,10 @@ already resident in HBM.  Rank 0 prints one JSON line:
 
 The default workload is the largest one (B=1, D=1024, L=2^20, N=16, complex
 exp-trapezoidal, bf16 I/O, fp32 arithmetic), on which the HBM-bandwidth target
-is stated.
+is stated.  A decode workload (--workload decode_...) times ssm_scan_step
+instead: a step is one token for every sequence of the batch, the state read
+and written in HBM, and the same line is printed with B*D tokens*channels per
+step.
 """
 from __future__ import annotations
 
@@ -54,6 +57,20 @@ def algorithmic_bytes(w) -> int:
             + 2 * e * B * L * N * (1 + cplx)    # B, C
             + 4 * D * N + 4 * D                 # A, D
             + 4 * B * D * N * (1 + cplx))       # h_last
+
+
+def decode_algorithmic_bytes(w) -> int:
+    """One decode step: inputs of the step and the previous step's u and B rows
+    read once, the state read and written once, y written once."""
+    e = 4 if w.io_dtype == "f32" else 2
+    B, D, N = w.batch, w.dim, w.dstate
+    trap = 1 if w.disc == "trap" else 0
+    cplx = 1 if w.is_complex else 0
+    return (e * B * D * (3 + 2 * trap)           # u, delta, y, (lambda, u_prev)
+            + e * B * D * N * cplx               # theta
+            + e * B * N * (1 + cplx) * (2 + trap)  # B, C, (B_prev)
+            + 4 * D * N + 4 * D                  # A, D
+            + 2 * 4 * B * D * N * (1 + cplx))    # h read and written
 
 
 def kernel_source_hash() -> str:
@@ -118,6 +135,93 @@ def cpu_baseline(inputs, w, y_gpu, target_s: float):
     }
 
 
+def cpu_baseline_decode(inputs, w, h_start, target_s: float):
+    """Time the fp64 oracle on one decode step of a channel sample (the oracle
+    run for one step from the given state), repeated up to `target_s` s."""
+    import numpy as np
+
+    import oracle
+    from selective_state_space_42_amd.inputs import channel_sample
+
+    threads = max(1, min(os.cpu_count() or 1, 64))
+    idx = sorted(np.random.default_rng(0).permutation(w.dim)[:max(threads, 64)].tolist())
+    x = channel_sample(inputs, idx)
+    cur = {k: (None if v is None else (v[:, 1:2] if k in ("u", "delta", "lam", "theta", "Bm", "Cm") else v))
+           for k, v in x.items()}
+    h0 = h_start[:, idx].float().cpu().double().numpy()
+    q0 = None
+    if w.disc == "trap":  # q_{-1} = B_{-1} u_{-1}, previous step's rows
+        bp, up = x["Bm"][:, 0], x["u"][:, 0]
+        q0 = (bp[:, None, ...] * (up[:, :, None, None] if w.is_complex else up[:, :, None]))
+    spent, calls = 0.0, 0
+    while spent < target_s:
+        t0 = time.perf_counter()
+        oracle.scan(cur["u"], cur["delta"], cur["A"], cur["Bm"], cur["Cm"], cur["Dskip"], cur["theta"],
+                    cur["lam"], disc=w.disc, is_complex=w.is_complex, h0=h0, q0=q0, nthreads=threads)
+        spent += time.perf_counter() - t0
+        calls += 1
+    tc = calls * w.batch * len(idx)
+    return {
+        "value": tc / spent, "unit": UNIT, "cores": min(threads, len(idx)), "kind": "oracle",
+        "sample": f"{len(idx)} of {w.dim} channels (random, seed 0), every batch row, one decode step from a "
+                  f"given state, repeated {calls} times: {tc} tokens*channels in {spent:.1f} s of fp64 C "
+                  f"oracle time",
+    }
+
+
+def bench_decode(args, w, torch, dev):
+    from selective_state_space_42_amd.inputs import make_inputs
+    from selective_state_space_42_amd.scan import ssm_scan_step
+
+    log(f"generating {w.name} on {torch.cuda.get_device_name(dev)}")
+    inputs = make_inputs(w, device=dev)
+    prev = {k: (None if v is None else v[:, 0].contiguous()) for k, v in inputs.items()
+            if k in ("u", "Bm")}
+    cur = {k: (None if v is None else (v[:, 1].contiguous() if k in ("u", "delta", "lam", "theta", "Bm", "Cm")
+                                        else v)) for k, v in inputs.items()}
+    h_shape = (w.batch, w.dim, w.dstate, 2) if w.is_complex else (w.batch, w.dim, w.dstate)
+    g = torch.Generator(device=dev).manual_seed(1)
+    h = torch.randn(h_shape, generator=g, device=dev)
+    h_start = h.clone()
+    y = torch.empty_like(cur["u"])
+    stream = torch.cuda.current_stream(dev)
+    trap = w.disc == "trap"
+
+    def step():
+        ssm_scan_step(cur["u"], cur["delta"], cur["A"], cur["Bm"], cur["Cm"], cur["Dskip"], cur["theta"],
+                      cur["lam"], h=h, u_prev=prev["u"] if trap else None, B_prev=prev["Bm"] if trap else None,
+                      disc=w.disc, y=y, stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    log(f"timed {args.steps} decode steps: {ms * 1e3:.2f} us/step")
+    alg_bytes = decode_algorithmic_bytes(w)
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": w.batch * w.dim / (ms * 1e-3), "unit": UNIT, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": 1, "dstate": w.dstate,
+                   "disc": w.disc, "complex": w.is_complex, "io_dtype": w.io_dtype, "algo": "step"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profile(w.name, "step"),
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a channel sample")
+        out["cpu_baseline"] = cpu_baseline_decode(inputs, w, h_start, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration(torch, dev, nbytes: int, steps: int, warmup: int):
     """A plain copy of known size: reads and writes `nbytes` per launch."""
     n = (nbytes + 15) // 16 * 4
@@ -158,15 +262,18 @@ def main():
 
     import torch
 
-    from selective_state_space_42_amd.inputs import WORKLOADS, make_inputs
+    from selective_state_space_42_amd.inputs import DECODE_WORKLOADS, WORKLOADS, make_inputs
     from selective_state_space_42_amd.scan import make_desc, ssm_scan_fwd, ssm_scan_workspace_bytes
 
-    w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.copy_calibration:
         copy_calibration(torch, dev, args.copy_calibration, args.steps, args.warmup)
         return
+    if args.workload in DECODE_WORKLOADS:
+        bench_decode(args, DECODE_WORKLOADS[args.workload], torch, dev)
+        return
+    w = WORKLOADS[args.workload]
     log(f"generating {w.name} on {torch.cuda.get_device_name(dev)}")
     inputs = make_inputs(w, device=dev)
     torch.cuda.synchronize()

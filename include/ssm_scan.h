@@ -184,21 +184,22 @@ int ssm_scan_fwd_ex(const ssm_scan_desc_t *desc, const void *u, const void *delt
  *   A [D][N] fp32, D [D] fp32 or NULL     as for ssm_scan_fwd
  *   B, C   [B][N] or [B][N][2] io dtype   projections of this step
  *   theta  [B][D][N] io dtype or NULL     rotation of this step (complex state)
+ *   u_prev [B][D] io dtype, or NULL       EXP_TRAPEZOIDAL: u and B of the previous
+ *   B_prev layout of B, or NULL           step, whose product q_{t-1} = B_{t-1} u_{t-1}
+ *                                         the trapezoid's beta multiplies; both NULL
+ *                                         means no previous step (q_{t-1} = 0);
+ *                                         must be NULL for the other discretisations
  *   h      [B][D][N] or [B][D][N][2] fp32 read as h_{t-1}, overwritten with h_t
  *                                         (required)
- *   q      same layout as h, fp32         EXP_TRAPEZOIDAL: read as q_{t-1} = B_{t-1} u_{t-1}
- *                                         and overwritten with q_t = B_t u_t
- *                                         (required); must be NULL otherwise
  *   y      [B][D] io dtype                output of this step (written)
  *
- * h and q of ssm_scan_fwd_ex's h_last and q_last continue a scanned prompt;
- * zeros start from an empty history.  N may be up to 64.  No workspace.
- * h and q must not alias each other or any other argument.  Returns an
- * ssm_status_t.
+ * After a prompt scanned by ssm_scan_fwd_ex, its h_last is the state and the
+ * prompt's last u and B rows are u_prev and B_prev.  N may be up to 64.  No
+ * workspace.  h must not alias any other argument.  Returns an ssm_status_t.
  */
 int ssm_scan_step(const ssm_scan_desc_t *desc, const void *u, const void *delta, const float *A,
                   const void *B, const void *C, const float *D, const void *theta, const void *lambda,
-                  float *h, float *q, void *y, void *stream);
+                  const void *u_prev, const void *B_prev, float *h, void *y, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *ssm_scan_status_string(int status);

@@ -81,26 +81,37 @@ int launch_sequential(const ssm_scan_desc_t* d, const ssm::SeqParams& p, hipStre
     return hip_status(hipGetLastError());
 }
 
-template <typename T>
-int launch_step(const ssm_scan_desc_t* d, const ssm::StepParams& p, hipStream_t s) {
+template <typename T, bool PAIRS>
+int launch_step_k(const ssm_scan_desc_t* d, const ssm::StepParams& p, hipStream_t s) {
     const int64_t waves = (d->batch * d->dim + (64 / p.lpc) - 1) / (64 / p.lpc);
     const int64_t blocks = (waves + 3) / 4;
     if (blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
     const dim3 grid(static_cast<unsigned>(blocks)), block(256);
     if (d->is_complex) {
         if (d->disc == SSM_DISC_EXP_EULER)
-            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kEuler, true>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kEuler, true, PAIRS>), grid, block, 0, s, p);
         else
-            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kTrap, true>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kTrap, true, PAIRS>), grid, block, 0, s, p);
     } else {
         if (d->disc == SSM_DISC_ZOH)
-            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kZOH, false>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kZOH, false, PAIRS>), grid, block, 0, s, p);
         else if (d->disc == SSM_DISC_EXP_EULER)
-            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kEuler, false>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kEuler, false, PAIRS>), grid, block, 0, s, p);
         else
-            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kTrap, false>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kTrap, false, PAIRS>), grid, block, 0, s, p);
     }
     return hip_status(hipGetLastError());
+}
+
+// The paired step kernel reads each lane's two states with one vector load
+// per array: N even and every array aligned to a pair of its elements.
+template <typename T>
+int launch_step(const ssm_scan_desc_t* d, const ssm::StepParams& p, hipStream_t s) {
+    const size_t es = sizeof(T), cw = d->is_complex ? 2 : 1;
+    const bool pairs = d->dstate % 2 == 0 && aligned(p.h, 8 * cw) && aligned(p.A, 8) &&
+                       aligned(p.B, 2 * cw * es) && aligned(p.C, 2 * cw * es) &&
+                       (!p.B_prev || aligned(p.B_prev, 2 * cw * es)) && (!p.theta || aligned(p.theta, 2 * es));
+    return pairs ? launch_step_k<T, true>(d, p, s) : launch_step_k<T, false>(d, p, s);
 }
 
 // Pointer checks shared by the scan and the step: required inputs present,
@@ -207,21 +218,22 @@ int ssm_scan_fwd_ex(const ssm_scan_desc_t* desc, const void* u, const void* delt
 }
 
 int ssm_scan_step(const ssm_scan_desc_t* desc, const void* u, const void* delta, const float* A, const void* B,
-                  const void* C, const float* D, const void* theta, const void* lambda, float* h, float* q,
-                  void* y, void* stream) {
+                  const void* C, const float* D, const void* theta, const void* lambda, const void* u_prev,
+                  const void* B_prev, float* h, void* y, void* stream) {
     int st = check_desc(desc);
     if (st != SSM_OK) return st;
     if (desc->seqlen != 1) return SSM_ERR_INVALID_ARGUMENT;
     st = check_inputs(desc, u, delta, A, B, C, D, theta, lambda, y);
     if (st != SSM_OK) return st;
     const bool trap = desc->disc == SSM_DISC_EXP_TRAPEZOIDAL;
-    if (!h || trap != (q != nullptr)) return SSM_ERR_INVALID_ARGUMENT;
-    const size_t ss = desc->is_complex ? 8 : 4;
-    if (!aligned(h, ss) || (q && !aligned(q, ss))) return SSM_ERR_INVALID_ARGUMENT;
+    if (!h || !aligned(h, desc->is_complex ? 8 : 4)) return SSM_ERR_INVALID_ARGUMENT;
+    if ((u_prev != nullptr) != (B_prev != nullptr) || (!trap && u_prev)) return SSM_ERR_INVALID_ARGUMENT;
+    const size_t es = desc->io_dtype == SSM_DTYPE_F32 ? 4 : 2;
+    if ((u_prev && !aligned(u_prev, es)) || (B_prev && !aligned(B_prev, es))) return SSM_ERR_INVALID_ARGUMENT;
 
     ssm::StepParams p{};
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.theta = theta;
-    p.lambda = lambda; p.h = h; p.q = q; p.y = y;
+    p.lambda = lambda; p.u_prev = u_prev; p.B_prev = B_prev; p.h = h; p.y = y;
     p.batch = desc->batch; p.dim = desc->dim; p.dstate = desc->dstate;
     p.lpc = next_pow2((desc->dstate + 1) / 2);
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -73,6 +73,16 @@ WORKLOADS = {
         "neg_exp_uniform", 0.5),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
+
+# Decode-step workloads: one token per call with the state kept in memory, a
+# serving batch of B sequences.  seqlen = 2 holds the previous step (whose u
+# and B the trapezoid needs) and the current one; the fields are drawn as for
+# the complex exp-trapezoidal bf16 workload.
+DECODE_WORKLOADS = {
+    "decode_complex_trap_bf16_b256_d2560_n16": Workload(
+        "decode_complex_trap_bf16_b256_d2560_n16", 256, 2560, 2, 16, "trap", True, "bf16", -3.0, 0.5,
+        "neg_exp_uniform", 0.5),
+}
 SEED_BASE = 42
 
 

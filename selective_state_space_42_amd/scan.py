@@ -53,7 +53,7 @@ def _lib():
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_scan_fwd_ex.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 14 + [ctypes.c_size_t, vp]
     lib.ssm_scan_fwd_ex.restype = ctypes.c_int
-    lib.ssm_scan_step.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 12
+    lib.ssm_scan_step.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 13
     lib.ssm_scan_step.restype = ctypes.c_int
     lib.ssm_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
     lib.ssm_scan_workspace_bytes.restype = ctypes.c_size_t
@@ -157,11 +157,13 @@ def ssm_scan_fwd_ex(u, delta, A, B, C, D=None, theta=None, lam=None, h0=None, q0
     return y, h_last, q_last
 
 
-def ssm_scan_step(u, delta, A, B, C, D=None, theta=None, lam=None, *, h, q=None, disc: str, y=None, stream=None):
-    """One decode step, updating h (and q for the trapezoid) in place; returns y.
+def ssm_scan_step(u, delta, A, B, C, D=None, theta=None, lam=None, *, h, u_prev=None, B_prev=None, disc: str,
+                  y=None, stream=None):
+    """One decode step, updating h in place; returns y.
 
-    u, delta, lam (B,D); A (D,N) fp32; B, C (B,N) real or (B,N,2) complex;
-    D (D,) fp32; theta (B,D,N); h, q (B,D,N) or (B,D,N,2) fp32.
+    u, delta, lam, u_prev (B,D); A (D,N) fp32; B, C, B_prev (B,N) real or
+    (B,N,2) complex; D (D,) fp32; theta (B,D,N); h (B,D,N) or (B,D,N,2) fp32.
+    u_prev and B_prev (the previous step's u and B) are for the trapezoid.
     """
     Bsz, Dm = u.shape
     N = A.shape[1]
@@ -172,7 +174,8 @@ def ssm_scan_step(u, delta, A, B, C, D=None, theta=None, lam=None, *, h, q=None,
     if stream is None:
         stream = torch.cuda.current_stream(u.device).cuda_stream if u.is_cuda else 0
     st = _lib().ssm_scan_step(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                              _ptr(theta), _ptr(lam), _ptr(h), _ptr(q), _ptr(y), ctypes.c_void_p(stream))
+                              _ptr(theta), _ptr(lam), _ptr(u_prev), _ptr(B_prev), _ptr(h), _ptr(y),
+                              ctypes.c_void_p(stream))
     if st != 0:
         raise ScanError(st, "ssm_scan_step")
     return y

@@ -120,10 +120,10 @@ def call_ex(desc, u=P, delta=P, A=P, B=P, C=P, D=0, theta=0, lam=0, h0=0, q0=0, 
                                None)
 
 
-def call_step(desc, u=P, delta=P, A=P, B=P, C=P, D=0, theta=0, lam=0, h=P, q=0, y=P):
+def call_step(desc, u=P, delta=P, A=P, B=P, C=P, D=0, theta=0, lam=0, u_prev=0, B_prev=0, h=P, y=P):
     lib = scan._lib()
     dp = None if desc is None else ctypes.byref(desc)
-    args = [u, delta, A, B, C, D, theta, lam, h, q, y]
+    args = [u, delta, A, B, C, D, theta, lam, u_prev, B_prev, h, y]
     return lib.ssm_scan_step(dp, *[ctypes.c_void_p(a) if a else None for a in args], None)
 
 
@@ -143,12 +143,14 @@ def test_continuation_argument_rules():
 
 def test_step_argument_rules():
     assert call_step(None) == INVALID
-    assert call_step(desc(L=2)) == INVALID                      # one step per call
-    assert call_step(desc(L=1), h=0) == INVALID                 # state required
-    assert call_step(desc(L=1, disc="trap"), lam=P) == INVALID  # trapezoid needs q
-    assert call_step(desc(L=1, disc="euler"), q=P) == INVALID   # q only for the trapezoid
+    assert call_step(desc(L=2)) == INVALID                              # one step per call
+    assert call_step(desc(L=1), h=0) == INVALID                         # state required
+    assert call_step(desc(L=1, disc="trap")) == INVALID                 # trapezoid needs lambda
+    assert call_step(desc(L=1, disc="trap"), lam=P, u_prev=P) == INVALID  # u_prev and B_prev together
+    assert call_step(desc(L=1, disc="trap"), lam=P, B_prev=P) == INVALID
+    assert call_step(desc(L=1, disc="euler"), u_prev=P, B_prev=P) == INVALID  # trapezoid only
     assert call_step(desc(L=1, cplx=True), h=P + 4) == INVALID
-    assert call_step(desc(L=1, disc="trap"), lam=P, q=P + 2) == INVALID
+    assert call_step(desc(L=1, disc="trap"), lam=P, u_prev=P + 2, B_prev=P) == INVALID
     assert call_step(desc(L=1), u=P + 2) == INVALID
     assert call_step(desc(L=1, N=65)) == UNSUPPORTED
     assert call_step(desc(L=1, disc="zoh", cplx=True)) == UNSUPPORTED

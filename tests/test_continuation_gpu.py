@@ -2,7 +2,8 @@
 
 ssm_scan_fwd_ex takes the state before step 0 (h0) and the trapezoid's
 previous input term (q0 = B_{-1} u_{-1}) and returns q_last; ssm_scan_step
-advances a state kept in memory by one step.  Both are compared with the fp64
+advances a state kept in memory by one step (the trapezoid's previous term
+from the previous step's u and B rows).  Both are compared with the fp64
 oracle, whose own continuation is pinned bitwise to its one-shot result
 (tests/test_oracle_pins.py):
 
@@ -129,11 +130,12 @@ def test_decode_after_prompt(mode, N):
     trap = w.disc == "trap"
     inp = make_inputs(w, seed=11, device="cuda")
     prompt = 60
-    y0, h, q = ssm_scan_fwd_ex(*_args(_time_slice(inp, 0, prompt)), disc=w.disc, want_q_last=trap)
+    y0, h, _ = ssm_scan_fwd_ex(*_args(_time_slice(inp, 0, prompt)), disc=w.disc)
     ys = [y0]
     for t in range(prompt, w.seqlen):
-        x = _step_inputs(inp, t)
-        ys.append(ssm_scan_step(*_args(x), h=h, q=q, disc=w.disc)[:, None, :])
+        x, xp = _step_inputs(inp, t), _step_inputs(inp, t - 1)
+        prev = dict(u_prev=xp["u"], B_prev=xp["Bm"]) if trap else {}
+        ys.append(ssm_scan_step(*_args(x), h=h, disc=w.disc, **prev)[:, None, :])
     torch.cuda.synchronize()
     ref_y, ref_h, _ = _oracle(w, all_channels(inp))
     err_y, err_h = _errs(w, torch.cat(ys, dim=1), h, ref_y, ref_h)
@@ -144,14 +146,19 @@ def test_decode_after_prompt(mode, N):
 
 @pytest.mark.parametrize("mode", ["real_trap_f32", "complex_trap_f32", "complex_trap_bf16", "complex_euler_f32"])
 def test_decode_from_empty_history(mode):
-    """Decoding from h = 0 (and q = 0) step by step equals the scan from step 0."""
+    """Decoding from h = 0 with no previous step equals the scan from step 0."""
     w = MODES[mode].scaled(batch=2, dim=24, seqlen=20)
     trap = w.disc == "trap"
     inp = make_inputs(w, seed=13, device="cuda")
     shape = (w.batch, w.dim, w.dstate) + ((2,) if w.is_complex else ())
     h = torch.zeros(shape, device="cuda")
-    q = torch.zeros(shape, device="cuda") if trap else None
-    ys = [ssm_scan_step(*_args(_step_inputs(inp, t)), h=h, q=q, disc=w.disc)[:, None, :] for t in range(w.seqlen)]
+    ys = []
+    for t in range(w.seqlen):
+        prev = {}
+        if trap and t > 0:  # no previous step at t = 0
+            xp = _step_inputs(inp, t - 1)
+            prev = dict(u_prev=xp["u"], B_prev=xp["Bm"])
+        ys.append(ssm_scan_step(*_args(_step_inputs(inp, t)), h=h, disc=w.disc, **prev)[:, None, :])
     torch.cuda.synchronize()
     ref_y, ref_h, _ = _oracle(w, all_channels(inp))
     err_y, err_h = _errs(w, torch.cat(ys, dim=1), h, ref_y, ref_h)
