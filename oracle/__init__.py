@@ -13,9 +13,13 @@ Functions:
   combine()  -- the operator combine (a2,b2)(x)(a1,b1) = (a2 a1, a2 b1 + b2)
                 from fengwang.github.io "complex parallel scan", section "the
                 mathematical essence of the parallel scan".
+  scan_bwd() -- gradients of the scan by reverse mode of the same sequential
+                definition (ssm_oracle_bwd.c).
 
-Parity status: every function here is pinned by tests/test_oracle_pins.py
-against closed forms, special cases and invariants; none is "parity unpinned".
+Parity status: every function here is pinned -- scan() and combine() by
+tests/test_oracle_pins.py against closed forms, special cases and invariants,
+scan_bwd() by tests/test_oracle_bwd_pins.py against central finite
+differences of scan(); none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -27,6 +31,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssm_oracle.c")
+_SRC_BWD = os.path.join(_HERE, "ssm_oracle_bwd.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 DISC = {"zoh": 0, "euler": 1, "trap": 2}
@@ -38,7 +43,7 @@ def build() -> str:
     """Compile the oracle with gcc.  Returns the path of the shared library."""
     cmd = [
         "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
-        "-ffp-contract=off", "-pthread", "-o", _LIB, _SRC, "-lm",
+        "-ffp-contract=off", "-pthread", "-o", _LIB, _SRC, _SRC_BWD, "-lm",
     ]
     subprocess.run(cmd, check=True)
     return _LIB
@@ -48,13 +53,15 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(_SRC), os.path.getmtime(_SRC_BWD)):
         build()
     lib = ctypes.CDLL(_LIB)
     dp = ctypes.c_void_p
     i64 = ctypes.c_int64
     lib.oracle_scan_f64.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int] + [dp] * 13 + [ctypes.c_int]
     lib.oracle_scan_f64.restype = ctypes.c_int
+    lib.oracle_scan_bwd_f64.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int] + [dp] * 20
+    lib.oracle_scan_bwd_f64.restype = ctypes.c_int
     lib.oracle_combine_f64.argtypes = [i64, dp, dp, dp, dp, dp, dp]
     lib.oracle_combine_f64.restype = None
     _lib = lib
@@ -99,6 +106,37 @@ def scan(u, delta, A, Bm, Cm, Dskip=None, theta=None, lam=None, *, disc: str, is
     if return_q:
         return y, h_last, q_last
     return y, h_last
+
+
+def scan_bwd(u, delta, A, Bm, Cm, Dskip=None, theta=None, lam=None, *, disc: str, is_complex: bool,
+             dy, dh_last=None, h0=None):
+    """Gradients of L = sum(dy * y) + <dh_last, h_last> w.r.t. every input.
+
+    Returns a dict with du, ddelta (B,L,D); dA (D,N); dB, dC (layout of Bm);
+    dD (D,) when Dskip is given; dtheta (B,L,D,N) when theta is given;
+    dlambda (B,L,D) for the trapezoid; dh0 (layout of h_last).  Complex
+    gradients are (d/dre, d/dim).
+    """
+    lib = _load()
+    u, delta, A, Bm, Cm, dy = map(_f64, (u, delta, A, Bm, Cm, dy))
+    Dskip, theta, lam, h0, dh_last = map(_f64, (Dskip, theta, lam, h0, dh_last))
+    B, L, D = u.shape
+    N = A.shape[1]
+    cw = (2,) if is_complex else ()
+    out = dict(du=np.empty((B, L, D)), ddelta=np.empty((B, L, D)), dA=np.empty((D, N)),
+               dB=np.empty(Bm.shape), dC=np.empty(Cm.shape),
+               dD=np.empty((D,)) if Dskip is not None else None,
+               dtheta=np.empty((B, L, D, N)) if theta is not None else None,
+               dlambda=np.empty((B, L, D)) if disc == "trap" else None,
+               dh0=np.empty((B, D, N) + cw))
+    rc = lib.oracle_scan_bwd_f64(
+        B, L, D, N, DISC[disc], int(bool(is_complex)),
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(theta), _ptr(lam), _ptr(h0),
+        _ptr(dy), _ptr(dh_last), *(_ptr(out[k]) for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dtheta",
+                                                          "dlambda", "dh0")))
+    if rc != 0:
+        raise ValueError(f"oracle_scan_bwd_f64 returned {rc}")
+    return out
 
 
 def combine(a2, b2, a1, b1):
