@@ -201,6 +201,48 @@ int ssm_scan_step(const ssm_scan_desc_t *desc, const void *u, const void *delta,
                   const void *B, const void *C, const float *D, const void *theta, const void *lambda,
                   const void *u_prev, const void *B_prev, float *h, void *y, void *stream);
 
+/* Bytes of workspace ssm_scan_bwd needs for `desc`: the state before every
+ * 32-step segment, ceil(L/32) * B * D * N * (8 complex, 4 real) bytes
+ * (e.g. 1.34 GB for B=4, L=8192, D=2560, N=16 complex).  0 for an invalid
+ * descriptor. */
+size_t ssm_scan_bwd_workspace_bytes(const ssm_scan_desc_t *desc);
+
+/*
+ * Gradients of the scan (the backward pass), for
+ *     Loss = sum(dy * y) + <dh_last, h_last>
+ * with y, h_last the outputs of ssm_scan_fwd_ex(..., h0, q0 = NULL, ...) on the
+ * same inputs.  The forward states are regenerated from per-segment
+ * snapshots during the reverse sweep and never stored whole, which is how
+ * the fengwang.github.io essay describes training a scan (its opening
+ * section, and its hardware-challenges section on the backward kernel with
+ * recomputation); the gradient formulas are reverse-mode differentiation of
+ * the recurrence and discretisations above.
+ *
+ *   inputs   u, delta, A, B, C, D, theta, lambda, h0 as for ssm_scan_fwd_ex
+ *            (h0 may be NULL; desc->algo is ignored)
+ *   dy       [B][L][D] io dtype        upstream gradient of y
+ *   dh_last  layout of h_last, or NULL upstream gradient of h_last (NULL: 0)
+ * outputs (fp32, written; complex gradients are (dL/dRe, dL/dIm)):
+ *   du, ddelta        [B][L][D]                   required
+ *   dA                [D][N]                      required (sum over b, t)
+ *   dB, dC            layout of B and C           required (sum over d)
+ *   dD                [D], or NULL                sum over b, t of dy * u
+ *   dtheta            [B][L][D][N], or NULL       only when theta is given
+ *   dlambda           [B][L][D]                   required for EXP_TRAPEZOIDAL,
+ *                                                 NULL otherwise
+ *   dh0               layout of h_last, or NULL   gradient of the state before step 0
+ *   workspace         ssm_scan_bwd_workspace_bytes(desc) bytes, 256-byte aligned
+ *
+ * dA, dB, dC and dD are sums taken with atomic adds, so their last bits can
+ * vary between runs.  Outputs must not alias inputs or each other.  Returns
+ * an ssm_status_t.
+ */
+int ssm_scan_bwd(const ssm_scan_desc_t *desc, const void *u, const void *delta, const float *A,
+                 const void *B, const void *C, const float *D, const void *theta, const void *lambda,
+                 const float *h0, const void *dy, const float *dh_last, float *du, float *ddelta,
+                 float *dA, float *dB, float *dC, float *dD, float *dtheta, float *dlambda, float *dh0,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *ssm_scan_status_string(int status);
 

@@ -14,6 +14,7 @@
 #include "kernel_sequential.h"
 #include "kernel_chunked.h"
 #include "kernel_step.h"
+#include "kernel_backward.h"
 
 namespace {
 
@@ -112,6 +113,45 @@ int launch_step(const ssm_scan_desc_t* d, const ssm::StepParams& p, hipStream_t 
                        aligned(p.B, 2 * cw * es) && aligned(p.C, 2 * cw * es) &&
                        (!p.B_prev || aligned(p.B_prev, 2 * cw * es)) && (!p.theta || aligned(p.theta, 2 * es));
     return pairs ? launch_step_k<T, true>(d, p, s) : launch_step_k<T, false>(d, p, s);
+}
+
+template <typename T, int DISC, bool CPLX>
+void launch_bwd_pair(const ssm::BwdParams& p, dim3 grid, hipStream_t s) {
+    hipLaunchKernelGGL((ssm::bwd_ckpt_kernel<T, DISC, CPLX>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((ssm::bwd_main_kernel<T, DISC, CPLX>), grid, dim3(256), 0, s, p);
+}
+
+template <typename T>
+int launch_bwd(const ssm_scan_desc_t* d, const ssm::BwdParams& p, hipStream_t s) {
+    const int64_t waves = (d->batch * d->dim + (64 / p.lpc) - 1) / (64 / p.lpc);
+    const int64_t blocks = (waves + 3) / 4;
+    if (blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+    const int64_t cw = d->is_complex ? 2 : 1;
+    const int64_t na = d->dim * d->dstate, nb = d->batch * d->seqlen * d->dstate * cw, nd = p.dD ? d->dim : 0;
+    int64_t zb = (na + 2 * nb + nd + 255) / 256;
+    if (zb > 16384) zb = 16384;
+    hipLaunchKernelGGL(ssm::bwd_zero_kernel, dim3(static_cast<unsigned>(zb)), dim3(256), 0, s, p.dA, na, p.dB, nb,
+                       p.dC, nb, p.dD, nd);
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (d->is_complex) {
+        if (d->disc == SSM_DISC_EXP_EULER)
+            launch_bwd_pair<T, ssm::kEuler, true>(p, grid, s);
+        else
+            launch_bwd_pair<T, ssm::kTrap, true>(p, grid, s);
+    } else {
+        if (d->disc == SSM_DISC_ZOH)
+            launch_bwd_pair<T, ssm::kZOH, false>(p, grid, s);
+        else if (d->disc == SSM_DISC_EXP_EULER)
+            launch_bwd_pair<T, ssm::kEuler, false>(p, grid, s);
+        else
+            launch_bwd_pair<T, ssm::kTrap, false>(p, grid, s);
+    }
+    return hip_status(hipGetLastError());
+}
+
+size_t bwd_workspace(const ssm_scan_desc_t* d) {
+    const int64_t nseg = (d->seqlen + ssm::bwd::kSeg - 1) / ssm::bwd::kSeg;
+    return static_cast<size_t>(nseg * d->batch * d->dim * d->dstate * (d->is_complex ? 8 : 4));
 }
 
 // Pointer checks shared by the scan and the step: required inputs present,
@@ -238,6 +278,47 @@ int ssm_scan_step(const ssm_scan_desc_t* desc, const void* u, const void* delta,
     p.lpc = next_pow2((desc->dstate + 1) / 2);
     hipStream_t s = static_cast<hipStream_t>(stream);
     return desc->io_dtype == SSM_DTYPE_F32 ? launch_step<float>(desc, p, s) : launch_step<uint16_t>(desc, p, s);
+}
+
+size_t ssm_scan_bwd_workspace_bytes(const ssm_scan_desc_t* desc) {
+    if (check_desc(desc) != SSM_OK) return 0;
+    return bwd_workspace(desc);
+}
+
+int ssm_scan_bwd(const ssm_scan_desc_t* desc, const void* u, const void* delta, const float* A, const void* B,
+                 const void* C, const float* D, const void* theta, const void* lambda, const float* h0,
+                 const void* dy, const float* dh_last, float* du, float* ddelta, float* dA, float* dB, float* dC,
+                 float* dD, float* dtheta, float* dlambda, float* dh0, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    int st = check_desc(desc);
+    if (st != SSM_OK) return st;
+    st = check_inputs(desc, u, delta, A, B, C, D, theta, lambda, dy);
+    if (st != SSM_OK) return st;
+    const bool trap = desc->disc == SSM_DISC_EXP_TRAPEZOIDAL;
+    if (!du || !ddelta || !dA || !dB || !dC) return SSM_ERR_INVALID_ARGUMENT;
+    if (trap != (dlambda != nullptr)) return SSM_ERR_INVALID_ARGUMENT;
+    if (dtheta && !theta) return SSM_ERR_INVALID_ARGUMENT;
+    const float* f32[] = {du, ddelta, dA, dB, dC, dD, dtheta, dlambda};
+    for (const float* q : f32)
+        if (q && !aligned(q, 4)) return SSM_ERR_INVALID_ARGUMENT;
+    const size_t ss = desc->is_complex ? 8 : 4;
+    const void* st_ptrs[] = {h0, dh_last, dh0};
+    for (const void* q : st_ptrs)
+        if (q && !aligned(q, ss)) return SSM_ERR_INVALID_ARGUMENT;
+    const size_t need = bwd_workspace(desc);
+    if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(workspace, 256)) return SSM_ERR_INVALID_ARGUMENT;
+
+    ssm::BwdParams p{};
+    p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.theta = theta; p.lambda = lambda;
+    p.h0 = h0; p.dy = dy; p.dh_last = dh_last;
+    p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB; p.dC = dC; p.dD = dD; p.dtheta = dtheta;
+    p.dlambda = dlambda; p.dh0 = dh0;
+    p.ckpt = static_cast<float*>(workspace);
+    p.batch = desc->batch; p.seqlen = desc->seqlen; p.dim = desc->dim; p.dstate = desc->dstate;
+    p.lpc = next_pow2(desc->dstate);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return desc->io_dtype == SSM_DTYPE_F32 ? launch_bwd<float>(desc, p, s) : launch_bwd<uint16_t>(desc, p, s);
 }
 
 }  // extern "C"

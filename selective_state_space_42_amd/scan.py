@@ -55,6 +55,10 @@ def _lib():
     lib.ssm_scan_fwd_ex.restype = ctypes.c_int
     lib.ssm_scan_step.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 13
     lib.ssm_scan_step.restype = ctypes.c_int
+    lib.ssm_scan_bwd.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 21 + [ctypes.c_size_t, vp]
+    lib.ssm_scan_bwd.restype = ctypes.c_int
+    lib.ssm_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
+    lib.ssm_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
     lib.ssm_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_scan_status_string.argtypes = [ctypes.c_int]
@@ -179,3 +183,39 @@ def ssm_scan_step(u, delta, A, B, C, D=None, theta=None, lam=None, *, h, u_prev=
     if st != 0:
         raise ScanError(st, "ssm_scan_step")
     return y
+
+
+def ssm_scan_bwd_workspace_bytes(desc: ScanDesc) -> int:
+    return int(_lib().ssm_scan_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def ssm_scan_bwd(u, delta, A, B, C, D=None, theta=None, lam=None, h0=None, *, dy, dh_last=None, disc: str,
+                 want_dD: bool = True, want_dtheta: bool = True, want_dh0: bool = False, workspace=None,
+                 stream=None) -> dict:
+    """Gradients of sum(dy * y) + <dh_last, h_last>; returns a dict of fp32 tensors
+    du, ddelta, dA, dB, dC, dD, dtheta, dlambda, dh0 (None where not computed)."""
+    Bsz, L, Dm = u.shape
+    N = A.shape[1]
+    is_complex = B.dim() == 4
+    desc = make_desc(Bsz, L, Dm, N, u.dtype, disc, is_complex)
+    f32 = dict(dtype=torch.float32, device=u.device)
+    hshape = (Bsz, Dm, N, 2) if is_complex else (Bsz, Dm, N)
+    g = dict(du=torch.empty((Bsz, L, Dm), **f32), ddelta=torch.empty((Bsz, L, Dm), **f32),
+             dA=torch.empty((Dm, N), **f32), dB=torch.empty(B.shape, **f32), dC=torch.empty(C.shape, **f32),
+             dD=torch.empty((Dm,), **f32) if want_dD else None,
+             dtheta=torch.empty(theta.shape, **f32) if (theta is not None and want_dtheta) else None,
+             dlambda=torch.empty((Bsz, L, Dm), **f32) if disc == "trap" else None,
+             dh0=torch.empty(hshape, **f32) if want_dh0 else None)
+    need = ssm_scan_bwd_workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream if u.is_cuda else 0
+    st = _lib().ssm_scan_bwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                             _ptr(theta), _ptr(lam), _ptr(h0), _ptr(dy), _ptr(dh_last),
+                             *(_ptr(g[k]) for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dtheta", "dlambda",
+                                                    "dh0")),
+                             _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+    if st != 0:
+        raise ScanError(st, "ssm_scan_bwd")
+    return g

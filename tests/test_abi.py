@@ -27,8 +27,9 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = scan._lib()
     names = declared_functions()
-    assert {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_step", "ssm_scan_workspace_bytes",
-            "ssm_scan_status_string", "ssm_scan_abi_version", "ssm_scan_last_hip_error"} <= set(names)
+    assert {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_step", "ssm_scan_bwd", "ssm_scan_workspace_bytes",
+            "ssm_scan_bwd_workspace_bytes", "ssm_scan_status_string", "ssm_scan_abi_version",
+            "ssm_scan_last_hip_error"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -154,3 +155,27 @@ def test_step_argument_rules():
     assert call_step(desc(L=1), u=P + 2) == INVALID
     assert call_step(desc(L=1, N=65)) == UNSUPPORTED
     assert call_step(desc(L=1, disc="zoh", cplx=True)) == UNSUPPORTED
+
+
+def call_bwd(desc, u=P, delta=P, A=P, B=P, C=P, D=0, theta=0, lam=0, h0=0, dy=P, dh=0, du=P, ddelta=P, dA=P,
+             dB=P, dC=P, dD=0, dtheta=0, dlam=0, dh0=0, ws=P, ws_bytes=1 << 40):
+    lib = scan._lib()
+    args = [u, delta, A, B, C, D, theta, lam, h0, dy, dh, du, ddelta, dA, dB, dC, dD, dtheta, dlam, dh0, ws]
+    return lib.ssm_scan_bwd(ctypes.byref(desc), *[ctypes.c_void_p(a) if a else None for a in args], ws_bytes, None)
+
+
+def test_backward_argument_rules():
+    for k in ["u", "dy", "du", "ddelta", "dA", "dB", "dC"]:
+        assert call_bwd(desc(), **{k: 0}) == INVALID, k
+    assert call_bwd(desc(disc="trap"), lam=P) == INVALID               # trapezoid needs dlambda
+    assert call_bwd(desc(disc="euler"), dlam=P) == INVALID             # dlambda only for the trapezoid
+    assert call_bwd(desc(cplx=True), dtheta=P) == INVALID              # dtheta needs theta
+    assert call_bwd(desc(cplx=True), theta=P, dh0=P + 4) == INVALID    # complex state gradient: 8 bytes
+    assert call_bwd(desc(), du=P + 2) == INVALID
+    assert call_bwd(desc(N=65)) == UNSUPPORTED
+    d = desc(B=2, L=100, D=8, N=16, cplx=True)
+    need = scan.ssm_scan_bwd_workspace_bytes(d)
+    assert need == 4 * 2 * 8 * 16 * 8                                  # ceil(100/32) snapshots of the state
+    assert call_bwd(d, ws=0) == WS_SMALL
+    assert call_bwd(d, ws_bytes=need - 1) == WS_SMALL
+    assert call_bwd(d, ws=P + 64, ws_bytes=need) == INVALID            # not 256-byte aligned
