@@ -45,7 +45,8 @@
 namespace ssm {
 
 namespace bwd {
-constexpr int kSeg = 32;  // steps per recompute segment (states kept in registers)
+constexpr int kSeg = 16;  // steps per recompute segment (states kept in LDS)
+constexpr int kGroup = 8;  // steps whose loads are issued together
 }
 
 struct BwdParams {
@@ -89,41 +90,128 @@ __global__ void __launch_bounds__(256) bwd_zero_kernel(float* a, int64_t na, flo
     }
 }
 
-// One step's operands of a lane (zero past N or past the channels).
+// One step's operands of a lane (zero past N, past the channels and on a
+// masked step, which then leaves the state unchanged: alpha = 1, bterm = 0).
 struct BwdStep {
     float x, dt, lam, ar, ai, br, bi, cr, ci, a, rho, em1;
 };
 
+// Lane geometry.  Every load uses clamped (always valid) indices and masks
+// its value afterwards, so loads carry no branches and the compiler can
+// issue a whole segment's loads together.
+struct BwdLane {
+    int64_t ch, b, d;  // b, d clamped to the last channel
+    int n, nc;         // nc clamped to N - 1
+    bool ch_ok, ok;
+};
+
+__device__ __forceinline__ BwdLane bwd_lane(const BwdParams& p) {
+    BwdLane l;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+    l.ch = wave * (64 / p.lpc) + lane / p.lpc;
+    l.n = lane & (p.lpc - 1);
+    l.ch_ok = l.ch < p.batch * p.dim;
+    l.ok = l.ch_ok && l.n < p.dstate;
+    const int64_t chc = l.ch_ok ? l.ch : p.batch * p.dim - 1;
+    l.b = chc / p.dim;
+    l.d = chc % p.dim;
+    l.nc = l.n < p.dstate ? l.n : static_cast<int>(p.dstate) - 1;
+    return l;
+}
+
+// A lane's input pointers at the first step of a segment; step k of the
+// segment is k strides further (strides fit 32 bits, checked by the host).
+template <typename T>
+struct BwdPtrs {
+    const T *u, *dt, *lam, *th, *B, *C, *dy;
+    int32_t s_tc, s_th, s_bn;  // strides per step: D, D*N (theta), N*cw (B, C)
+};
+
+// Move a lane's pointers by `steps` steps.  The moved pointers are made
+// opaque to the compiler, and no memory access may cross this point, so an
+// unrolled sweep issues its loads a group of kGroup steps at a time (one
+// memory latency per group) instead of computing every step's addresses and
+// loads up front (which would hold a whole segment's operands in
+// registers).
+template <typename T>
+__device__ __forceinline__ void bwd_step_ptrs(BwdPtrs<T>& q, int steps) {
+    q.u += steps * q.s_tc;
+    q.dt += steps * q.s_tc;
+    q.lam += steps * q.s_tc;
+    q.dy += steps * q.s_tc;
+    q.th += steps * q.s_th;
+    q.B += steps * q.s_bn;
+    q.C += steps * q.s_bn;
+    asm volatile("" : "+v"(q.u), "+v"(q.dt), "+v"(q.lam), "+v"(q.dy), "+v"(q.th), "+v"(q.B), "+v"(q.C)::"memory");
+}
+
+template <typename T, bool CPLX>
+__device__ __forceinline__ BwdPtrs<T> bwd_ptrs(const BwdParams& p, const BwdLane& l, int64_t t0) {
+    const int64_t L = p.seqlen, D = p.dim, N = p.dstate, cw = CPLX ? 2 : 1;
+    const int64_t tc = (l.b * L + t0) * D + l.d;
+    const int64_t bn = ((l.b * L + t0) * N + l.nc) * cw;
+    BwdPtrs<T> q;
+    q.u = static_cast<const T*>(p.u) + tc;
+    q.dt = static_cast<const T*>(p.delta) + tc;
+    q.lam = p.lambda ? static_cast<const T*>(p.lambda) + tc : q.u;
+    // without theta the rotation is zero: read u's element and mask it
+    q.th = p.theta ? static_cast<const T*>(p.theta) + tc * N + l.nc : q.u;
+    q.B = static_cast<const T*>(p.B) + bn;
+    q.C = static_cast<const T*>(p.C) + bn;
+    q.dy = p.dy ? static_cast<const T*>(p.dy) + tc : q.u;
+    q.s_tc = static_cast<int32_t>(D);
+    q.s_th = p.theta ? static_cast<int32_t>(D * N) : static_cast<int32_t>(D);
+    q.s_bn = static_cast<int32_t>(N * cw);
+    return q;
+}
+
+// The loaded (unmasked) values of one step of a segment.
+struct BwdRaw {
+    float x, dt, lam, th, br, bi, cr, ci, dy;
+};
+
+// Loads of step k of the segment (k may be -1 for the step before it; any k
+// given must be a valid step).
 template <typename T, int DISC, bool CPLX>
-__device__ __forceinline__ BwdStep bwd_load(const BwdParams& p, int64_t b, int64_t d, int n, int64_t t, bool ch_ok,
-                                            bool ok) {
+__device__ __forceinline__ BwdRaw bwd_raw(const BwdPtrs<T>& q, int k, bool with_dy) {
     using E = Elem<T>;
+    BwdRaw r;
+    r.x = E::load(q.u, k * q.s_tc);
+    r.dt = E::load(q.dt, k * q.s_tc);
+    r.lam = DISC == kTrap ? E::load(q.lam, k * q.s_tc) : 0.f;
+    r.dy = with_dy ? E::load(q.dy, k * q.s_tc) : 0.f;
+    r.bi = r.ci = r.th = 0.f;
+    if constexpr (CPLX) {
+        r.br = E::load(q.B, k * q.s_bn);
+        r.bi = E::load(q.B, k * q.s_bn + 1);
+        r.cr = E::load(q.C, k * q.s_bn);
+        r.ci = E::load(q.C, k * q.s_bn + 1);
+        r.th = E::load(q.th, k * q.s_th);
+    } else {
+        r.br = E::load(q.B, k * q.s_bn);
+        r.cr = E::load(q.C, k * q.s_bn);
+    }
+    return r;
+}
+
+// Operands of a step from its loaded values; act = false masks the step.
+template <typename T, int DISC, bool CPLX>
+__device__ __forceinline__ BwdStep bwd_cook(const BwdParams& p, const BwdRaw& r, const BwdLane& l, float a_lane,
+                                            bool act) {
     constexpr int SC = std::is_same_v<T, uint16_t> ? kSinCosHw : kSinCosWide;
-    const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
-    BwdStep s{};
-    const int64_t tc = (b * L + t) * D + d;
-    if (ch_ok) {
-        s.x = E::load(static_cast<const T*>(p.u), tc);
-        s.dt = E::load(static_cast<const T*>(p.delta), tc);
-        if constexpr (DISC == kTrap) s.lam = E::load(static_cast<const T*>(p.lambda), tc);
-    }
-    float th = 0.f;
-    if (ok) {
-        s.a = p.A[d * N + n];
-        const int64_t bn = (b * L + t) * N + n;
-        const T* Bm = static_cast<const T*>(p.B);
-        const T* Cm = static_cast<const T*>(p.C);
-        if constexpr (CPLX) {
-            s.br = E::load(Bm, 2 * bn);
-            s.bi = E::load(Bm, 2 * bn + 1);
-            s.cr = E::load(Cm, 2 * bn);
-            s.ci = E::load(Cm, 2 * bn + 1);
-            if (p.theta) th = E::load(static_cast<const T*>(p.theta), tc * N + n);
-        } else {
-            s.br = E::load(Bm, bn);
-            s.cr = E::load(Cm, bn);
-        }
-    }
+    const bool cm = l.ch_ok && act, om = l.ok && act;
+    BwdStep s;
+    s.x = cm ? r.x : 0.f;
+    s.dt = cm ? r.dt : 0.f;
+    s.lam = cm ? r.lam : 0.f;
+    s.a = om ? a_lane : 0.f;
+    s.br = om ? r.br : 0.f;
+    s.bi = om ? r.bi : 0.f;
+    s.cr = om ? r.cr : 0.f;
+    s.ci = om ? r.ci : 0.f;
+    const float th = (om && p.theta) ? r.th : 0.f;
+    s.em1 = 0.f;
     if constexpr (DISC == kZOH)
         exp_expm1(s.dt * s.a, s.dt * prep_A(s.a), &s.rho, &s.em1);
     else
@@ -139,24 +227,23 @@ __device__ __forceinline__ BwdStep bwd_load(const BwdParams& p, int64_t b, int64
     return s;
 }
 
-// q_t = B_t u_t of one lane (no transcendental)
+template <typename T, int DISC, bool CPLX>
+__device__ __forceinline__ BwdStep bwd_load(const BwdParams& p, const BwdPtrs<T>& q, const BwdLane& l, float a_lane,
+                                            int k, bool act) {
+    return bwd_cook<T, DISC, CPLX>(p, bwd_raw<T, DISC, CPLX>(q, k, false), l, a_lane, act);
+}
+
+// q = B u of step k of the segment (no transcendental); zero when masked
 template <typename T, bool CPLX>
-__device__ __forceinline__ void bwd_q(const BwdParams& p, int64_t b, int64_t d, int n, int64_t t, bool ch_ok,
-                                      bool ok, float* qr, float* qi) {
+__device__ __forceinline__ void bwd_q(const BwdPtrs<T>& q, const BwdLane& l, int k, bool act, float* qr,
+                                      float* qi) {
     using E = Elem<T>;
-    *qr = 0.f;
-    *qi = 0.f;
-    if (!ok || !ch_ok) return;
-    const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
-    const float x = E::load(static_cast<const T*>(p.u), (b * L + t) * D + d);
-    const int64_t bn = (b * L + t) * N + n;
-    const T* Bm = static_cast<const T*>(p.B);
-    if constexpr (CPLX) {
-        *qr = E::load(Bm, 2 * bn) * x;
-        *qi = E::load(Bm, 2 * bn + 1) * x;
-    } else {
-        *qr = E::load(Bm, bn) * x;
-    }
+    const float x = E::load(q.u, k * q.s_tc);
+    const bool om = l.ok && act;
+    const float br = E::load(q.B, k * q.s_bn);
+    const float bi = CPLX ? E::load(q.B, k * q.s_bn + 1) : 0.f;
+    *qr = om ? br * x : 0.f;
+    *qi = om ? bi * x : 0.f;
 }
 
 // b-term of a step from its operands and q_{t-1} = (qpr, qpi)
@@ -177,41 +264,37 @@ __device__ __forceinline__ void bwd_bterm(const BwdStep& s, float qpr, float qpi
     }
 }
 
-// lane geometry shared by both kernels
-struct BwdLane {
-    int64_t ch, b, d;
-    int n;
-    bool ch_ok, ok;
-};
-
-__device__ __forceinline__ BwdLane bwd_lane(const BwdParams& p) {
-    BwdLane l;
-    const int lane = threadIdx.x & 63;
-    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
-    l.ch = wave * (64 / p.lpc) + lane / p.lpc;
-    l.n = lane & (p.lpc - 1);
-    l.ch_ok = l.ch < p.batch * p.dim;
-    l.ok = l.ch_ok && l.n < p.dstate;
-    l.b = l.ch_ok ? l.ch / p.dim : 0;
-    l.d = l.ch_ok ? l.ch % p.dim : 0;
-    return l;
+// The gradients are written only to outputs, which the caller guarantees do
+// not alias any input; telling the compiler so lets it issue later steps'
+// loads ahead of earlier steps' stores.
+__device__ __forceinline__ void bwd_assume_disjoint(const BwdParams& p) {
+    const void* in[] = {p.u, p.delta, p.A, p.B, p.C, p.theta, p.lambda, p.dy, p.ckpt};
+    float* out[] = {p.du, p.ddelta, p.dB, p.dC, p.dtheta, p.dlambda};
+#pragma unroll
+    for (int i = 0; i < 9; ++i)
+#pragma unroll
+        for (int o = 0; o < 6; ++o)
+            if (in[i] && out[o]) __builtin_assume_separate_storage(in[i], out[o]);
 }
 
 template <typename T, int DISC, bool CPLX>
 __global__ void __launch_bounds__(256) bwd_ckpt_kernel(BwdParams p) {
-    using E = Elem<T>;
+    constexpr int kSeg = bwd::kSeg;
     const BwdLane l = bwd_lane(p);
     const int64_t L = p.seqlen, N = p.dstate;
-    const int64_t s0 = (l.b * p.dim + l.d) * N + l.n;  // (b, d, n)
-    const int64_t plane = p.batch * p.dim * N;          // one snapshot
+    const int64_t s0 = (l.b * p.dim + l.d) * N + l.nc;  // (b, d, n)
+    const int64_t plane = p.batch * p.dim * N;           // one snapshot
+    const int64_t nseg = (L + kSeg - 1) / kSeg;
     float hr = 0.f, hi = 0.f, qpr = 0.f, qpi = 0.f;
     if (l.ok && p.h0) {
         hr = CPLX ? p.h0[2 * s0] : p.h0[s0];
         hi = CPLX ? p.h0[2 * s0 + 1] : 0.f;
     }
-    for (int64_t t = 0; t < L; ++t) {
-        if (t % bwd::kSeg == 0 && l.ok) {
-            const int64_t k = (t / bwd::kSeg) * plane + s0;
+    const float a_lane = p.A[l.d * N + l.nc];
+    for (int64_t sg = 0; sg < nseg; ++sg) {
+        const int64_t t0 = sg * kSeg;
+        if (l.ok) {
+            const int64_t k = sg * plane + s0;
             if constexpr (CPLX) {
                 p.ckpt[2 * k] = hr;
                 p.ckpt[2 * k + 1] = hi;
@@ -219,14 +302,20 @@ __global__ void __launch_bounds__(256) bwd_ckpt_kernel(BwdParams p) {
                 p.ckpt[k] = hr;
             }
         }
-        const BwdStep s = bwd_load<T, DISC, CPLX>(p, l.b, l.d, l.n, t, l.ch_ok, l.ok);
-        float br, bi;
-        bwd_bterm<DISC>(s, qpr, qpi, &br, &bi);
-        qpr = s.br * s.x;
-        qpi = s.bi * s.x;
-        const float nr = s.ar * hr - s.ai * hi + br;
-        hi = s.ar * hi + s.ai * hr + bi;
-        hr = nr;
+        if (sg == nseg - 1) break;  // the state after the last segment is not needed
+        // a full segment (only the last may be ragged, and it is not swept)
+        const BwdPtrs<T> q = bwd_ptrs<T, CPLX>(p, l, t0);
+#pragma unroll 8
+        for (int k = 0; k < kSeg; ++k) {
+            const BwdStep s = bwd_load<T, DISC, CPLX>(p, q, l, a_lane, k, true);
+            float br, bi;
+            bwd_bterm<DISC>(s, qpr, qpi, &br, &bi);
+            qpr = s.br * s.x;
+            qpi = s.bi * s.x;
+            const float nr = s.ar * hr - s.ai * hi + br;
+            hi = s.ar * hi + s.ai * hr + bi;
+            hr = nr;
+        }
     }
 }
 
@@ -238,16 +327,18 @@ __device__ __forceinline__ float chan_sum(float v, int lpc) {
 
 template <typename T, int DISC, bool CPLX>
 __global__ void __launch_bounds__(256) bwd_main_kernel(BwdParams p) {
-    using E = Elem<T>;
-    constexpr int kSeg = bwd::kSeg;
+    constexpr int kSeg = bwd::kSeg, kG = bwd::kGroup;
+    // the segment's states h_t, per wave and lane (each wave uses only its own rows)
+    __shared__ float2 s_h[4][kSeg][64];
+    bwd_assume_disjoint(p);
     const BwdLane l = bwd_lane(p);
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lpc = p.lpc;
     const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
-    const int64_t s0 = (l.b * D + l.d) * N + l.n;
+    const int64_t s0 = (l.b * D + l.d) * N + l.nc;
     const int64_t plane = p.batch * D * N;
     const int64_t nseg = (L + kSeg - 1) / kSeg;
-    const T* dyp = static_cast<const T*>(p.dy);
+    const float a_lane = p.A[l.d * N + l.nc];
     const float skip = (l.ch_ok && p.Dskip) ? p.Dskip[l.d] : 0.f;
     // the wave's channels share one batch row: dB, dC are summed across them first
     const int64_t wave_ch0 = __shfl(l.ch, 0, 64);
@@ -271,132 +362,162 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(BwdParams p) {
             hpr = CPLX ? p.ckpt[2 * k] : p.ckpt[k];
             hpi = CPLX ? p.ckpt[2 * k + 1] : 0.f;
         }
+        const BwdPtrs<T> q = bwd_ptrs<T, CPLX>(p, l, t0);
         float q0r = 0.f, q0i = 0.f;
-        if (DISC == kTrap && t0 > 0) bwd_q<T, CPLX>(p, l.b, l.d, l.n, t0 - 1, l.ch_ok, l.ok, &q0r, &q0i);
-        // forward over the segment: h_t into registers
-        float hsr[kSeg], hsi[kSeg];
+        if (DISC == kTrap && t0 > 0) bwd_q<T, CPLX>(q, l, -1, true, &q0r, &q0i);
+
+        // forward over the segment, kG steps per load group: h_t into LDS
+        // (steps past the end are masked and leave the state unchanged)
         {
             float hr = hpr, hi = hpi, qpr = q0r, qpi = q0i;
+            BwdPtrs<T> qf = q;
 #pragma unroll
-            for (int k = 0; k < kSeg; ++k) {
-                if (k < len) {
-                    const BwdStep s = bwd_load<T, DISC, CPLX>(p, l.b, l.d, l.n, t0 + k, l.ch_ok, l.ok);
+            for (int g0 = 0; g0 < kSeg; g0 += kG) {
+                if (g0 > 0) bwd_step_ptrs(qf, kG);
+                BwdRaw rw[kG];
+#pragma unroll
+                for (int j = 0; j < kG; ++j) rw[j] = bwd_raw<T, DISC, CPLX>(qf, (g0 + j < len ? g0 + j : len - 1) - g0, false);
+#pragma unroll
+                for (int j = 0; j < kG; ++j) {
+                    const BwdStep st = bwd_cook<T, DISC, CPLX>(p, rw[j], l, a_lane, g0 + j < len);
                     float br, bi;
-                    bwd_bterm<DISC>(s, qpr, qpi, &br, &bi);
-                    qpr = s.br * s.x;
-                    qpi = s.bi * s.x;
-                    const float nr = s.ar * hr - s.ai * hi + br;
-                    hi = s.ar * hi + s.ai * hr + bi;
+                    bwd_bterm<DISC>(st, qpr, qpi, &br, &bi);
+                    qpr = st.br * st.x;
+                    qpi = st.bi * st.x;
+                    const float nr = st.ar * hr - st.ai * hi + br;
+                    hi = st.ar * hi + st.ai * hr + bi;
                     hr = nr;
+                    s_h[w][g0 + j][lane] = make_float2(hr, hi);
                 }
-                hsr[k] = hr;
-                hsi[k] = hi;
             }
         }
-        // reverse sweep over the segment
+
+        // reverse sweep over the segment, one load group at a time (masked
+        // steps change nothing and store nothing)
+        BwdPtrs<T> qv = q;
+        bwd_step_ptrs(qv, kSeg - kG);
+        float2 hnext = s_h[w][kSeg - 1][lane];  // h_t of the step being processed
 #pragma unroll
-        for (int k = kSeg - 1; k >= 0; --k) {
-            if (k >= len) continue;
-            const int64_t t = t0 + k;
-            const int64_t tc = (l.b * L + t) * D + l.d;
-            const BwdStep s = bwd_load<T, DISC, CPLX>(p, l.b, l.d, l.n, t, l.ch_ok, l.ok);
-            const float g = l.ch_ok ? E::load(dyp, tc) : 0.f;
-            const float htr = hsr[k], hti = hsi[k];
-            const float hpr_t = k > 0 ? hsr[k - 1] : hpr, hpi_t = k > 0 ? hsi[k - 1] : hpi;
-            // y_t = Re(C h_t) + D u_t
-            Gr += g * s.cr;
-            Gi -= g * s.ci;
-            float gCr = g * htr, gCi = -g * hti;
-            // h_t = alpha h_{t-1} + bterm:  dalpha = conj(h_{t-1}) G
-            float gar = hpr_t * Gr + hpi_t * Gi, gai = hpr_t * Gi - hpi_t * Gr;
-            float gqr = dqr, gqi = dqi;
-            float gdt = 0.f, glam = 0.f, gz = 0.f;
-            const float qr = s.br * s.x, qi = s.bi * s.x;
-            if constexpr (DISC == kZOH) {
-                const float kap = s.a != 0.f ? s.em1 / s.a : s.dt;
-                gqr += kap * Gr;
-                gqi += kap * Gi;
-                const float gk = Gr * qr + Gi * qi;
-                const float z = s.dt * s.a;
-                // d kappa / dA = (delta e^z - kappa)/A = delta^2 sum_m z^m (m+1)/(m+2)!; the
-                // closed form cancels for small z, so |z| < 1/2 takes the series (to m = 6:
-                // truncation below 4e-7 relative)
-                const float ser =
-                    0.5f +
-                    z * (1.f / 3.f +
-                         z * (1.f / 8.f + z * (1.f / 30.f + z * (1.f / 144.f + z * (1.f / 840.f + z * (1.f / 5760.f))))));
-                const float dk = fabsf(z) < 0.5f ? s.dt * s.dt * ser : (s.dt * s.rho - kap) / s.a;
-                gdt += gk * s.rho;
-                accA += gk * dk;
-            } else if constexpr (DISC == kEuler) {
-                gqr += s.dt * Gr;
-                gqi += s.dt * Gi;
-                gdt += Gr * qr + Gi * qi;
-            } else {
-                float qpr = q0r, qpi = q0i;  // q_{t-1}
-                if (k > 0) bwd_q<T, CPLX>(p, l.b, l.d, l.n, t - 1, l.ch_ok, l.ok, &qpr, &qpi);
-                const float aqr = s.ar * qpr - s.ai * qpi, aqi = s.ar * qpi + s.ai * qpr;  // alpha q_{t-1}
-                const float e = (1.f - s.lam) * s.dt;
-                gqr += s.lam * s.dt * Gr;
-                gqi += s.lam * s.dt * Gi;
-                glam += Gr * (s.dt * qr - s.dt * aqr) + Gi * (s.dt * qi - s.dt * aqi);
-                gdt += Gr * (s.lam * qr + (1.f - s.lam) * aqr) + Gi * (s.lam * qi + (1.f - s.lam) * aqi);
-                gar += e * (qpr * Gr + qpi * Gi);  // conj(e q_{t-1}) G
-                gai += e * (qpr * Gi - qpi * Gr);
-                dqr = e * (s.ar * Gr + s.ai * Gi);  // conj(e alpha) G, to q_{t-1}
-                dqi = e * (s.ar * Gi - s.ai * Gr);
-            }
-            // q_t = B_t u_t
-            float gBr = s.x * gqr, gBi = s.x * gqi;
-            float gu = gqr * s.br + gqi * s.bi;
-            // alpha = exp(z + i theta): P = conj(dalpha) alpha
-            const float Pr = gar * s.ar + gai * s.ai, Pi = gar * s.ai - gai * s.ar;
-            gz = Pr;
-            gdt += gz * s.a;
-            accA += gz * s.dt;
-            if (CPLX && p.dtheta && l.ok) p.dtheta[tc * N + l.n] = -Pi;
-            // to h_{t-1}: G = conj(alpha) G
-            {
-                const float nr = s.ar * Gr + s.ai * Gi;
-                Gi = s.ar * Gi - s.ai * Gr;
-                Gr = nr;
-            }
-            if (!l.ok) gu = gdt = glam = gBr = gBi = gCr = gCi = 0.f;
-            // per (b, t, d): sums over the channel's states
-            gu = chan_sum(gu, lpc);
-            gdt = chan_sum(gdt, lpc);
-            if constexpr (DISC == kTrap) glam = chan_sum(glam, lpc);
-            if (l.n == 0 && l.ch_ok) {
-                p.du[tc] = gu + g * skip;
-                p.ddelta[tc] = gdt;
-                if constexpr (DISC == kTrap) p.dlambda[tc] = glam;
-                accD += g * s.x;
-            }
-            // per (b, t, n): sums over channels
-            const int64_t bn = (l.b * L + t) * N + l.n;
-            if (one_row) {
-                for (int off = lpc; off < 64; off <<= 1) {
-                    gBr += __shfl_xor(gBr, off, 64);
-                    gCr += __shfl_xor(gCr, off, 64);
-                    if constexpr (CPLX) {
-                        gBi += __shfl_xor(gBi, off, 64);
-                        gCi += __shfl_xor(gCi, off, 64);
-                    }
+        for (int g0 = kSeg - kG; g0 >= 0; g0 -= kG) {
+            if (g0 < kSeg - kG) bwd_step_ptrs(qv, -kG);
+            BwdRaw rw[kG];
+#pragma unroll
+            for (int j = 0; j < kG; ++j) rw[j] = bwd_raw<T, DISC, CPLX>(qv, (g0 + j < len ? g0 + j : len - 1) - g0, true);
+            // q_{t-1} of the group's first step: the step before the group
+            float qbr = q0r, qbi = q0i;
+            if (DISC == kTrap && g0 > 0)
+                bwd_q<T, CPLX>(qv, l, g0 - 1 < len ? -1 : len - 1 - g0, g0 - 1 < len, &qbr, &qbi);
+#pragma unroll
+            for (int j = kG - 1; j >= 0; --j) {
+                const int k = g0 + j;
+                const bool act = k < len;
+                const int64_t t = t0 + (act ? k : len - 1);
+                const int64_t tc = (l.b * L + t) * D + l.d;
+                const BwdStep s = bwd_cook<T, DISC, CPLX>(p, rw[j], l, a_lane, act);
+                const float g = (l.ch_ok && act) ? rw[j].dy : 0.f;
+                const float htr = hnext.x, hti = hnext.y;
+                const float2 hprev = k > 0 ? s_h[w][k - 1][lane] : make_float2(hpr, hpi);
+                hnext = hprev;
+                const float hpr_t = hprev.x, hpi_t = hprev.y;
+                // y_t = Re(C h_t) + D u_t
+                Gr += g * s.cr;
+                Gi -= g * s.ci;
+                float gCr = g * htr, gCi = -g * hti;
+                if (!l.ok) gCr = gCi = 0.f;
+                // h_t = alpha h_{t-1} + bterm:  dalpha = conj(h_{t-1}) G
+                float gar = hpr_t * Gr + hpi_t * Gi, gai = hpr_t * Gi - hpi_t * Gr;
+                float gqr = dqr, gqi = dqi;
+                float gdt = 0.f, glam = 0.f;
+                const float qr = s.br * s.x, qi = s.bi * s.x;
+                if constexpr (DISC == kZOH) {
+                    const float kap = s.a != 0.f ? s.em1 / s.a : s.dt;
+                    gqr += kap * Gr;
+                    gqi += kap * Gi;
+                    const float gk = Gr * qr + Gi * qi;
+                    const float z = s.dt * s.a;
+                    // d kappa / dA = (delta e^z - kappa)/A = delta^2 sum_m z^m (m+1)/(m+2)!; the
+                    // closed form cancels for small z, so |z| < 1/2 takes the series (to m = 6:
+                    // truncation below 4e-7 relative)
+                    const float ser =
+                        0.5f +
+                        z * (1.f / 3.f +
+                             z * (1.f / 8.f +
+                                  z * (1.f / 30.f + z * (1.f / 144.f + z * (1.f / 840.f + z * (1.f / 5760.f))))));
+                    const float dk = fabsf(z) < 0.5f ? s.dt * s.dt * ser : (s.dt * s.rho - kap) / s.a;
+                    gdt += gk * s.rho;
+                    accA += gk * dk;
+                } else if constexpr (DISC == kEuler) {
+                    gqr += s.dt * Gr;
+                    gqi += s.dt * Gi;
+                    gdt += Gr * qr + Gi * qi;
+                } else {
+                    // q_{t-1}: from the previous step's loads, or the step before the group
+                    const bool om = l.ok && act;
+                    const float qpr = j > 0 ? (om ? rw[j - 1].br * rw[j - 1].x : 0.f) : (act ? qbr : 0.f);
+                    const float qpi = j > 0 ? (om ? rw[j - 1].bi * rw[j - 1].x : 0.f) : (act ? qbi : 0.f);
+                    const float aqr = s.ar * qpr - s.ai * qpi, aqi = s.ar * qpi + s.ai * qpr;  // alpha q_{t-1}
+                    const float e = (1.f - s.lam) * s.dt;
+                    gqr += s.lam * s.dt * Gr;
+                    gqi += s.lam * s.dt * Gi;
+                    glam += Gr * (s.dt * qr - s.dt * aqr) + Gi * (s.dt * qi - s.dt * aqi);
+                    gdt += Gr * (s.lam * qr + (1.f - s.lam) * aqr) + Gi * (s.lam * qi + (1.f - s.lam) * aqi);
+                    gar += e * (qpr * Gr + qpi * Gi);  // conj(e q_{t-1}) G
+                    gai += e * (qpr * Gi - qpi * Gr);
+                    dqr = e * (s.ar * Gr + s.ai * Gi);  // conj(e alpha) G, to q_{t-1}
+                    dqi = e * (s.ar * Gi - s.ai * Gr);
                 }
-                if (lane < lpc && l.ok) {
+                // q_t = B_t u_t
+                float gBr = s.x * gqr, gBi = s.x * gqi;
+                float gu = gqr * s.br + gqi * s.bi;
+                // alpha = exp(z + i theta): P = conj(dalpha) alpha
+                const float Pr = gar * s.ar + gai * s.ai, Pi = gar * s.ai - gai * s.ar;
+                gdt += Pr * s.a;
+                accA += Pr * s.dt;
+                // to h_{t-1}: G = conj(alpha) G
+                {
+                    const float nr = s.ar * Gr + s.ai * Gi;
+                    Gi = s.ar * Gi - s.ai * Gr;
+                    Gr = nr;
+                }
+                if (!l.ok) gu = gdt = glam = gBr = gBi = 0.f;
+                // per (b, t, d): sums over the channel's states
+                gu = chan_sum(gu, lpc);
+                gdt = chan_sum(gdt, lpc);
+                if constexpr (DISC == kTrap) glam = chan_sum(glam, lpc);
+                if (!act) continue;  // uniform: a masked step has nothing to store
+                if (CPLX && p.dtheta && l.ok) p.dtheta[tc * N + l.n] = -Pi;
+                if (l.n == 0 && l.ch_ok) {
+                    p.du[tc] = gu + g * skip;
+                    p.ddelta[tc] = gdt;
+                    if constexpr (DISC == kTrap) p.dlambda[tc] = glam;
+                    accD += g * s.x;
+                }
+                // per (b, t, n): sums over channels
+                const int64_t bn = (l.b * L + t) * N + l.n;
+                if (one_row) {
+                    for (int off = lpc; off < 64; off <<= 1) {
+                        gBr += __shfl_xor(gBr, off, 64);
+                        gCr += __shfl_xor(gCr, off, 64);
+                        if constexpr (CPLX) {
+                            gBi += __shfl_xor(gBi, off, 64);
+                            gCi += __shfl_xor(gCi, off, 64);
+                        }
+                    }
+                    if (lane < lpc && l.ok) {
+                        atomicAdd(&p.dB[CPLX ? 2 * bn : bn], gBr);
+                        atomicAdd(&p.dC[CPLX ? 2 * bn : bn], gCr);
+                        if constexpr (CPLX) {
+                            atomicAdd(&p.dB[2 * bn + 1], gBi);
+                            atomicAdd(&p.dC[2 * bn + 1], gCi);
+                        }
+                    }
+                } else if (l.ok) {
                     atomicAdd(&p.dB[CPLX ? 2 * bn : bn], gBr);
                     atomicAdd(&p.dC[CPLX ? 2 * bn : bn], gCr);
                     if constexpr (CPLX) {
                         atomicAdd(&p.dB[2 * bn + 1], gBi);
                         atomicAdd(&p.dC[2 * bn + 1], gCi);
                     }
-                }
-            } else if (l.ok) {
-                atomicAdd(&p.dB[CPLX ? 2 * bn : bn], gBr);
-                atomicAdd(&p.dC[CPLX ? 2 * bn : bn], gCr);
-                if constexpr (CPLX) {
-                    atomicAdd(&p.dB[2 * bn + 1], gBi);
-                    atomicAdd(&p.dC[2 * bn + 1], gCi);
                 }
             }
         }

@@ -305,6 +305,8 @@ int ssm_scan_bwd(const ssm_scan_desc_t* desc, const void* u, const void* delta, 
     const void* st_ptrs[] = {h0, dh_last, dh0};
     for (const void* q : st_ptrs)
         if (q && !aligned(q, ss)) return SSM_ERR_INVALID_ARGUMENT;
+    // per-step element strides inside a 32-step segment are 32-bit
+    if (desc->dim * desc->dstate * ssm::bwd::kSeg >= (int64_t(1) << 31)) return SSM_ERR_UNSUPPORTED;
     const size_t need = bwd_workspace(desc);
     if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned(workspace, 256)) return SSM_ERR_INVALID_ARGUMENT;
