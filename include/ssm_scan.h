@@ -202,8 +202,8 @@ int ssm_scan_step(const ssm_scan_desc_t *desc, const void *u, const void *delta,
                   const void *u_prev, const void *B_prev, float *h, void *y, void *stream);
 
 /* Bytes of workspace ssm_scan_bwd needs for `desc`: the state before every
- * 32-step segment, ceil(L/32) * B * D * N * (8 complex, 4 real) bytes
- * (e.g. 1.34 GB for B=4, L=8192, D=2560, N=16 complex).  0 for an invalid
+ * 16-step segment, ceil(L/16) * B * D * N * (8 complex, 4 real) bytes
+ * (e.g. 2.68 GB for B=4, L=8192, D=2560, N=16 complex).  0 for an invalid
  * descriptor. */
 size_t ssm_scan_bwd_workspace_bytes(const ssm_scan_desc_t *desc);
 

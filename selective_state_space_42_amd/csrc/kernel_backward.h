@@ -25,8 +25,9 @@
 //      segment of kSeg steps (the only state-sized data in memory: L/kSeg
 //      snapshots).
 //   2. bwd_main_kernel walks the segments from the last to the first: it
-//      recomputes the segment's states from its snapshot into registers,
-//      then runs the reverse sweep over them.
+//      recomputes the segment's states from its snapshot into wave-private
+//      LDS, then runs the reverse sweep over them.  Both sweeps issue their
+//      loads kGroup steps at a time.
 // Sums: du, ddelta, dlambda per (b, t, d) over the channel's lanes by
 // shuffles; dB, dC per (b, t, n) over channels, first across the wave's
 // channels by shuffles, then one atomic add per wave; dA per (d, n) and dD

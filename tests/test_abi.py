@@ -175,7 +175,7 @@ def test_backward_argument_rules():
     assert call_bwd(desc(N=65)) == UNSUPPORTED
     d = desc(B=2, L=100, D=8, N=16, cplx=True)
     need = scan.ssm_scan_bwd_workspace_bytes(d)
-    assert need == 4 * 2 * 8 * 16 * 8                                  # ceil(100/32) snapshots of the state
+    assert need == 7 * 2 * 8 * 16 * 8                                  # ceil(100/16) snapshots of the state
     assert call_bwd(d, ws=0) == WS_SMALL
     assert call_bwd(d, ws_bytes=need - 1) == WS_SMALL
     assert call_bwd(d, ws=P + 64, ws_bytes=need) == INVALID            # not 256-byte aligned
