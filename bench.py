@@ -21,7 +21,8 @@ exp-trapezoidal, bf16 I/O, fp32 arithmetic), on which the HBM-bandwidth target
 is stated.  A decode workload (--workload decode_...) times ssm_scan_step
 instead: a step is one token for every sequence of the batch, the state read
 and written in HBM, and the same line is printed with B*D tokens*channels per
-step.
+step.  --backward times ssm_scan_bwd (all input gradients of the scan) on the
+workload instead of the forward scan.
 """
 from __future__ import annotations
 
@@ -71,6 +72,20 @@ def decode_algorithmic_bytes(w) -> int:
             + e * B * N * (1 + cplx) * (2 + trap)  # B, C, (B_prev)
             + 4 * D * N + 4 * D                  # A, D
             + 2 * 4 * B * D * N * (1 + cplx))    # h read and written
+
+
+def backward_algorithmic_bytes(w) -> int:
+    """The backward pass: every input and dy read once, every gradient (fp32)
+    written once."""
+    e = 4 if w.io_dtype == "f32" else 2
+    B, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
+    trap = 1 if w.disc == "trap" else 0
+    cplx = 1 if w.is_complex else 0
+    reads = (e * B * L * D * (3 + trap) + e * B * L * D * N * cplx + 2 * e * B * L * N * (1 + cplx)
+             + 4 * D * N + 4 * D)
+    writes = (4 * B * L * D * (2 + trap) + 4 * B * L * D * N * cplx + 2 * 4 * B * L * N * (1 + cplx)
+              + 4 * D * N + 4 * D)
+    return reads + writes
 
 
 def kernel_source_hash() -> str:
@@ -222,6 +237,94 @@ def bench_decode(args, w, torch, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_backward(args, w, torch, dev):
+    import numpy as np
+
+    from selective_state_space_42_amd.inputs import make_inputs
+    from selective_state_space_42_amd.scan import make_desc, ssm_scan_bwd, ssm_scan_bwd_workspace_bytes
+
+    log(f"generating {w.name} on {torch.cuda.get_device_name(dev)}")
+    inputs = make_inputs(w, device=dev)
+    g = torch.Generator(device=dev).manual_seed(2)
+    dy = torch.randn(inputs["u"].shape, generator=g, device=dev).to(inputs["u"].dtype)
+    desc = make_desc(w.batch, w.seqlen, w.dim, w.dstate, inputs["u"].dtype, w.disc, w.is_complex)
+    ws = torch.empty(max(ssm_scan_bwd_workspace_bytes(desc), 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        return ssm_scan_bwd(inputs["u"], inputs["delta"], inputs["A"], inputs["Bm"], inputs["Cm"], inputs["Dskip"],
+                            inputs["theta"], inputs["lam"], dy=dy, disc=w.disc, workspace=ws,
+                            stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # the binding allocates the gradient tensors on every call; the timed loop
+    # calls the library directly on one set of them
+    grads = step()
+    torch.cuda.synchronize()
+    import ctypes
+
+    from selective_state_space_42_amd import scan as _scan
+    ptr = _scan._ptr
+    lib = _scan._lib()
+
+    def call():
+        st = lib.ssm_scan_bwd(ctypes.byref(desc), ptr(inputs["u"]), ptr(inputs["delta"]), ptr(inputs["A"]),
+                              ptr(inputs["Bm"]), ptr(inputs["Cm"]), ptr(inputs["Dskip"]), ptr(inputs["theta"]),
+                              ptr(inputs["lam"]), None, ptr(dy), None,
+                              *(ptr(grads[k]) for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dtheta", "dlambda")),
+                              None, ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"ssm_scan_bwd status {st}")
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    log(f"timed {args.steps} backward passes: {ms:.3f} ms each")
+    alg = backward_algorithmic_bytes(w)
+    achieved = alg / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": w.batch * w.seqlen * w.dim / (ms * 1e-3), "unit": UNIT, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen, "dstate": w.dstate,
+                   "disc": w.disc, "complex": w.is_complex, "io_dtype": w.io_dtype, "algo": "backward"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profile(w.name, "backward"),
+                     "algorithmic_bytes_per_launch": alg},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from selective_state_space_42_amd.inputs import channel_sample
+
+        log("timing the fp64 oracle's backward on a channel sample")
+        spent, tc, nch = 0.0, 0, 0
+        order = np.random.default_rng(0).permutation(w.dim).tolist()
+        dyh = None
+        for c in order:
+            x = channel_sample(inputs, [c])
+            dyh = dy.index_select(2, torch.as_tensor([c], device=dev)).float().cpu().double().numpy()
+            t0 = time.perf_counter()
+            oracle.scan_bwd(x["u"], x["delta"], x["A"], x["Bm"], x["Cm"], x["Dskip"], x["theta"], x["lam"],
+                            disc=w.disc, is_complex=w.is_complex, dy=dyh)
+            spent += time.perf_counter() - t0
+            tc += w.batch * w.seqlen
+            nch += 1
+            if spent >= args.cpu_seconds:
+                break
+        out["cpu_baseline"] = {
+            "value": tc / spent, "unit": UNIT, "cores": 1, "kind": "oracle",
+            "sample": f"{nch} of {w.dim} channels (random, seed 0), one at a time, every batch row and step: "
+                      f"{tc} tokens*channels in {spent:.1f} s of the single-threaded fp64 C oracle backward"}
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration(torch, dev, nbytes: int, steps: int, warmup: int):
     """A plain copy of known size: reads and writes `nbytes` per launch."""
     n = (nbytes + 15) // 16 * 4
@@ -250,6 +353,7 @@ def main():
     ap.add_argument("--algo", default="auto", choices=["auto", "sequential", "chunked"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true", help="time the backward pass (ssm_scan_bwd) instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the scan, time a plain device-to-device copy of BYTES bytes "
                          "(the known-size kernel that HBM byte counters are scaled against)")
@@ -274,6 +378,9 @@ def main():
         bench_decode(args, DECODE_WORKLOADS[args.workload], torch, dev)
         return
     w = WORKLOADS[args.workload]
+    if args.backward:
+        bench_backward(args, w, torch, dev)
+        return
     log(f"generating {w.name} on {torch.cuda.get_device_name(dev)}")
     inputs = make_inputs(w, device=dev)
     torch.cuda.synchronize()
