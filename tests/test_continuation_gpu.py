@@ -164,3 +164,31 @@ def test_decode_from_empty_history(mode):
     err_y, err_h = _errs(w, torch.cat(ys, dim=1), h, ref_y, ref_h)
     tol = TOL[w.io_dtype]
     assert err_y <= tol and err_h <= tol, (err_y, err_h, tol)
+
+
+def test_decode_full_size_sampled():
+    """The decode workload bench.py times (B=256, D=2560, N=16 complex trapezoidal
+    bf16), three steps from a random state, compared on a channel sample with the
+    oracle continued from the same state and previous step."""
+    from selective_state_space_42_amd.inputs import DECODE_WORKLOADS, channel_sample
+
+    w = DECODE_WORKLOADS["decode_complex_trap_bf16_b256_d2560_n16"].scaled(seqlen=4)
+    inp = make_inputs(w, seed=31, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(8)
+    h = torch.randn((w.batch, w.dim, w.dstate, 2), generator=g, device="cuda")
+    h_start = h.clone()
+    ys = []
+    for t in range(1, 4):  # step 0 is the previous step of the first decoded one
+        x, xp = _step_inputs(inp, t), _step_inputs(inp, t - 1)
+        ys.append(ssm_scan_step(*_args(x), h=h, u_prev=xp["u"], B_prev=xp["Bm"], disc=w.disc)[:, None, :])
+    torch.cuda.synchronize()
+    idx = sorted(np.random.default_rng(0).choice(w.dim, 24, replace=False).tolist())
+    x = channel_sample(_time_slice(inp, 1, 4), idx)
+    prev = channel_sample(_time_slice(inp, 0, 1), idx)
+    q0 = prev["Bm"][:, 0][:, None, :, :] * prev["u"][:, 0][:, :, None, None]
+    ref_y, ref_h, _ = _oracle(w, x, h0=_host(h_start[:, idx]), q0=q0)
+    sel = torch.as_tensor(idx, device="cuda")
+    err_y = rel_err(_host(torch.cat(ys, dim=1).index_select(2, sel)), ref_y)
+    err_h = rel_err_complex(_host(h.index_select(1, sel)), ref_h)
+    print(f"decode full size err_y={err_y:.3e} err_h={err_h:.3e}", flush=True)
+    assert err_y <= TOL["bf16"] and err_h <= TOL["bf16"], (err_y, err_h)
