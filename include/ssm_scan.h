@@ -243,6 +243,51 @@ int ssm_scan_bwd(const ssm_scan_desc_t *desc, const void *u, const void *delta, 
                  float *dA, float *dB, float *dC, float *dD, float *dtheta, float *dlambda, float *dh0,
                  void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The state-space dual (SSD) form, for heads with a scalar decay
+ * (blog.lonae.com essay on the dual spectral theory of SSMs, section 3,
+ * "Mamba-2's SSD duality"): the channels of a head share delta_t and a
+ * scalar A, so all their states decay alike, and the scan becomes a causal
+ * decaying linear attention computed chunk by chunk with matrix products.
+ * For channel d of head h = d / headdim, with exponential-Euler b-terms:
+ *
+ *   h_t[n] = exp(delta_t[h] A[h]) h_{t-1}[n] + delta_t[h] B_t[n] u_t[d],   h_{-1} = 0
+ *   y_t[d] = sum_n C_t[n] h_t[n] + D[d] u_t[d]
+ *
+ * which is ssm_scan_fwd (real state, EXP_EULER) with delta and A broadcast
+ * over each head's channels.
+ */
+typedef struct {
+    int64_t batch;    /* B >= 1 */
+    int64_t seqlen;   /* L >= 1 */
+    int64_t dim;      /* D >= 1, a multiple of headdim */
+    int64_t dstate;   /* N, 1 <= N <= 64 */
+    int64_t headdim;  /* channels per head; 64 */
+    int32_t io_dtype; /* SSM_DTYPE_BF16 (fp32 I/O returns SSM_ERR_UNSUPPORTED) */
+    int32_t reserved; /* 0 */
+} ssm_ssd_desc_t;
+
+/* Bytes of workspace ssm_ssd_fwd needs: two fp32 N x headdim states and one
+ * decay per (batch, head, 64-step chunk); 0 for an invalid or unsupported
+ * descriptor. */
+size_t ssm_ssd_workspace_bytes(const ssm_ssd_desc_t *desc);
+
+/*
+ *   u       [B][L][D]   bf16     inputs
+ *   delta   [B][L][H]   bf16     step size of each head (H = D / headdim)
+ *   A       [H]         fp32     scalar decay rate of each head
+ *   B, C    [B][L][N]   bf16     projections shared by all heads
+ *   D       [D] fp32 or NULL     skip term
+ *   y       [B][L][D]   bf16     output (written)
+ *   h_last  [B][D][N] fp32, or NULL   final state (written)
+ *   workspace  ssm_ssd_workspace_bytes(desc) bytes, 256-byte aligned
+ * Returns an ssm_status_t (SSM_ERR_UNSUPPORTED for fp32 I/O, headdim != 64,
+ * D not a multiple of headdim or N > 64).
+ */
+int ssm_ssd_fwd(const ssm_ssd_desc_t *desc, const void *u, const void *delta, const float *A,
+                const void *B, const void *C, const float *D, void *y, float *h_last, void *workspace,
+                size_t workspace_bytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *ssm_scan_status_string(int status);
 

@@ -15,6 +15,7 @@
 #include "kernel_chunked.h"
 #include "kernel_step.h"
 #include "kernel_backward.h"
+#include "kernel_ssd.h"
 
 namespace {
 
@@ -152,6 +153,27 @@ int launch_bwd(const ssm_scan_desc_t* d, const ssm::BwdParams& p, hipStream_t s)
 size_t bwd_workspace(const ssm_scan_desc_t* d) {
     const int64_t nseg = (d->seqlen + ssm::bwd::kSeg - 1) / ssm::bwd::kSeg;
     return static_cast<size_t>(nseg * d->batch * d->dim * d->dstate * (d->is_complex ? 8 : 4));
+}
+
+int check_ssd_desc(const ssm_ssd_desc_t* d) {
+    if (!d) return SSM_ERR_INVALID_ARGUMENT;
+    if (d->batch < 1 || d->seqlen < 1 || d->dim < 1 || d->dstate < 1 || d->headdim < 1)
+        return SSM_ERR_INVALID_ARGUMENT;
+    if (d->io_dtype != SSM_DTYPE_F32 && d->io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
+    if (d->io_dtype != SSM_DTYPE_BF16 || d->headdim != ssm::ssd::kP || d->dim % d->headdim != 0 ||
+        d->dstate > ssm::ssd::kMaxN)
+        return SSM_ERR_UNSUPPORTED;
+    int64_t r;
+    if (__builtin_mul_overflow(d->batch, d->seqlen, &r) || __builtin_mul_overflow(r, d->dim, &r) ||
+        __builtin_mul_overflow(r, int64_t(8), &r))
+        return SSM_ERR_INVALID_ARGUMENT;
+    return SSM_OK;
+}
+
+size_t ssd_workspace(const ssm_ssd_desc_t* d) {
+    const int64_t H = d->dim / d->headdim, nC = (d->seqlen + ssm::ssd::kQ - 1) / ssm::ssd::kQ;
+    const int64_t planes = d->batch * H * nC;
+    return static_cast<size_t>(2 * ssm::round256(planes * d->dstate * d->headdim * 4) + ssm::round256(planes * 4));
 }
 
 // Pointer checks shared by the scan and the step: required inputs present,
@@ -321,6 +343,46 @@ int ssm_scan_bwd(const ssm_scan_desc_t* desc, const void* u, const void* delta, 
     p.lpc = next_pow2(desc->dstate);
     hipStream_t s = static_cast<hipStream_t>(stream);
     return desc->io_dtype == SSM_DTYPE_F32 ? launch_bwd<float>(desc, p, s) : launch_bwd<uint16_t>(desc, p, s);
+}
+
+size_t ssm_ssd_workspace_bytes(const ssm_ssd_desc_t* desc) {
+    if (check_ssd_desc(desc) != SSM_OK) return 0;
+    return ssd_workspace(desc);
+}
+
+int ssm_ssd_fwd(const ssm_ssd_desc_t* desc, const void* u, const void* delta, const float* A, const void* B,
+                const void* C, const float* D, void* y, float* h_last, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    const int st = check_ssd_desc(desc);
+    if (st != SSM_OK) return st;
+    if (!u || !delta || !A || !B || !C || !y) return SSM_ERR_INVALID_ARGUMENT;
+    const void* io_ptrs[] = {u, delta, B, C, y};
+    for (const void* q : io_ptrs)
+        if (!aligned(q, 2)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!aligned(A, 4) || (D && !aligned(D, 4)) || (h_last && !aligned(h_last, 4))) return SSM_ERR_INVALID_ARGUMENT;
+    const size_t need = ssd_workspace(desc);
+    if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(workspace, 256)) return SSM_ERR_INVALID_ARGUMENT;
+
+    ssm::SsdParams p{};
+    p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.y = y; p.h_last = h_last;
+    p.batch = desc->batch; p.seqlen = desc->seqlen; p.dim = desc->dim; p.dstate = desc->dstate;
+    p.heads = desc->dim / desc->headdim;
+    p.nchunks = (desc->seqlen + ssm::ssd::kQ - 1) / ssm::ssd::kQ;
+    const int64_t planes = p.batch * p.heads * p.nchunks;
+    char* ws = static_cast<char*>(workspace);
+    const uint64_t plane_bytes = ssm::round256(planes * p.dstate * ssm::ssd::kP * 4);
+    p.S = reinterpret_cast<float*>(ws);
+    p.Hin = reinterpret_cast<float*>(ws + plane_bytes);
+    p.E = reinterpret_cast<float*>(ws + 2 * plane_bytes);
+    if (planes > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+    const int64_t pass_threads = p.batch * p.heads * p.dstate * ssm::ssd::kP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(ssm::ssd_state_kernel<uint16_t>, dim3(static_cast<unsigned>(planes)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(ssm::ssd_pass_kernel, dim3(static_cast<unsigned>((pass_threads + 255) / 256)), dim3(256), 0, s,
+                       p);
+    hipLaunchKernelGGL(ssm::ssd_out_kernel<uint16_t>, dim3(static_cast<unsigned>(planes)), dim3(256), 0, s, p);
+    return hip_status(hipGetLastError());
 }
 
 }  // extern "C"

@@ -184,3 +184,70 @@ def channel_sample(inputs: dict, d_index) -> dict:
 def all_channels(inputs: dict) -> dict:
     """Host fp64 copies of every input (small workloads only)."""
     return channel_sample(inputs, range(inputs["u"].shape[2]))
+
+
+# ---- the state-space dual (SSD) setting: heads of `headdim` channels sharing
+# a step size per (b, t, head) and a scalar A per head; real state,
+# exponential-Euler b-terms, B and C shared by all heads, bf16 I/O.  Fields are
+# drawn like the other workloads': u, B, C, D ~ N(0, 1), delta per head =
+# softplus(N(-3, 0.5)), A per head = -exp(U(-3, 0)).
+@dataclasses.dataclass(frozen=True)
+class SsdWorkload:
+    name: str
+    batch: int
+    dim: int
+    seqlen: int
+    dstate: int
+    headdim: int = 64
+    io_dtype: str = "bf16"
+    delta_mu: float = -3.0
+    delta_sigma: float = 0.5
+
+    @property
+    def heads(self):
+        return self.dim // self.headdim
+
+    def scaled(self, **kw) -> "SsdWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+SSD_WORKLOADS = {
+    "ssd_real_bf16_b4_d2560_l8192_n16_p64": SsdWorkload("ssd_real_bf16_b4_d2560_l8192_n16_p64", 4, 2560, 8192, 16),
+}
+
+
+def make_ssd_inputs(w: SsdWorkload, seed: Optional[int] = None, device="cpu") -> dict:
+    """One seeded instance of an SSD workload: u (B,L,D), delta (B,L,H),
+    A (H,), Bm, Cm (B,L,N), Dskip (D,)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(SEED_BASE + 100 if seed is None else seed)
+    io = torch_dtype(w.io_dtype)
+    B, L, D, N, H = w.batch, w.seqlen, w.dim, w.dstate, w.heads
+    kw = dict(device=device)
+    u = _fill(torch.empty((B, L, D), dtype=io, **kw), gen, "normal", 0.0, 1.0)
+    delta = _fill(torch.empty((B, L, H), dtype=io, **kw), gen, "normal", w.delta_mu, w.delta_sigma,
+                  post=torch.nn.functional.softplus)
+    A = _fill(torch.empty((H,), dtype=torch.float32, **kw), gen, "uniform", -3.0, 0.0, post=lambda v: -torch.exp(v))
+    Bm = _fill(torch.empty((B, L, N), dtype=io, **kw), gen, "normal", 0.0, 1.0)
+    Cm = _fill(torch.empty((B, L, N), dtype=io, **kw), gen, "normal", 0.0, 1.0)
+    Dskip = _fill(torch.empty((D,), dtype=torch.float32, **kw), gen, "normal", 0.0, 1.0)
+    return dict(u=u, delta=delta, A=A, Bm=Bm, Cm=Cm, Dskip=Dskip)
+
+
+def ssd_as_scan(inputs: dict, w: SsdWorkload, d_index=None) -> dict:
+    """The same problem in the scan's layout (delta per channel, A per (d, n)),
+    for channels d_index (all when None), as host fp64 arrays (exact widening)."""
+    D = w.dim
+    idx = list(range(D)) if d_index is None else list(d_index)
+    heads = torch.as_tensor([d // w.headdim for d in idx], device=inputs["u"].device)
+    sel = torch.as_tensor(idx, device=inputs["u"].device)
+
+    def host(t):
+        return t.float().cpu().double().numpy()
+
+    return dict(
+        u=host(inputs["u"].index_select(2, sel)),
+        delta=host(inputs["delta"].index_select(2, heads)),
+        A=host(inputs["A"].index_select(0, heads)[:, None].expand(len(idx), w.dstate)),
+        Bm=host(inputs["Bm"]), Cm=host(inputs["Cm"]),
+        Dskip=host(inputs["Dskip"].index_select(0, sel)), theta=None, lam=None)

@@ -29,6 +29,14 @@ class ScanDesc(ctypes.Structure):
     ]
 
 
+class SsdDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("headdim", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 class ScanError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -59,6 +67,10 @@ def _lib():
     lib.ssm_scan_bwd.restype = ctypes.c_int
     lib.ssm_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
     lib.ssm_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssm_ssd_fwd.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 9 + [ctypes.c_size_t, vp]
+    lib.ssm_ssd_fwd.restype = ctypes.c_int
+    lib.ssm_ssd_workspace_bytes.argtypes = [ctypes.POINTER(SsdDesc)]
+    lib.ssm_ssd_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
     lib.ssm_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_scan_status_string.argtypes = [ctypes.c_int]
@@ -219,3 +231,38 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, theta=None, lam=None, h0=None, *, dy
     if st != 0:
         raise ScanError(st, "ssm_scan_bwd")
     return g
+
+
+def make_ssd_desc(batch, seqlen, dim, dstate, headdim, io_dtype) -> SsdDesc:
+    return SsdDesc(int(batch), int(seqlen), int(dim), int(dstate), int(headdim),
+                   int(SSM_DTYPE.get(io_dtype, io_dtype)), 0)
+
+
+def ssm_ssd_workspace_bytes(desc: SsdDesc) -> int:
+    return int(_lib().ssm_ssd_workspace_bytes(ctypes.byref(desc)))
+
+
+def ssm_ssd_fwd(u, delta, A, B, C, D=None, *, headdim: int = 64, y=None, h_last=None, want_h_last: bool = True,
+                workspace=None, stream=None):
+    """The SSD form on torch device tensors; returns (y, h_last).
+
+    u (B,L,D) bf16; delta (B,L,H) bf16 with H = D / headdim; A (H,) fp32;
+    B, C (B,L,N) bf16; D (D,) fp32.
+    """
+    Bsz, L, Dm = u.shape
+    N = B.shape[2]
+    desc = make_ssd_desc(Bsz, L, Dm, N, headdim, u.dtype)
+    if y is None:
+        y = torch.empty_like(u)
+    if h_last is None and want_h_last:
+        h_last = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=u.device)
+    need = ssm_ssd_workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream if u.is_cuda else 0
+    st = _lib().ssm_ssd_fwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y),
+                            _ptr(h_last), _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+    if st != 0:
+        raise ScanError(st, "ssm_ssd_fwd")
+    return y, h_last

@@ -21,15 +21,15 @@ P = 0x10000  # an aligned fake device address (never dereferenced)
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(ssm_scan_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ssm_(?:scan|ssd)_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     lib = scan._lib()
     names = declared_functions()
     assert {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_step", "ssm_scan_bwd", "ssm_scan_workspace_bytes",
-            "ssm_scan_bwd_workspace_bytes", "ssm_scan_status_string", "ssm_scan_abi_version",
-            "ssm_scan_last_hip_error"} <= set(names)
+            "ssm_scan_bwd_workspace_bytes", "ssm_ssd_fwd", "ssm_ssd_workspace_bytes", "ssm_scan_status_string",
+            "ssm_scan_abi_version", "ssm_scan_last_hip_error"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -179,3 +179,33 @@ def test_backward_argument_rules():
     assert call_bwd(d, ws=0) == WS_SMALL
     assert call_bwd(d, ws_bytes=need - 1) == WS_SMALL
     assert call_bwd(d, ws=P + 64, ws_bytes=need) == INVALID            # not 256-byte aligned
+
+
+def call_ssd(desc, u=P, delta=P, A=P, B=P, C=P, D=0, y=P, h=0, ws=P, ws_bytes=1 << 40):
+    lib = scan._lib()
+    dp = None if desc is None else ctypes.byref(desc)
+    args = [u, delta, A, B, C, D, y, h, ws]
+    return lib.ssm_ssd_fwd(dp, *[ctypes.c_void_p(a) if a else None for a in args], ws_bytes, None)
+
+
+def ssd_desc(B=1, L=100, D=128, N=16, P=64, dtype="bf16"):
+    return scan.make_ssd_desc(B, L, D, N, P, {"f32": 0, "bf16": 1}[dtype])
+
+
+def test_ssd_argument_rules():
+    assert call_ssd(None) == INVALID
+    for kw in [dict(B=0), dict(L=0), dict(D=0), dict(N=0), dict(P=0)]:
+        assert call_ssd(ssd_desc(**kw)) == INVALID, kw
+    assert call_ssd(ssd_desc(dtype="f32")) == UNSUPPORTED
+    assert call_ssd(ssd_desc(P=32, D=128)) == UNSUPPORTED
+    assert call_ssd(ssd_desc(D=100)) == UNSUPPORTED
+    assert call_ssd(ssd_desc(N=65)) == UNSUPPORTED
+    for k in ["u", "delta", "A", "B", "C", "y"]:
+        assert call_ssd(ssd_desc(), **{k: 0}) == INVALID, k
+    assert call_ssd(ssd_desc(), u=P + 1) == INVALID
+    d = ssd_desc(B=2, L=100, D=128, N=16)
+    need = scan.ssm_ssd_workspace_bytes(d)
+    assert need == 2 * (2 * 2 * 2 * 16 * 64 * 4) + 256           # 2 rows x 2 heads x 2 chunks
+    assert call_ssd(d, ws=0) == WS_SMALL
+    assert call_ssd(d, ws_bytes=need - 1) == WS_SMALL
+    assert call_ssd(d, ws=P + 64, ws_bytes=need) == INVALID
