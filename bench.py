@@ -22,7 +22,8 @@ is stated.  A decode workload (--workload decode_...) times ssm_scan_step
 instead: a step is one token for every sequence of the batch, the state read
 and written in HBM, and the same line is printed with B*D tokens*channels per
 step.  --backward times ssm_scan_bwd (all input gradients of the scan) on the
-workload instead of the forward scan.
+workload instead of the forward scan.  An SSD workload (--workload ssd_...)
+times ssm_ssd_fwd, the chunked matrix form for heads with a scalar decay.
 """
 from __future__ import annotations
 
@@ -86,6 +87,13 @@ def backward_algorithmic_bytes(w) -> int:
     writes = (4 * B * L * D * (2 + trap) + 4 * B * L * D * N * cplx + 2 * 4 * B * L * N * (1 + cplx)
               + 4 * D * N + 4 * D)
     return reads + writes
+
+
+def ssd_algorithmic_bytes(w) -> int:
+    """The SSD form: u, delta (per head), B, C, A, D read once; y, h_last written once."""
+    e = 2
+    B, L, D, N, H = w.batch, w.seqlen, w.dim, w.dstate, w.heads
+    return e * B * L * D * 2 + e * B * L * H + 2 * e * B * L * N + 4 * H + 4 * D + 4 * B * D * N
 
 
 def kernel_source_hash() -> str:
@@ -325,6 +333,78 @@ def bench_backward(args, w, torch, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_ssd(args, w, torch, dev):
+    import numpy as np
+
+    from selective_state_space_42_amd.inputs import make_ssd_inputs, ssd_as_scan
+    from selective_state_space_42_amd.scan import make_ssd_desc, ssm_ssd_fwd, ssm_ssd_workspace_bytes
+
+    log(f"generating {w.name} on {torch.cuda.get_device_name(dev)}")
+    inputs = make_ssd_inputs(w, device=dev)
+    y = torch.empty_like(inputs["u"])
+    h_last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+    desc = make_ssd_desc(w.batch, w.seqlen, w.dim, w.dstate, w.headdim, inputs["u"].dtype)
+    ws = torch.empty(max(ssm_ssd_workspace_bytes(desc), 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ssm_ssd_fwd(inputs["u"], inputs["delta"], inputs["A"], inputs["Bm"], inputs["Cm"], inputs["Dskip"],
+                    headdim=w.headdim, y=y, h_last=h_last, workspace=ws, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    log(f"timed {args.steps} SSD passes: {ms:.3f} ms each")
+    alg = ssd_algorithmic_bytes(w)
+    achieved = alg / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": w.batch * w.seqlen * w.dim / (ms * 1e-3), "unit": UNIT, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen, "dstate": w.dstate,
+                   "headdim": w.headdim, "disc": "euler", "complex": False, "io_dtype": w.io_dtype, "algo": "ssd"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profile(w.name, "ssd"),
+                     "algorithmic_bytes_per_launch": alg},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        log("timing the fp64 oracle on a channel sample")
+        threads = max(1, min(os.cpu_count() or 1, 64))
+        order = np.random.default_rng(0).permutation(w.dim).tolist()
+        spent, tc, used, err, groups = 0.0, 0, 0, 0.0, 0
+        for g0 in range(0, w.dim, threads):
+            idx = sorted(order[g0:g0 + threads])
+            x = ssd_as_scan(inputs, w, idx)
+            t0 = time.perf_counter()
+            y_ref, _ = oracle.scan(x["u"], x["delta"], x["A"], x["Bm"], x["Cm"], x["Dskip"], disc="euler",
+                                   is_complex=False, nthreads=len(idx))
+            spent += time.perf_counter() - t0
+            tc += w.batch * w.seqlen * len(idx)
+            used = max(used, len(idx))
+            groups += 1
+            yg = y.index_select(2, torch.as_tensor(idx, device=dev)).float().cpu().double().numpy()
+            err = max(err, float(np.max(np.abs(yg - y_ref)) / np.max(np.abs(y_ref))))
+            if spent >= args.cpu_seconds:
+                break
+        out["cpu_baseline"] = {
+            "value": tc / spent, "unit": UNIT, "cores": used, "kind": "oracle",
+            "sample": f"{tc // (w.batch * w.seqlen)} of {w.dim} channels (random, seed 0) in {groups} group(s), "
+                      f"every batch row and step, as the equivalent scan: {tc} tokens*channels in {spent:.1f} s "
+                      f"of fp64 C oracle time on {used} pthreads",
+            "parity_err_y_on_sample": err}
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration(torch, dev, nbytes: int, steps: int, warmup: int):
     """A plain copy of known size: reads and writes `nbytes` per launch."""
     n = (nbytes + 15) // 16 * 4
@@ -366,7 +446,7 @@ def main():
 
     import torch
 
-    from selective_state_space_42_amd.inputs import DECODE_WORKLOADS, WORKLOADS, make_inputs
+    from selective_state_space_42_amd.inputs import DECODE_WORKLOADS, SSD_WORKLOADS, WORKLOADS, make_inputs
     from selective_state_space_42_amd.scan import make_desc, ssm_scan_fwd, ssm_scan_workspace_bytes
 
     dev = torch.device("cuda:0")
@@ -376,6 +456,9 @@ def main():
         return
     if args.workload in DECODE_WORKLOADS:
         bench_decode(args, DECODE_WORKLOADS[args.workload], torch, dev)
+        return
+    if args.workload in SSD_WORKLOADS:
+        bench_ssd(args, SSD_WORKLOADS[args.workload], torch, dev)
         return
     w = WORKLOADS[args.workload]
     if args.backward:
