@@ -273,7 +273,7 @@ typedef struct {
 size_t ssm_ssd_workspace_bytes(const ssm_ssd_desc_t *desc);
 
 /*
- *   u       [B][L][D]   bf16     inputs
+ *   u       [B][L][D]   bf16     inputs (16-byte aligned: read in rows of 8 channels)
  *   delta   [B][L][H]   bf16     step size of each head (H = D / headdim)
  *   A       [H]         fp32     scalar decay rate of each head
  *   B, C    [B][L][N]   bf16     projections shared by all heads

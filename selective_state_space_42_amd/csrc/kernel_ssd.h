@@ -15,9 +15,12 @@
 //   Y[t, p]   = sum_{s <= t} exp(cum_t - cum_s) (C_t . B_s) delta_s X[s, p]   (intra-chunk)
 //             + exp(cum_t) sum_n C_t[n] H_in[n, p]                            (state entering the chunk)
 //   H_out     = exp(cum_{Q-1}) H_in + sum_s exp(cum_{Q-1} - cum_s) delta_s B_s X[s, :]
-// The intra-chunk product (Q x Q) . (Q x P) is a dense contraction: it runs
-// on the bf16 MFMA units (v_mfma_f32_32x32x8_bf16, fp32 accumulation); the
-// small terms over N run on the vector units.
+// Every term is a dense contraction and runs on the bf16 MFMA units
+// (v_mfma_f32_32x32x8_bf16, fp32 accumulation): C B^T (Q x N . N x Q), the
+// intra-chunk product (Q x Q . Q x P), C H_in (Q x N . N x P) and the chunk
+// state (N x Q . Q x P).  The operands are rounded to bf16 (u, B and C are
+// bf16 already; the decay-weighted matrix, the weighted B and H_in are
+// rounded); exp of the cumulative decays runs on the vector units.
 //
 // Three kernels (per batch row b and head h, chunks of Q = 64 steps, heads of
 // P = 64 channels):
@@ -67,49 +70,103 @@ __device__ __forceinline__ void ssd_cumsum_wave(float* s, int lane) {
     s[lane] = v;
 }
 
+typedef short ssd_bf16x4 __attribute__((ext_vector_type(4)));
+typedef float ssd_f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint16_t ssd_bf16(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+
+// One 32 x 32 block of A . B with K = 8 * ksteps on the bf16 MFMA units, both
+// operands in LDS with k contiguous: a_rows[i][k] (rows i0 ..) and b_cols[j][k]
+// (columns j0 ..).  Lane l supplies A[i0 + l % 32][k0 + 4 (l / 32) + 0..3] and
+// B[k0 + 4 (l / 32) + 0..3][j0 + l % 32]; the 32 x 32 result is spread as
+// acc[r] = C[i0 + 8 (r / 4) + 4 (l / 32) + r % 4][j0 + l % 32].
+template <int kStride>
+__device__ __forceinline__ void ssd_mfma_block(const uint16_t (*a_rows)[kStride], const uint16_t (*b_cols)[kStride],
+                                               int i0, int j0, int ksteps, int lane, ssd_f32x16& acc) {
+    const int kh = lane >> 5;
+    for (int ks = 0; ks < ksteps; ++ks) {
+        const int k0 = ks * 8 + 4 * kh;
+        const ssd_bf16x4 av = *reinterpret_cast<const ssd_bf16x4*>(&a_rows[i0 + (lane & 31)][k0]);
+        const ssd_bf16x4 bv = *reinterpret_cast<const ssd_bf16x4*>(&b_cols[j0 + (lane & 31)][k0]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(av, bv, acc, 0, 0, 0);
+    }
+}
+
+// X of one (chunk, head) into LDS transposed (rows p, columns t), zero past
+// the sequence end: 16-byte loads of 8 channels each (the head's 64 channels
+// of a step are one 128-byte row).
+template <typename T>
+__device__ __forceinline__ void ssd_load_xt(const T* u, int64_t row0, int64_t D, int len, int tid,
+                                            uint16_t (*s_xt)[ssd::kQ + ssd::kPad]) {
+    static_assert(sizeof(T) == 2, "bf16 rows");
+    for (int i = tid; i < ssd::kQ * ssd::kP / 8; i += 256) {
+        const int t = i / (ssd::kP / 8), p8 = (i % (ssd::kP / 8)) * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (t < len) v = *reinterpret_cast<const uint4*>(u + (row0 + t) * D + p8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            s_xt[p8 + 2 * q][t] = static_cast<uint16_t>(w[q]);
+            s_xt[p8 + 2 * q + 1][t] = static_cast<uint16_t>(w[q] >> 16);
+        }
+    }
+}
+
+constexpr float kSsdLog2e = 1.4426950408889634f;
+
+// row of element r of a lane's 32 x 32 accumulator block
+__device__ __forceinline__ int ssd_acc_row(int i0, int lane, int r) { return i0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
 template <typename T>
 __global__ void __launch_bounds__(256) ssd_state_kernel(SsdParams p) {
     using namespace ssd;
     using E = Elem<T>;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t nC = p.nchunks, H = p.heads, L = p.seqlen, D = p.dim, N = p.dstate;
     const int64_t c = blockIdx.x % nC, bh = blockIdx.x / nC, b = bh / H, h = bh % H;
     const int64_t t0 = c * kQ;
     const int len = static_cast<int>(L - t0 < kQ ? L - t0 : kQ);
-    __shared__ float s_x[kQ][kP + 1];
-    __shared__ float s_b[kQ][kMaxN + 1];
+    // S = (B o w)^T X as an (N x Q)(Q x P) product: rows n (padded to 64),
+    // k = t contiguous in both operands
+    __shared__ __align__(16) uint16_t s_bw[kMaxN][kQ + kPad];  // B[t][n] w_t, transposed
+    __shared__ __align__(16) uint16_t s_xt[kP][kQ + kPad];     // X transposed
     __shared__ float s_cum[kQ], s_w[kQ];
     const T* u = static_cast<const T*>(p.u);
     const T* Bm = static_cast<const T*>(p.B);
     const T* dl = static_cast<const T*>(p.delta);
-    for (int i = tid; i < kQ * kP; i += 256) {
-        const int t = i / kP, pp = i % kP;
-        s_x[t][pp] = t < len ? E::load(u, (b * L + t0 + t) * D + h * kP + pp) : 0.f;
-    }
-    for (int i = tid; i < kQ * N; i += 256) {
-        const int t = static_cast<int>(i / N), n = static_cast<int>(i % N);
-        s_b[t][n] = t < len ? E::load(Bm, (b * L + t0 + t) * N + n) : 0.f;
-    }
-    const float a = p.A[h];
+    ssd_load_xt<T>(u + h * kP, b * L + t0, D, len, tid, s_xt);
+    // cumulative decays in log2 units: exp(cum) = 2^(cum log2 e) on the hardware exp2
+    const float a2 = p.A[h] * kSsdLog2e;
     if (tid < kQ) {
         const float dt = tid < len ? E::load(dl, (b * L + t0 + tid) * H + h) : 0.f;
         s_w[tid] = dt;
-        s_cum[tid] = dt * a;
+        s_cum[tid] = dt * a2;
         ssd_cumsum_wave(s_cum, tid);
+        s_w[tid] = dt * __builtin_amdgcn_exp2f(s_cum[kQ - 1] - s_cum[tid]);  // exp(cum_{Q-1} - cum_t) delta_t
     }
     __syncthreads();
-    const float last = s_cum[kQ - 1];
-    if (tid < kQ) s_w[tid] *= expf(last - s_cum[tid]);  // exp(cum_{Q-1} - cum_s) delta_s
-    __syncthreads();
-    float* S = p.S + (bh * nC + c) * N * kP;
-    for (int i = tid; i < N * kP; i += 256) {
-        const int n = i / kP, pp = i % kP;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int t = 0; t < kQ; ++t) acc = fmaf(s_b[t][n] * s_w[t], s_x[t][pp], acc);
-        S[i] = acc;
+    const int nrows = N <= 32 ? 32 : 64;
+    for (int i = tid; i < nrows * kQ; i += 256) {
+        const int n = i / kQ, t = i % kQ;
+        const float v = (n < N && t < len) ? E::load(Bm, (b * L + t0 + t) * N + n) * s_w[t] : 0.f;
+        s_bw[n][t] = ssd_bf16(v);
     }
-    if (tid == 0) p.E[bh * nC + c] = expf(last);
+    __syncthreads();
+    // wave w: rows n0 = 32 (w / 2) (if present), columns p0 = 32 (w % 2)
+    const int n0 = 32 * (wave >> 1), p0 = 32 * (wave & 1);
+    if (n0 < nrows) {
+        ssd_f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        ssd_mfma_block<kQ + kPad>(s_bw, s_xt, n0, p0, kQ / 8, lane, acc);
+        float* S = p.S + (bh * nC + c) * N * kP;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int n = ssd_acc_row(n0, lane, r);
+            if (n < N) S[n * kP + p0 + (lane & 31)] = acc[r];
+        }
+    }
+    if (tid == 0) p.E[bh * nC + c] = __builtin_amdgcn_exp2f(s_cum[kQ - 1]);
 }
 
 __global__ void __launch_bounds__(256) ssd_pass_kernel(SsdParams p) {
@@ -147,9 +204,6 @@ __global__ void __launch_bounds__(256) ssd_pass_kernel(SsdParams p) {
     }
 }
 
-typedef short ssd_bf16x4 __attribute__((ext_vector_type(4)));
-typedef float ssd_f32x16 __attribute__((ext_vector_type(16)));
-
 template <typename T>
 __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
     using namespace ssd;
@@ -159,77 +213,72 @@ __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
     const int64_t c = blockIdx.x % nC, bh = blockIdx.x / nC, b = bh / H, h = bh % H;
     const int64_t t0 = c * kQ;
     const int len = static_cast<int>(L - t0 < kQ ? L - t0 : kQ);
-    // MFMA operands in bf16: M = (C B^T) o decay o delta (rows t, columns s) and
-    // X transposed (rows p, columns s), so each lane's 4 consecutive k values
-    // are one 8-byte LDS read
-    __shared__ __align__(16) uint16_t s_m[kQ][kQ + kPad];
+    const int npad = static_cast<int>((N + 7) / 8 * 8);  // K of the products over n
+    // bf16 MFMA operands, k contiguous: C and B rows (k = n), H_in transposed
+    // (rows p, k = n), X transposed (rows p, k = s), M (rows t, k = s)
+    __shared__ __align__(16) uint16_t s_c[kQ][kMaxN + kPad];
+    __shared__ __align__(16) uint16_t s_b[kQ][kMaxN + kPad];
+    __shared__ __align__(16) uint16_t s_ht[kP][kMaxN + kPad];
     __shared__ __align__(16) uint16_t s_xt[kP][kQ + kPad];
-    __shared__ float s_c[kQ][kMaxN + 1];
-    __shared__ float s_b[kQ][kMaxN + 1];
-    __shared__ float s_h[kMaxN][kP + 1];
+    __shared__ __align__(16) uint16_t s_m[kQ][kQ + kPad];
     __shared__ float s_cum[kQ], s_dt[kQ];
     const T* u = static_cast<const T*>(p.u);
     const T* Bm = static_cast<const T*>(p.B);
     const T* Cm = static_cast<const T*>(p.C);
     const T* dl = static_cast<const T*>(p.delta);
-    for (int i = tid; i < kQ * kP; i += 256) {
-        const int t = i / kP, pp = i % kP;
-        const float x = t < len ? E::load(u, (b * L + t0 + t) * D + h * kP + pp) : 0.f;
-        s_xt[pp][t] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));  // exact for bf16 input
-    }
-    for (int i = tid; i < kQ * N; i += 256) {
-        const int t = static_cast<int>(i / N), n = static_cast<int>(i % N);
-        const bool ok = t < len;
-        s_b[t][n] = ok ? E::load(Bm, (b * L + t0 + t) * N + n) : 0.f;
-        s_c[t][n] = ok ? E::load(Cm, (b * L + t0 + t) * N + n) : 0.f;
+    ssd_load_xt<T>(u + h * kP, b * L + t0, D, len, tid, s_xt);
+    for (int i = tid; i < kQ * npad; i += 256) {
+        const int t = i / npad, n = i % npad;
+        const bool ok = t < len && n < N;
+        s_b[t][n] = ok ? ssd_bf16(E::load(Bm, (b * L + t0 + t) * N + n)) : uint16_t(0);
+        s_c[t][n] = ok ? ssd_bf16(E::load(Cm, (b * L + t0 + t) * N + n)) : uint16_t(0);
     }
     const float* Hin = p.Hin + (bh * nC + c) * N * kP;
-    for (int i = tid; i < N * kP; i += 256) s_h[i / kP][i % kP] = Hin[i];
-    const float a = p.A[h];
+    for (int i = tid; i < npad * kP; i += 256) {
+        const int n = i / kP, pp = i % kP;
+        s_ht[pp][n] = n < N ? ssd_bf16(Hin[n * kP + pp]) : uint16_t(0);
+    }
+    const float a2 = p.A[h] * kSsdLog2e;  // cumulative decays in log2 units
     if (tid < kQ) {
         const float dt = tid < len ? E::load(dl, (b * L + t0 + tid) * H + h) : 0.f;
         s_dt[tid] = dt;
-        s_cum[tid] = dt * a;
+        s_cum[tid] = dt * a2;
         ssd_cumsum_wave(s_cum, tid);
     }
     __syncthreads();
-    // M[t][s] = (C_t . B_s) exp(cum_t - cum_s) delta_s for s <= t, else 0
-    for (int i = tid; i < kQ * kQ; i += 256) {
-        const int t = i / kQ, s = i % kQ;
-        float v = 0.f;
-        if (s <= t) {
-            float g = 0.f;
-            for (int n = 0; n < N; ++n) g = fmaf(s_c[t][n], s_b[s][n], g);
-            v = g * expf(s_cum[t] - s_cum[s]) * s_dt[s];
+    // G = C B^T: wave w forms block (rows t 32 (w / 2), columns s 32 (w % 2)) and
+    // turns it into M = G o exp(cum_t - cum_s) o delta_s (zero above the
+    // diagonal); the block above the diagonal is never read
+    const int gi = 32 * (wave >> 1), gs = 32 * (wave & 1);
+    if (gs <= gi) {
+        ssd_f32x16 g;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) g[r] = 0.f;
+        ssd_mfma_block<kMaxN + kPad>(s_c, s_b, gi, gs, npad / 8, lane, g);
+        const int sc = gs + (lane & 31);
+        const float cs = s_cum[sc], ds = s_dt[sc];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = ssd_acc_row(gi, lane, r);
+            s_m[t][sc] = ssd_bf16(sc <= t ? g[r] * __builtin_amdgcn_exp2f(s_cum[t] - cs) * ds : 0.f);
         }
-        s_m[t][s] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
     }
     __syncthreads();
-    // Y_intra: wave w computes rows i0 .. i0+31, columns j0 .. j0+31; column
-    // blocks past the rows are zero (causal) and skipped
-    const int i0 = (wave >> 1) * 32, j0 = (wave & 1) * 32;
-    ssd_f32x16 acc;
+    // Y = M X + diag(exp(cum)) C H_in: wave w computes rows i0, columns j0
+    const int i0 = 32 * (wave >> 1), j0 = 32 * (wave & 1);
+    ssd_f32x16 acc, inter;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    const int kh = lane >> 5;  // which 4 of the 8 k values of a step
-#pragma unroll
-    for (int k0 = 0; k0 < kQ; k0 += 8) {
-        if (k0 >= i0 + 32) break;  // uniform per wave
-        const ssd_bf16x4 av = *reinterpret_cast<const ssd_bf16x4*>(&s_m[i0 + (lane & 31)][k0 + 4 * kh]);
-        const ssd_bf16x4 bv = *reinterpret_cast<const ssd_bf16x4*>(&s_xt[j0 + (lane & 31)][k0 + 4 * kh]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(av, bv, acc, 0, 0, 0);
-    }
-    // outputs: lane holds column j, rows i = i0 + 8 (r / 4) + 4 kh + r % 4
+    for (int r = 0; r < 16; ++r) acc[r] = inter[r] = 0.f;
+    ssd_mfma_block<kQ + kPad>(s_m, s_xt, i0, j0, (i0 + 32) / 8, lane, acc);  // causal: k < i0 + 32
+    ssd_mfma_block<kMaxN + kPad>(s_c, s_ht, i0, j0, npad / 8, lane, inter);
     const int j = j0 + (lane & 31);
     const float dsk = p.Dskip ? p.Dskip[h * kP + j] : 0.f;
     T* y = static_cast<T*>(p.y);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int i = i0 + 8 * (r >> 2) + 4 * kh + (r & 3);
-        float inter = 0.f;
-        for (int n = 0; n < N; ++n) inter = fmaf(s_c[i][n], s_h[n][j], inter);
+        const int i = ssd_acc_row(i0, lane, r);
         const float x = __uint_as_float(static_cast<uint32_t>(s_xt[j][i]) << 16);
-        const float v = acc[r] + expf(s_cum[i]) * inter + dsk * x;
+        const float v = acc[r] + __builtin_amdgcn_exp2f(s_cum[i]) * inter[r] + dsk * x;
         if (i < len) E::store(y, (b * L + t0 + i) * D + h * kP + j, v);
     }
 }
