@@ -117,7 +117,9 @@ constexpr float kSsdLog2e = 1.4426950408889634f;
 // row of element r of a lane's 32 x 32 accumulator block
 __device__ __forceinline__ int ssd_acc_row(int i0, int lane, int r) { return i0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-template <typename T>
+// NMAX: the largest N the instantiation handles (16 or 64); it sizes the LDS
+// tiles, so small state sizes leave room for more resident workgroups.
+template <typename T, int NMAX>
 __global__ void __launch_bounds__(256) ssd_state_kernel(SsdParams p) {
     using namespace ssd;
     using E = Elem<T>;
@@ -128,7 +130,8 @@ __global__ void __launch_bounds__(256) ssd_state_kernel(SsdParams p) {
     const int len = static_cast<int>(L - t0 < kQ ? L - t0 : kQ);
     // S = (B o w)^T X as an (N x Q)(Q x P) product: rows n (padded to 64),
     // k = t contiguous in both operands
-    __shared__ __align__(16) uint16_t s_bw[kMaxN][kQ + kPad];  // B[t][n] w_t, transposed
+    constexpr int kRows = NMAX <= 32 ? 32 : 64;                  // n rows, padded to MFMA blocks
+    __shared__ __align__(16) uint16_t s_bw[kRows][kQ + kPad];  // B[t][n] w_t, transposed
     __shared__ __align__(16) uint16_t s_xt[kP][kQ + kPad];     // X transposed
     __shared__ float s_cum[kQ], s_w[kQ];
     const T* u = static_cast<const T*>(p.u);
@@ -145,7 +148,7 @@ __global__ void __launch_bounds__(256) ssd_state_kernel(SsdParams p) {
         s_w[tid] = dt * __builtin_amdgcn_exp2f(s_cum[kQ - 1] - s_cum[tid]);  // exp(cum_{Q-1} - cum_t) delta_t
     }
     __syncthreads();
-    const int nrows = N <= 32 ? 32 : 64;
+    const int nrows = N <= 32 ? 32 : kRows;
     for (int i = tid; i < nrows * kQ; i += 256) {
         const int n = i / kQ, t = i % kQ;
         const float v = (n < N && t < len) ? E::load(Bm, (b * L + t0 + t) * N + n) * s_w[t] : 0.f;
@@ -204,7 +207,7 @@ __global__ void __launch_bounds__(256) ssd_pass_kernel(SsdParams p) {
     }
 }
 
-template <typename T>
+template <typename T, int NMAX>
 __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
     using namespace ssd;
     using E = Elem<T>;
@@ -216,9 +219,9 @@ __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
     const int npad = static_cast<int>((N + 7) / 8 * 8);  // K of the products over n
     // bf16 MFMA operands, k contiguous: C and B rows (k = n), H_in transposed
     // (rows p, k = n), X transposed (rows p, k = s), M (rows t, k = s)
-    __shared__ __align__(16) uint16_t s_c[kQ][kMaxN + kPad];
-    __shared__ __align__(16) uint16_t s_b[kQ][kMaxN + kPad];
-    __shared__ __align__(16) uint16_t s_ht[kP][kMaxN + kPad];
+    __shared__ __align__(16) uint16_t s_c[kQ][NMAX + kPad];
+    __shared__ __align__(16) uint16_t s_b[kQ][NMAX + kPad];
+    __shared__ __align__(16) uint16_t s_ht[kP][NMAX + kPad];
     __shared__ __align__(16) uint16_t s_xt[kP][kQ + kPad];
     __shared__ __align__(16) uint16_t s_m[kQ][kQ + kPad];
     __shared__ float s_cum[kQ], s_dt[kQ];
@@ -254,7 +257,7 @@ __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
         ssd_f32x16 g;
 #pragma unroll
         for (int r = 0; r < 16; ++r) g[r] = 0.f;
-        ssd_mfma_block<kMaxN + kPad>(s_c, s_b, gi, gs, npad / 8, lane, g);
+        ssd_mfma_block<NMAX + kPad>(s_c, s_b, gi, gs, npad / 8, lane, g);
         const int sc = gs + (lane & 31);
         const float cs = s_cum[sc], ds = s_dt[sc];
 #pragma unroll
@@ -270,7 +273,7 @@ __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = inter[r] = 0.f;
     ssd_mfma_block<kQ + kPad>(s_m, s_xt, i0, j0, (i0 + 32) / 8, lane, acc);  // causal: k < i0 + 32
-    ssd_mfma_block<kMaxN + kPad>(s_c, s_ht, i0, j0, npad / 8, lane, inter);
+    ssd_mfma_block<NMAX + kPad>(s_c, s_ht, i0, j0, npad / 8, lane, inter);
     const int j = j0 + (lane & 31);
     const float dsk = p.Dskip ? p.Dskip[h * kP + j] : 0.f;
     T* y = static_cast<T*>(p.y);

@@ -379,10 +379,17 @@ int ssm_ssd_fwd(const ssm_ssd_desc_t* desc, const void* u, const void* delta, co
     if (planes > INT32_MAX) return SSM_ERR_UNSUPPORTED;
     const int64_t pass_threads = p.batch * p.heads * p.dstate * ssm::ssd::kP;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(ssm::ssd_state_kernel<uint16_t>, dim3(static_cast<unsigned>(planes)), dim3(256), 0, s, p);
+    const dim3 grid(static_cast<unsigned>(planes));
+    if (p.dstate <= 16)
+        hipLaunchKernelGGL((ssm::ssd_state_kernel<uint16_t, 16>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((ssm::ssd_state_kernel<uint16_t, ssm::ssd::kMaxN>), grid, dim3(256), 0, s, p);
     hipLaunchKernelGGL(ssm::ssd_pass_kernel, dim3(static_cast<unsigned>((pass_threads + 255) / 256)), dim3(256), 0, s,
                        p);
-    hipLaunchKernelGGL(ssm::ssd_out_kernel<uint16_t>, dim3(static_cast<unsigned>(planes)), dim3(256), 0, s, p);
+    if (p.dstate <= 16)
+        hipLaunchKernelGGL((ssm::ssd_out_kernel<uint16_t, 16>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((ssm::ssd_out_kernel<uint16_t, ssm::ssd::kMaxN>), grid, dim3(256), 0, s, p);
     return hip_status(hipGetLastError());
 }
 
