@@ -278,7 +278,7 @@ size_t ssm_ssd_workspace_bytes(const ssm_ssd_desc_t *desc);
  *   A       [H]         fp32     scalar decay rate of each head
  *   B, C    [B][L][N]   bf16     projections shared by all heads
  *   D       [D] fp32 or NULL     skip term
- *   y       [B][L][D]   bf16     output (written)
+ *   y       [B][L][D]   bf16     output (written; 16-byte aligned like u)
  *   h_last  [B][D][N] fp32, or NULL   final state (written)
  *   workspace  ssm_ssd_workspace_bytes(desc) bytes, 256-byte aligned
  * Returns an ssm_status_t (SSM_ERR_UNSUPPORTED for fp32 I/O, headdim != 64,

@@ -276,13 +276,24 @@ __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
     ssd_mfma_block<NMAX + kPad>(s_c, s_ht, i0, j0, npad / 8, lane, inter);
     const int j = j0 + (lane & 31);
     const float dsk = p.Dskip ? p.Dskip[h * kP + j] : 0.f;
-    T* y = static_cast<T*>(p.y);
+    float v[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int i = ssd_acc_row(i0, lane, r);
         const float x = __uint_as_float(static_cast<uint32_t>(s_xt[j][i]) << 16);
-        const float v = acc[r] + __builtin_amdgcn_exp2f(s_cum[i]) * inter[r] + dsk * x;
-        if (i < len) E::store(y, (b * L + t0 + i) * D + h * kP + j, v);
+        v[r] = acc[r] + __builtin_amdgcn_exp2f(s_cum[i]) * inter[r] + dsk * x;
+    }
+    // the output tile goes through LDS (rows t, columns p; M's space, free once
+    // every wave has finished its products) and out as 16-byte row pieces
+    __syncthreads();
+    uint16_t (*s_y)[kQ + kPad] = s_m;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s_y[ssd_acc_row(i0, lane, r)][j] = ssd_bf16(v[r]);
+    __syncthreads();
+    T* y = static_cast<T*>(p.y) + h * kP;
+    for (int i = tid; i < kQ * kP / 8; i += 256) {
+        const int t = i / (kP / 8), p8 = (i % (kP / 8)) * 8;
+        if (t < len) *reinterpret_cast<uint4*>(y + (b * L + t0 + t) * D + p8) = *reinterpret_cast<const uint4*>(&s_y[t][p8]);
     }
 }
 

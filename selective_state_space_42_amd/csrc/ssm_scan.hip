@@ -359,7 +359,7 @@ int ssm_ssd_fwd(const ssm_ssd_desc_t* desc, const void* u, const void* delta, co
     const void* io_ptrs[] = {u, delta, B, C, y};
     for (const void* q : io_ptrs)
         if (!aligned(q, 2)) return SSM_ERR_INVALID_ARGUMENT;
-    if (!aligned(u, 16)) return SSM_ERR_INVALID_ARGUMENT;  // read in 16-byte rows of 8 channels
+    if (!aligned(u, 16) || !aligned(y, 16)) return SSM_ERR_INVALID_ARGUMENT;  // moved in 16-byte rows of 8 channels
     if (!aligned(A, 4) || (D && !aligned(D, 4)) || (h_last && !aligned(h_last, 4))) return SSM_ERR_INVALID_ARGUMENT;
     const size_t need = ssd_workspace(desc);
     if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE_TOO_SMALL;

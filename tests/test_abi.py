@@ -203,7 +203,8 @@ def test_ssd_argument_rules():
     for k in ["u", "delta", "A", "B", "C", "y"]:
         assert call_ssd(ssd_desc(), **{k: 0}) == INVALID, k
     assert call_ssd(ssd_desc(), u=P + 1) == INVALID
-    assert call_ssd(ssd_desc(), u=P + 8) == INVALID                      # u is read in 16-byte rows
+    assert call_ssd(ssd_desc(), u=P + 8) == INVALID                      # u and y move in 16-byte rows
+    assert call_ssd(ssd_desc(), y=P + 8) == INVALID
     d = ssd_desc(B=2, L=100, D=128, N=16)
     need = scan.ssm_ssd_workspace_bytes(d)
     assert need == 2 * (2 * 2 * 2 * 16 * 64 * 4) + 256           # 2 rows x 2 heads x 2 chunks
