@@ -15,11 +15,15 @@ Functions:
                 mathematical essence of the parallel scan".
   scan_bwd() -- gradients of the scan by reverse mode of the same sequential
                 definition (ssm_oracle_bwd.c).
+  scan_mimo() -- the multi-input multi-output form: R inputs and R outputs
+                per token and channel sharing one state (ssm_oracle_mimo.c).
 
 Parity status: every function here is pinned -- scan() and combine() by
 tests/test_oracle_pins.py against closed forms, special cases and invariants,
 scan_bwd() by tests/test_oracle_bwd_pins.py against central finite
-differences of scan(); none is "parity unpinned".
+differences of scan(), scan_mimo() by tests/test_oracle_mimo_pins.py against
+scan() (R = 1 and superposition over the inputs) and a cumulative-sum closed
+form; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -32,6 +36,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssm_oracle.c")
 _SRC_BWD = os.path.join(_HERE, "ssm_oracle_bwd.c")
+_SRC_MIMO = os.path.join(_HERE, "ssm_oracle_mimo.c")
+_SOURCES = (_SRC, _SRC_BWD, _SRC_MIMO)
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 DISC = {"zoh": 0, "euler": 1, "trap": 2}
@@ -43,7 +49,7 @@ def build() -> str:
     """Compile the oracle with gcc.  Returns the path of the shared library."""
     cmd = [
         "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
-        "-ffp-contract=off", "-pthread", "-o", _LIB, _SRC, _SRC_BWD, "-lm",
+        "-ffp-contract=off", "-pthread", "-o", _LIB, *_SOURCES, "-lm",
     ]
     subprocess.run(cmd, check=True)
     return _LIB
@@ -53,7 +59,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(_SRC), os.path.getmtime(_SRC_BWD)):
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(f) for f in _SOURCES):
         build()
     lib = ctypes.CDLL(_LIB)
     dp = ctypes.c_void_p
@@ -62,6 +68,8 @@ def _load():
     lib.oracle_scan_f64.restype = ctypes.c_int
     lib.oracle_scan_bwd_f64.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int] + [dp] * 20
     lib.oracle_scan_bwd_f64.restype = ctypes.c_int
+    lib.oracle_scan_mimo_f64.argtypes = [i64] * 5 + [ctypes.c_int, ctypes.c_int] + [dp] * 13 + [ctypes.c_int]
+    lib.oracle_scan_mimo_f64.restype = ctypes.c_int
     lib.oracle_combine_f64.argtypes = [i64, dp, dp, dp, dp, dp, dp]
     lib.oracle_combine_f64.restype = None
     _lib = lib
@@ -137,6 +145,38 @@ def scan_bwd(u, delta, A, Bm, Cm, Dskip=None, theta=None, lam=None, *, disc: str
     if rc != 0:
         raise ValueError(f"oracle_scan_bwd_f64 returned {rc}")
     return out
+
+
+def scan_mimo(u, delta, A, Bm, Cm, Dskip=None, theta=None, lam=None, *, disc: str, is_complex: bool,
+              h0=None, q0=None, nthreads: int = 0, return_q: bool = False):
+    """The MIMO scan in fp64: one state per (b, d) shared by R inputs and outputs.
+
+    Shapes (row-major): u: (B,L,D,R); delta, lam: (B,L,D); A: (D,N);
+    Bm, Cm: (B,L,N,R) real or (B,L,N,R,2) complex; Dskip: (D,);
+    theta: (B,L,D,N); h0, q0: layout of h_last.  Returns (y (B,L,D,R),
+    h_last (B,D,N[,2])) and q_last (the trapezoid's q_{L-1} = sum_r B u)
+    when return_q is set.
+    """
+    lib = _load()
+    u, delta, A, Bm, Cm = map(_f64, (u, delta, A, Bm, Cm))
+    Dskip, theta, lam, h0, q0 = map(_f64, (Dskip, theta, lam, h0, q0))
+    B, L, D, R = u.shape
+    N = A.shape[1]
+    cw = (2,) if is_complex else ()
+    if Bm.shape != (B, L, N, R) + cw or Cm.shape != Bm.shape:
+        raise ValueError(f"Bm/Cm must be {(B, L, N, R) + cw}, got {Bm.shape} and {Cm.shape}")
+    y = np.empty((B, L, D, R), dtype=np.float64)
+    h_last = np.empty((B, D, N) + cw, dtype=np.float64)
+    q_last = np.empty((B, D, N) + cw, dtype=np.float64)
+    rc = lib.oracle_scan_mimo_f64(
+        B, L, D, N, R, DISC[disc], int(bool(is_complex)),
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(theta), _ptr(lam),
+        _ptr(h0), _ptr(q0), _ptr(y), _ptr(h_last), _ptr(q_last), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_scan_mimo_f64 returned {rc}")
+    if return_q:
+        return y, h_last, q_last
+    return y, h_last
 
 
 def combine(a2, b2, a1, b1):
