@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 2
+#define SSM_SCAN_ABI_VERSION 3
 
 /* Element type of u, delta, B, C, theta, lambda and y.  A, D and h_last are
  * always fp32; all arithmetic is fp32 (bf16 inputs are widened exactly, y is
@@ -287,6 +287,79 @@ size_t ssm_ssd_workspace_bytes(const ssm_ssd_desc_t *desc);
 int ssm_ssd_fwd(const ssm_ssd_desc_t *desc, const void *u, const void *delta, const float *A,
                 const void *B, const void *C, const float *D, void *y, float *h_last, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/*
+ * The multi-input multi-output (MIMO) scan: each (b, d) channel keeps ONE
+ * state h[n] that R inputs feed and R outputs read.  B and C are N x R per
+ * step instead of N-vectors (the ai.tomabc.com Mamba-3 story, MIMO section
+ * and its shape table: R parallel input/output channels share the state,
+ * and the work per step grows from O(N) to O(N R) with the same state
+ * traffic; the metaphor-xennon Mamba-3 notes, section 3.3).  Per b, d, n:
+ *
+ *   q_t[n] = sum_r B_t[n, r] u_t[r]
+ *   h_t[n] = alpha_t[n] h_{t-1}[n] + bterm_t[n]     (alpha and bterm of the
+ *            chosen discretisation exactly as for ssm_scan_fwd, with this
+ *            q_t; the trapezoid's q_{t-1} is the previous step's sum)
+ *   y_t[r] = Re( sum_n C_t[n, r] h_t[n] ) + D[d] u_t[r]
+ *
+ * R = 1 is ssm_scan_fwd_ex with a trailing unit axis on u, B, C and y.
+ */
+typedef struct {
+    int64_t batch;      /* B >= 1 */
+    int64_t seqlen;     /* L >= 1 (1 for ssm_mimo_step) */
+    int64_t dim;        /* D >= 1 */
+    int64_t dstate;     /* N, 1 <= N <= 64 */
+    int64_t rank;       /* R: inputs and outputs per token and channel; 1, 2, 4 or 8 */
+    int64_t chunk;      /* steps per time chunk; 0 lets the library choose (ignored by the step) */
+    int32_t io_dtype;   /* ssm_dtype_t */
+    int32_t disc;       /* ssm_disc_t */
+    int32_t is_complex; /* 0 or 1, as for ssm_scan_desc_t */
+    int32_t reserved;   /* 0 */
+} ssm_mimo_desc_t;
+
+/* Bytes of workspace ssm_mimo_fwd needs: a (decay product, state) pair per
+ * (b, d, n) for every time chunk but the last, (chunks - 1) * B * D * N *
+ * (16 complex, 8 real) bytes; 0 when one chunk covers the sequence or the
+ * descriptor is invalid.  The library's choice of chunk depends only on the
+ * descriptor. */
+size_t ssm_mimo_workspace_bytes(const ssm_mimo_desc_t *desc);
+
+/*
+ *   u       [B][L][D][R]   io dtype   inputs (aligned to min(16, R * element) bytes)
+ *   delta, lambda  [B][L][D] io dtype as for ssm_scan_fwd (lambda: EXP_TRAPEZOIDAL only)
+ *   A [D][N] fp32, D [D] fp32 or NULL as for ssm_scan_fwd; D is shared by a channel's R outputs
+ *   B, C    [B][L][N][R] or [B][L][N][R][2] io dtype
+ *                                     (aligned to min(16, R * 2 * element) bytes if complex,
+ *                                     min(16, R * element) if real)
+ *   theta   [B][L][D][N] io dtype or NULL   as for ssm_scan_fwd
+ *   h0, q0, h_last, q_last            as for ssm_scan_fwd_ex, with q = the sum above
+ *   y       [B][L][D][R]   io dtype   output (written; aligned like u)
+ *   workspace  ssm_mimo_workspace_bytes(desc) bytes, 16-byte aligned (may be
+ *              NULL when that is 0)
+ * Returns an ssm_status_t (SSM_ERR_UNSUPPORTED for R not in {1, 2, 4, 8},
+ * N > 64 or complex ZOH).
+ */
+int ssm_mimo_fwd(const ssm_mimo_desc_t *desc, const void *u, const void *delta, const float *A,
+                 const void *B, const void *C, const float *D, const void *theta, const void *lambda,
+                 const float *h0, const float *q0, void *y, float *h_last, float *q_last, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step of the MIMO recurrence, the state kept by the caller
+ * (the regime of the Mamba-3 story's inference table: R times the work of
+ * the single-input step for the same state traffic).  desc->seqlen must be
+ * 1.  The tensors are those of ssm_mimo_fwd with the time axis dropped:
+ *   u [B][D][R], delta and lambda [B][D], B and C [B][N][R] (or [..][2]),
+ *   theta [B][D][N] or NULL, y [B][D][R];
+ *   u_prev [B][D][R] and B_prev (layout of B): EXP_TRAPEZOIDAL only, the
+ *   previous step's inputs whose sum q_{t-1} the trapezoid's beta multiplies;
+ *   both NULL means no previous step;
+ *   h  [B][D][N] or [B][D][N][2] fp32, read as h_{t-1} and overwritten with h_t.
+ * Alignment as for ssm_mimo_fwd.  Returns an ssm_status_t.
+ */
+int ssm_mimo_step(const ssm_mimo_desc_t *desc, const void *u, const void *delta, const float *A,
+                  const void *B, const void *C, const float *D, const void *theta, const void *lambda,
+                  const void *u_prev, const void *B_prev, float *h, void *y, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *ssm_scan_status_string(int status);

@@ -7,8 +7,8 @@ be used without loading the HIP library.
 """
 
 __all__ = ["ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_step", "ssm_scan_bwd", "ssm_scan_workspace_bytes",
-           "ssm_scan_bwd_workspace_bytes", "ssm_ssd_fwd", "ssm_ssd_workspace_bytes", "ssm_scan_status_string",
-           "ssm_scan_abi_version"]
+           "ssm_scan_bwd_workspace_bytes", "ssm_ssd_fwd", "ssm_ssd_workspace_bytes", "ssm_mimo_fwd", "ssm_mimo_step",
+           "ssm_mimo_workspace_bytes", "ssm_scan_status_string", "ssm_scan_abi_version"]
 
 
 def __getattr__(name):

@@ -18,32 +18,55 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libssmscan.so")
-SOURCES = [os.path.join(CSRC, "ssm_scan.hip")]
+SOURCES = [os.path.join(CSRC, "ssm_scan.hip"), os.path.join(CSRC, "mimo.hip")]
 HEADERS = [os.path.join(ROOT, "include", "ssm_scan.h")] + [
     os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".h")]
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 
 
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+    "-Wno-unused-command-line-argument",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+]
+
+
 def hipcc_cmd(out: str = LIB, extra=()):
-    return [
-        "hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
-        "-Wno-unused-command-line-argument",
-        "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-        *extra, "-o", out, *SOURCES,
-    ]
+    """One hipcc line that compiles and links every source (for inspection)."""
+    return ["hipcc", *FLAGS, "-shared", *extra, "-o", out, *SOURCES]
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = hipcc_cmd(tmp)
-    if verbose:
-        print(" ".join(cmd))
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libssmscan.so")
+    """Compile the sources to objects in parallel, then link the library."""
+    import tempfile
+
+    with tempfile.TemporaryDirectory(prefix="ssmscan_build_") as tmpdir:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            cmd = ["hipcc", *FLAGS, "-c", "-o", obj, src]
+            if verbose:
+                print(" ".join(cmd))
+            procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True), src))
+            objs.append(obj)
+        failed = False
+        for proc, src in procs:
+            out, _ = proc.communicate()
+            if proc.returncode != 0:
+                sys.stderr.write(out)
+                failed = True
+        if failed:
+            raise RuntimeError("hipcc failed building libssmscan.so")
+        tmp = LIB + ".tmp"
+        cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd))
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("hipcc failed linking libssmscan.so")
     os.replace(tmp, LIB)
     return LIB
 

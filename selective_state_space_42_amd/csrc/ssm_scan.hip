@@ -16,6 +16,7 @@
 #include "kernel_step.h"
 #include "kernel_backward.h"
 #include "kernel_ssd.h"
+#include "mimo_launch.h"
 
 namespace {
 
@@ -187,6 +188,81 @@ int check_inputs(const ssm_scan_desc_t* desc, const void* u, const void* delta, 
     if (!desc->is_complex && theta) return SSM_ERR_INVALID_ARGUMENT;
     const size_t es = desc->io_dtype == SSM_DTYPE_F32 ? 4 : 2;
     const void* io_ptrs[] = {u, delta, B, C, theta, lambda, y};
+    for (const void* q : io_ptrs)
+        if (q && !aligned(q, es)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!aligned(A, 4) || (D && !aligned(D, 4))) return SSM_ERR_INVALID_ARGUMENT;
+    return SSM_OK;
+}
+
+int check_mimo_desc(const ssm_mimo_desc_t* d) {
+    if (!d) return SSM_ERR_INVALID_ARGUMENT;
+    if (d->batch < 1 || d->seqlen < 1 || d->dim < 1 || d->dstate < 1 || d->rank < 1 || d->chunk < 0 ||
+        d->reserved != 0)
+        return SSM_ERR_INVALID_ARGUMENT;
+    if (d->io_dtype != SSM_DTYPE_F32 && d->io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
+    if (d->disc < SSM_DISC_ZOH || d->disc > SSM_DISC_EXP_TRAPEZOIDAL) return SSM_ERR_UNSUPPORTED;
+    if (d->is_complex != 0 && d->is_complex != 1) return SSM_ERR_UNSUPPORTED;
+    if (d->is_complex && d->disc == SSM_DISC_ZOH) return SSM_ERR_UNSUPPORTED;
+    if (d->dstate > 64) return SSM_ERR_UNSUPPORTED;
+    if (d->rank != 1 && d->rank != 2 && d->rank != 4 && d->rank != 8) return SSM_ERR_UNSUPPORTED;
+    // byte offsets of [B][L][D][max(2N, R)] and [B][L][N][R][2] fp32 words fit an int64
+    const int64_t wide = 2 * d->dstate > d->rank ? 2 * d->dstate : d->rank;
+    int64_t r;
+    if (__builtin_mul_overflow(d->batch, d->seqlen, &r) || __builtin_mul_overflow(r, d->dim, &r) ||
+        __builtin_mul_overflow(r, wide, &r) || __builtin_mul_overflow(r, int64_t(4), &r))
+        return SSM_ERR_INVALID_ARGUMENT;
+    if (__builtin_mul_overflow(d->batch, d->seqlen, &r) || __builtin_mul_overflow(r, d->dstate, &r) ||
+        __builtin_mul_overflow(r, d->rank, &r) || __builtin_mul_overflow(r, int64_t(8), &r))
+        return SSM_ERR_INVALID_ARGUMENT;
+    return SSM_OK;
+}
+
+// lanes per channel of the MIMO kernels: one per state, at least one per output
+int mimo_lpc(const ssm_mimo_desc_t* d) {
+    const int l = next_pow2(d->dstate);
+    return l < d->rank ? static_cast<int>(d->rank) : l;
+}
+
+// Time chunks of the MIMO scan.  Unless the caller fixes the chunk length,
+// the sequence is cut into as many chunks (of at least 64 steps) as it takes
+// to give the GPU about 2^18 lanes, four waves per SIMD on 256 compute units;
+// a problem wide enough on its own runs as one chunk.
+void mimo_chunking(const ssm_mimo_desc_t* d, int64_t* chunk, int64_t* nchunks) {
+    int64_t c = d->chunk;
+    if (c == 0) {
+        constexpr int64_t kTargetLanes = int64_t(1) << 18;
+        const int64_t lanes = d->batch * d->dim * mimo_lpc(d);
+        int64_t want = (kTargetLanes + lanes - 1) / lanes;
+        const int64_t most = (d->seqlen + 63) / 64;
+        if (want > most) want = most;
+        if (want < 1) want = 1;
+        c = (d->seqlen + want - 1) / want;
+    }
+    if (c > d->seqlen) c = d->seqlen;
+    *chunk = c;
+    *nchunks = (d->seqlen + c - 1) / c;
+}
+
+size_t mimo_workspace(const ssm_mimo_desc_t* d) {
+    int64_t chunk, n;
+    mimo_chunking(d, &chunk, &n);
+    return static_cast<size_t>((n - 1) * d->batch * d->dim * d->dstate * (d->is_complex ? 16 : 8));
+}
+
+// Pointer checks of the MIMO scan and step: required inputs, lambda exactly
+// for the trapezoid, theta only for a complex state, and the alignment of
+// the runs the kernels read (u and y rows of R elements, B and C rows of R
+// (complex) elements, each read with loads of up to 16 bytes).
+int check_mimo_inputs(const ssm_mimo_desc_t* d, const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* theta, const void* lambda, const void* y) {
+    const bool trap = d->disc == SSM_DISC_EXP_TRAPEZOIDAL;
+    if (!u || !delta || !A || !B || !C || !y) return SSM_ERR_INVALID_ARGUMENT;
+    if (trap != (lambda != nullptr)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!d->is_complex && theta) return SSM_ERR_INVALID_ARGUMENT;
+    const size_t es = d->io_dtype == SSM_DTYPE_F32 ? 4 : 2, cw = d->is_complex ? 2 : 1;
+    const size_t ua = d->rank * es < 16 ? d->rank * es : 16, ba = d->rank * cw * es < 16 ? d->rank * cw * es : 16;
+    if (!aligned(u, ua) || !aligned(y, ua) || !aligned(B, ba) || !aligned(C, ba)) return SSM_ERR_INVALID_ARGUMENT;
+    const void* io_ptrs[] = {delta, theta, lambda};
     for (const void* q : io_ptrs)
         if (q && !aligned(q, es)) return SSM_ERR_INVALID_ARGUMENT;
     if (!aligned(A, 4) || (D && !aligned(D, 4))) return SSM_ERR_INVALID_ARGUMENT;
@@ -391,6 +467,74 @@ int ssm_ssd_fwd(const ssm_ssd_desc_t* desc, const void* u, const void* delta, co
     else
         hipLaunchKernelGGL((ssm::ssd_out_kernel<uint16_t, ssm::ssd::kMaxN>), grid, dim3(256), 0, s, p);
     return hip_status(hipGetLastError());
+}
+
+size_t ssm_mimo_workspace_bytes(const ssm_mimo_desc_t* desc) {
+    if (check_mimo_desc(desc) != SSM_OK) return 0;
+    return mimo_workspace(desc);
+}
+
+int ssm_mimo_fwd(const ssm_mimo_desc_t* desc, const void* u, const void* delta, const float* A, const void* B,
+                 const void* C, const float* D, const void* theta, const void* lambda, const float* h0,
+                 const float* q0, void* y, float* h_last, float* q_last, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    int st = check_mimo_desc(desc);
+    if (st != SSM_OK) return st;
+    st = check_mimo_inputs(desc, u, delta, A, B, C, D, theta, lambda, y);
+    if (st != SSM_OK) return st;
+    const bool trap = desc->disc == SSM_DISC_EXP_TRAPEZOIDAL;
+    if (!trap && (q0 || q_last)) return SSM_ERR_INVALID_ARGUMENT;
+    const size_t ss = desc->is_complex ? 8 : 4;
+    const void* st_ptrs[] = {h0, q0, h_last, q_last};
+    for (const void* q : st_ptrs)
+        if (q && !aligned(q, ss)) return SSM_ERR_INVALID_ARGUMENT;
+    int64_t chunk, nchunks;
+    mimo_chunking(desc, &chunk, &nchunks);
+    const size_t need = mimo_workspace(desc);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned(workspace, 16)) return SSM_ERR_INVALID_ARGUMENT;
+    }
+    const int lpc = mimo_lpc(desc);
+    const int64_t BD = desc->batch * desc->dim;
+    const int64_t blocks = ((BD * lpc + 63) / 64 * nchunks + 3) / 4;
+    if (nchunks > INT32_MAX || blocks > INT32_MAX || (BD * desc->dstate + 255) / 256 > INT32_MAX)
+        return SSM_ERR_UNSUPPORTED;
+
+    ssm::MimoParams p{};
+    p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.theta = theta; p.lambda = lambda;
+    p.h0 = h0; p.q0 = q0; p.y = y; p.h_last = h_last; p.q_last = q_last;
+    p.carry = static_cast<float*>(need > 0 ? workspace : nullptr);
+    p.batch = desc->batch; p.seqlen = desc->seqlen; p.dim = desc->dim; p.dstate = desc->dstate;
+    p.chunk = chunk; p.nchunks = static_cast<int32_t>(nchunks); p.lpc = lpc;
+    return hip_status(ssm::launch_mimo_scan(p, desc->io_dtype == SSM_DTYPE_BF16, desc->disc, desc->is_complex != 0,
+                                            static_cast<int>(desc->rank), static_cast<hipStream_t>(stream)));
+}
+
+int ssm_mimo_step(const ssm_mimo_desc_t* desc, const void* u, const void* delta, const float* A, const void* B,
+                  const void* C, const float* D, const void* theta, const void* lambda, const void* u_prev,
+                  const void* B_prev, float* h, void* y, void* stream) {
+    int st = check_mimo_desc(desc);
+    if (st != SSM_OK) return st;
+    if (desc->seqlen != 1) return SSM_ERR_INVALID_ARGUMENT;
+    st = check_mimo_inputs(desc, u, delta, A, B, C, D, theta, lambda, y);
+    if (st != SSM_OK) return st;
+    const bool trap = desc->disc == SSM_DISC_EXP_TRAPEZOIDAL;
+    if (!h || !aligned(h, desc->is_complex ? 8 : 4)) return SSM_ERR_INVALID_ARGUMENT;
+    if ((u_prev != nullptr) != (B_prev != nullptr) || (!trap && u_prev)) return SSM_ERR_INVALID_ARGUMENT;
+    const size_t es = desc->io_dtype == SSM_DTYPE_F32 ? 4 : 2, cw = desc->is_complex ? 2 : 1;
+    const size_t ua = desc->rank * es < 16 ? desc->rank * es : 16;
+    const size_t ba = desc->rank * cw * es < 16 ? desc->rank * cw * es : 16;
+    if ((u_prev && !aligned(u_prev, ua)) || (B_prev && !aligned(B_prev, ba))) return SSM_ERR_INVALID_ARGUMENT;
+    const int lpc = mimo_lpc(desc);
+    if (((desc->batch * desc->dim * lpc + 63) / 64 + 3) / 4 > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+
+    ssm::MimoStepParams p{};
+    p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.theta = theta; p.lambda = lambda;
+    p.u_prev = u_prev; p.B_prev = B_prev; p.h = h; p.y = y;
+    p.batch = desc->batch; p.dim = desc->dim; p.dstate = desc->dstate; p.lpc = lpc;
+    return hip_status(ssm::launch_mimo_step(p, desc->io_dtype == SSM_DTYPE_BF16, desc->disc, desc->is_complex != 0,
+                                            static_cast<int>(desc->rank), static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

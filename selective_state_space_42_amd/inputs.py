@@ -45,6 +45,7 @@ class Workload:
     a_kind: str       # "neg_index": A[d,n] = -(n+1);  "neg_exp_uniform": A = -exp(U(-3,0))
     bc_var: float     # variance of B, C (real) or of each of re/im (complex)
     theta_scale: float = 0.1  # theta = theta_scale * U(-pi, pi)
+    rank: int = 0     # MIMO workloads: R inputs and outputs per token and channel (0: single-input layout)
 
     @property
     def shape(self):
@@ -251,3 +252,58 @@ def ssd_as_scan(inputs: dict, w: SsdWorkload, d_index=None) -> dict:
         A=host(inputs["A"].index_select(0, heads)[:, None].expand(len(idx), w.dstate)),
         Bm=host(inputs["Bm"]), Cm=host(inputs["Cm"]),
         Dskip=host(inputs["Dskip"].index_select(0, sel)), theta=None, lam=None)
+
+
+# ---- the multi-input multi-output (MIMO) setting: R inputs and outputs per
+# token and channel sharing one state; u, y (B, L, D, R) and B, C (B, L, N, R)
+# or (B, L, N, R, 2).  R = 4 is the rank the Mamba-3 story's inference table
+# quotes.  Fields are drawn as for the complex exp-trapezoidal bf16 workload,
+# in the same order, each with its R axis.
+MIMO_WORKLOADS = {
+    "mimo_complex_trap_bf16_b4_d2560_l8192_n16_r4": Workload(
+        "mimo_complex_trap_bf16_b4_d2560_l8192_n16_r4", 4, 2560, 8192, 16, "trap", True, "bf16", -3.0, 0.5,
+        "neg_exp_uniform", 0.5, rank=4),
+}
+# decode steps: seqlen = 2 holds the previous step and the current one
+MIMO_DECODE_WORKLOADS = {
+    "mimo_decode_complex_trap_bf16_b256_d2560_n16_r4": Workload(
+        "mimo_decode_complex_trap_bf16_b256_d2560_n16_r4", 256, 2560, 2, 16, "trap", True, "bf16", -3.0, 0.5,
+        "neg_exp_uniform", 0.5, rank=4),
+}
+
+
+def make_mimo_inputs(w: Workload, seed: Optional[int] = None, device="cpu") -> dict:
+    """One seeded instance of a MIMO workload: u (B,L,D,R), delta, lam (B,L,D),
+    A (D,N), Bm, Cm (B,L,N,R[,2]), Dskip (D,), theta (B,L,D,N)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(SEED_BASE + 200 if seed is None else seed)
+    io = torch_dtype(w.io_dtype)
+    B, L, D, N, R = w.batch, w.seqlen, w.dim, w.dstate, w.rank
+    kw = dict(device=device)
+    u = _fill(torch.empty((B, L, D, R), dtype=io, **kw), gen, "normal", 0.0, 1.0)
+    delta = _fill(torch.empty((B, L, D), dtype=io, **kw), gen, "normal", w.delta_mu, w.delta_sigma,
+                  post=torch.nn.functional.softplus)
+    if w.a_kind == "neg_index":
+        A = -(torch.arange(1, N + 1, dtype=torch.float32, device=device)).repeat(D, 1).contiguous()
+    else:
+        A = _fill(torch.empty((D, N), dtype=torch.float32, **kw), gen, "uniform", -3.0, 0.0,
+                  post=lambda v: -torch.exp(v))
+    std = math.sqrt(w.bc_var)
+    parts = []
+    for _ in range(4 if w.is_complex else 2):  # B re, (B im,) C re, (C im)
+        parts.append(_fill(torch.empty((B, L, N, R), dtype=io, **kw), gen, "normal", 0.0, std))
+    if w.is_complex:
+        Bm = torch.stack(parts[:2], dim=-1).contiguous()
+        Cm = torch.stack(parts[2:], dim=-1).contiguous()
+    else:
+        Bm, Cm = parts
+    del parts
+    Dskip = _fill(torch.empty((D,), dtype=torch.float32, **kw), gen, "normal", 0.0, 1.0)
+    theta = None
+    if w.is_complex:
+        theta = _fill(torch.empty((B, L, D, N), dtype=io, **kw), gen, "uniform",
+                      -math.pi * w.theta_scale, math.pi * w.theta_scale)
+    lam = None
+    if w.disc == "trap":
+        lam = _fill(torch.empty((B, L, D), dtype=io, **kw), gen, "normal", 0.0, 1.0, post=torch.sigmoid)
+    return dict(u=u, delta=delta, A=A, Bm=Bm, Cm=Cm, Dskip=Dskip, theta=theta, lam=lam)

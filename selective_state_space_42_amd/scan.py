@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libssmscan.so")
 SSM_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 SSM_DISC = {"zoh": 0, "euler": 1, "trap": 2}
 SSM_ALGO = {"auto": 0, "sequential": 1, "chunked": 2}
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class ScanDesc(ctypes.Structure):
@@ -33,6 +33,15 @@ class SsdDesc(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
         ("dstate", ctypes.c_int64), ("headdim", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class MimoDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("rank", ctypes.c_int64), ("chunk", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32), ("disc", ctypes.c_int32), ("is_complex", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
 
@@ -71,6 +80,12 @@ def _lib():
     lib.ssm_ssd_fwd.restype = ctypes.c_int
     lib.ssm_ssd_workspace_bytes.argtypes = [ctypes.POINTER(SsdDesc)]
     lib.ssm_ssd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssm_mimo_fwd.argtypes = [ctypes.POINTER(MimoDesc)] + [vp] * 14 + [ctypes.c_size_t, vp]
+    lib.ssm_mimo_fwd.restype = ctypes.c_int
+    lib.ssm_mimo_step.argtypes = [ctypes.POINTER(MimoDesc)] + [vp] * 13
+    lib.ssm_mimo_step.restype = ctypes.c_int
+    lib.ssm_mimo_workspace_bytes.argtypes = [ctypes.POINTER(MimoDesc)]
+    lib.ssm_mimo_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
     lib.ssm_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_scan_status_string.argtypes = [ctypes.c_int]
@@ -266,3 +281,70 @@ def ssm_ssd_fwd(u, delta, A, B, C, D=None, *, headdim: int = 64, y=None, h_last=
     if st != 0:
         raise ScanError(st, "ssm_ssd_fwd")
     return y, h_last
+
+
+def make_mimo_desc(batch, seqlen, dim, dstate, rank, io_dtype, disc, is_complex, chunk: int = 0) -> MimoDesc:
+    return MimoDesc(int(batch), int(seqlen), int(dim), int(dstate), int(rank), int(chunk),
+                    int(SSM_DTYPE.get(io_dtype, io_dtype)), int(SSM_DISC.get(disc, disc)), int(bool(is_complex)), 0)
+
+
+def ssm_mimo_workspace_bytes(desc: MimoDesc) -> int:
+    return int(_lib().ssm_mimo_workspace_bytes(ctypes.byref(desc)))
+
+
+def ssm_mimo_fwd(u, delta, A, B, C, D=None, theta=None, lam=None, h0=None, q0=None, *, disc: str, y=None,
+                 h_last=None, q_last=None, want_h_last: bool = True, want_q_last: bool = False, workspace=None,
+                 chunk: int = 0, stream=None):
+    """The MIMO scan on torch device tensors; returns (y, h_last, q_last).
+
+    u (B,L,D,R); delta, lam (B,L,D); A (D,N) fp32; B, C (B,L,N,R) real or
+    (B,L,N,R,2) complex; D (D,) fp32; theta (B,L,D,N); h0, q0 and the
+    returned states (B,D,N[,2]) fp32.  chunk fixes the time-chunk length
+    (0: the library's choice).
+    """
+    Bsz, L, Dm, R = u.shape
+    N = A.shape[1]
+    is_complex = B.dim() == 5
+    desc = make_mimo_desc(Bsz, L, Dm, N, R, u.dtype, disc, is_complex, chunk)
+    shape = (Bsz, Dm, N, 2) if is_complex else (Bsz, Dm, N)
+    if y is None:
+        y = torch.empty_like(u)
+    if h_last is None and want_h_last:
+        h_last = torch.empty(shape, dtype=torch.float32, device=u.device)
+    if q_last is None and want_q_last:
+        q_last = torch.empty(shape, dtype=torch.float32, device=u.device)
+    need = ssm_mimo_workspace_bytes(desc)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream if u.is_cuda else 0
+    st = _lib().ssm_mimo_fwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                             _ptr(theta), _ptr(lam), _ptr(h0), _ptr(q0), _ptr(y), _ptr(h_last), _ptr(q_last),
+                             _ptr(workspace), ws_bytes, ctypes.c_void_p(stream))
+    if st != 0:
+        raise ScanError(st, "ssm_mimo_fwd")
+    return y, h_last, q_last
+
+
+def ssm_mimo_step(u, delta, A, B, C, D=None, theta=None, lam=None, *, h, u_prev=None, B_prev=None, disc: str,
+                  y=None, stream=None):
+    """One MIMO decode step, updating h in place; returns y.
+
+    u, u_prev (B,D,R); delta, lam (B,D); A (D,N) fp32; B, C, B_prev (B,N,R)
+    real or (B,N,R,2) complex; D (D,) fp32; theta (B,D,N); h (B,D,N[,2]) fp32.
+    """
+    Bsz, Dm, R = u.shape
+    N = A.shape[1]
+    is_complex = B.dim() == 4
+    desc = make_mimo_desc(Bsz, 1, Dm, N, R, u.dtype, disc, is_complex)
+    if y is None:
+        y = torch.empty_like(u)
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream if u.is_cuda else 0
+    st = _lib().ssm_mimo_step(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                              _ptr(theta), _ptr(lam), _ptr(u_prev), _ptr(B_prev), _ptr(h), _ptr(y),
+                              ctypes.c_void_p(stream))
+    if st != 0:
+        raise ScanError(st, "ssm_mimo_step")
+    return y

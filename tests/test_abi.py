@@ -21,21 +21,22 @@ P = 0x10000  # an aligned fake device address (never dereferenced)
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(ssm_(?:scan|ssd)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ssm_(?:scan|ssd|mimo)_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     lib = scan._lib()
     names = declared_functions()
     assert {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_step", "ssm_scan_bwd", "ssm_scan_workspace_bytes",
-            "ssm_scan_bwd_workspace_bytes", "ssm_ssd_fwd", "ssm_ssd_workspace_bytes", "ssm_scan_status_string",
-            "ssm_scan_abi_version", "ssm_scan_last_hip_error"} <= set(names)
+            "ssm_scan_bwd_workspace_bytes", "ssm_ssd_fwd", "ssm_ssd_workspace_bytes", "ssm_mimo_fwd",
+            "ssm_mimo_step", "ssm_mimo_workspace_bytes", "ssm_scan_status_string", "ssm_scan_abi_version",
+            "ssm_scan_last_hip_error"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_version_and_status_strings():
-    assert scan.ssm_scan_abi_version() == 2
+    assert scan.ssm_scan_abi_version() == 3
     for code, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported configuration"),
                        (3, "workspace too small"), (4, "HIP runtime error"), (99, "unknown status")]:
         assert scan.ssm_scan_status_string(code) == text
@@ -211,3 +212,73 @@ def test_ssd_argument_rules():
     assert call_ssd(d, ws=0) == WS_SMALL
     assert call_ssd(d, ws_bytes=need - 1) == WS_SMALL
     assert call_ssd(d, ws=P + 64, ws_bytes=need) == INVALID
+
+
+def mimo_desc(B=1, L=8, D=4, N=4, R=4, dtype="bf16", disc="trap", cplx=True, chunk=0):
+    return scan.make_mimo_desc(B, L, D, N, R, {"f32": 0, "bf16": 1}[dtype], disc, cplx, chunk)
+
+
+def call_mimo(desc, u=P, delta=P, A=P, B=P, C=P, D=0, theta=0, lam=P, h0=0, q0=0, y=P, h=0, q=0, ws=0,
+              ws_bytes=0):
+    lib = scan._lib()
+    dp = None if desc is None else ctypes.byref(desc)
+    args = [u, delta, A, B, C, D, theta, lam, h0, q0, y, h, q, ws]
+    return lib.ssm_mimo_fwd(dp, *[ctypes.c_void_p(a) if a else None for a in args], ws_bytes, None)
+
+
+def call_mimo_step(desc, u=P, delta=P, A=P, B=P, C=P, D=0, theta=0, lam=P, u_prev=0, B_prev=0, h=P, y=P):
+    lib = scan._lib()
+    args = [u, delta, A, B, C, D, theta, lam, u_prev, B_prev, h, y]
+    return lib.ssm_mimo_step(ctypes.byref(desc), *[ctypes.c_void_p(a) if a else None for a in args], None)
+
+
+def test_mimo_descriptor_rules():
+    assert call_mimo(None) == INVALID
+    for kw in [dict(B=0), dict(L=0), dict(D=0), dict(N=0), dict(R=0), dict(chunk=-1)]:
+        assert call_mimo(mimo_desc(**kw)) == INVALID, kw
+    for kw in [dict(R=3), dict(R=16), dict(N=65)]:
+        assert call_mimo(mimo_desc(**kw)) == UNSUPPORTED, kw
+    assert call_mimo(mimo_desc(disc="zoh", cplx=True), lam=0) == UNSUPPORTED
+    d = mimo_desc()
+    d.reserved = 1
+    assert call_mimo(d) == INVALID
+    assert call_mimo(mimo_desc(B=1 << 20, L=1 << 20, D=1 << 20, N=16)) == INVALID
+    assert scan.ssm_mimo_workspace_bytes(mimo_desc(R=3)) == 0
+
+
+def test_mimo_pointer_rules():
+    assert call_mimo(mimo_desc(), u=0) == INVALID
+    assert call_mimo(mimo_desc(), lam=0) == INVALID                       # the trapezoid needs lambda
+    assert call_mimo(mimo_desc(disc="euler"), lam=P) == INVALID           # and only it takes one
+    assert call_mimo(mimo_desc(disc="euler", cplx=False), lam=0, theta=P) == INVALID
+    assert call_mimo(mimo_desc(disc="euler"), lam=0, q0=P) == INVALID     # q0, q_last: trapezoid only
+    # u and y move in runs of R elements (here 8 bytes), B and C in runs of R complex elements (16 bytes)
+    assert call_mimo(mimo_desc(), u=P + 4) == INVALID
+    assert call_mimo(mimo_desc(), y=P + 4) == INVALID
+    assert call_mimo(mimo_desc(), B=P + 8) == INVALID
+    assert call_mimo(mimo_desc(), C=P + 8) == INVALID
+    assert call_mimo(mimo_desc(), h0=P + 4) == INVALID                    # complex state: 8-byte elements
+
+
+def test_mimo_workspace_follows_the_chunking():
+    # one chunk (a wide problem, or a fixed chunk covering L): no workspace
+    assert scan.ssm_mimo_workspace_bytes(mimo_desc(B=64, D=4096, L=1000, N=16)) == 0
+    assert scan.ssm_mimo_workspace_bytes(mimo_desc(L=100, chunk=100)) == 0
+    # a fixed chunk of 16 steps over 100: 7 chunks, 6 carried (P, h) pairs per (b, d, n)
+    assert scan.ssm_mimo_workspace_bytes(mimo_desc(B=2, D=3, N=5, L=100, chunk=16)) == 6 * 2 * 3 * 5 * 16
+    assert scan.ssm_mimo_workspace_bytes(mimo_desc(B=2, D=3, N=5, L=100, chunk=16, cplx=False)) == 6 * 2 * 3 * 5 * 8
+    # a narrow, long problem is cut into chunks of at least 64 steps
+    need = scan.ssm_mimo_workspace_bytes(mimo_desc(B=1, D=8, N=16, L=1 << 14))
+    assert need == (256 - 1) * 8 * 16 * 16
+    d = mimo_desc(L=100, chunk=16)
+    assert call_mimo(d, ws=P, ws_bytes=scan.ssm_mimo_workspace_bytes(d) - 1) == WS_SMALL
+    assert call_mimo(d, ws=0, ws_bytes=0) == WS_SMALL
+
+
+def test_mimo_step_rules():
+    assert call_mimo_step(mimo_desc(L=2)) == INVALID                      # one step
+    assert call_mimo_step(mimo_desc(L=1), h=0) == INVALID
+    assert call_mimo_step(mimo_desc(L=1), u_prev=P) == INVALID            # u_prev and B_prev together
+    assert call_mimo_step(mimo_desc(L=1, disc="euler"), lam=0, u_prev=P, B_prev=P) == INVALID
+    assert call_mimo_step(mimo_desc(L=1), u_prev=P + 4, B_prev=P) == INVALID
+    assert call_mimo_step(mimo_desc(L=1, R=3)) == UNSUPPORTED
