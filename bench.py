@@ -96,6 +96,31 @@ def ssd_algorithmic_bytes(w) -> int:
     return e * B * L * D * 2 + e * B * L * H + 2 * e * B * L * N + 4 * H + 4 * D + 4 * B * D * N
 
 
+def mimo_algorithmic_bytes(w) -> int:
+    """The MIMO scan: u and y (R per token and channel), delta, lambda, theta,
+    B and C (N x R per step), A, D read or written once, h_last written once."""
+    e = 4 if w.io_dtype == "f32" else 2
+    B, L, D, N, R = w.batch, w.seqlen, w.dim, w.dstate, w.rank
+    trap = 1 if w.disc == "trap" else 0
+    cplx = 1 if w.is_complex else 0
+    return (e * B * L * D * (2 * R + 1 + trap) + e * B * L * D * N * cplx + 2 * e * B * L * N * R * (1 + cplx)
+            + 4 * D * N + 4 * D + 4 * B * D * N * (1 + cplx))
+
+
+def mimo_decode_algorithmic_bytes(w) -> int:
+    """One MIMO decode step: the step's inputs and the previous step's u and B
+    read once, the state read and written once, the R outputs written once."""
+    e = 4 if w.io_dtype == "f32" else 2
+    B, D, N, R = w.batch, w.dim, w.dstate, w.rank
+    trap = 1 if w.disc == "trap" else 0
+    cplx = 1 if w.is_complex else 0
+    return (e * B * D * (2 * R + 1 + trap * (1 + R))     # u, y, delta, (lambda, u_prev)
+            + e * B * D * N * cplx                        # theta
+            + e * B * N * R * (1 + cplx) * (2 + trap)     # B, C, (B_prev)
+            + 4 * D * N + 4 * D                           # A, D
+            + 2 * 4 * B * D * N * (1 + cplx))             # h read and written
+
+
 def kernel_source_hash() -> str:
     csrc = os.path.join(ROOT, "selective_state_space_42_amd", "csrc")
     h = hashlib.sha256()
@@ -405,6 +430,157 @@ def bench_ssd(args, w, torch, dev):
     print(json.dumps(out), flush=True)
 
 
+def _timed(torch, stream, step, steps: int, warmup: int) -> float:
+    """ms per call of step() over `steps` calls after `warmup`, by events on `stream`."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def bench_mimo(args, w, torch, dev):
+    import numpy as np
+
+    from selective_state_space_42_amd.inputs import channel_sample, make_mimo_inputs
+    from selective_state_space_42_amd.scan import make_mimo_desc, ssm_mimo_fwd, ssm_mimo_workspace_bytes
+
+    log(f"generating {w.name} on {torch.cuda.get_device_name(dev)}")
+    inputs = make_mimo_inputs(w, device=dev)
+    y = torch.empty_like(inputs["u"])
+    h_last = torch.empty((w.batch, w.dim, w.dstate) + ((2,) if w.is_complex else ()), dtype=torch.float32,
+                         device=dev)
+    desc = make_mimo_desc(w.batch, w.seqlen, w.dim, w.dstate, w.rank, inputs["u"].dtype, w.disc, w.is_complex)
+    ws_bytes = ssm_mimo_workspace_bytes(desc)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ssm_mimo_fwd(inputs["u"], inputs["delta"], inputs["A"], inputs["Bm"], inputs["Cm"], inputs["Dskip"],
+                     inputs["theta"], inputs["lam"], disc=w.disc, y=y, h_last=h_last, workspace=ws,
+                     stream=stream.cuda_stream)
+
+    ms = _timed(torch, stream, step, args.steps, args.warmup)
+    log(f"timed {args.steps} MIMO scans: {ms:.3f} ms each")
+    alg = mimo_algorithmic_bytes(w)
+    achieved = alg / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": w.batch * w.seqlen * w.dim / (ms * 1e-3), "unit": UNIT, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen, "dstate": w.dstate,
+                   "rank": w.rank, "disc": w.disc, "complex": w.is_complex, "io_dtype": w.io_dtype,
+                   "algo": "mimo", "workspace_bytes": ws_bytes},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profile(w.name, "mimo"),
+                     "algorithmic_bytes_per_launch": alg},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        log("timing the fp64 MIMO oracle on a channel sample")
+        threads = max(1, min(os.cpu_count() or 1, 64))
+        order = np.random.default_rng(0).permutation(w.dim).tolist()
+        spent, tc, used, err, groups = 0.0, 0, 0, 0.0, 0
+        for g0 in range(0, w.dim, threads):
+            idx = sorted(order[g0:g0 + threads])
+            x = channel_sample(inputs, idx)
+            t0 = time.perf_counter()
+            y_ref, _ = oracle.scan_mimo(x["u"], x["delta"], x["A"], x["Bm"], x["Cm"], x["Dskip"], x["theta"],
+                                        x["lam"], disc=w.disc, is_complex=w.is_complex, nthreads=len(idx))
+            spent += time.perf_counter() - t0
+            tc += w.batch * w.seqlen * len(idx)
+            used = max(used, len(idx))
+            groups += 1
+            yg = y.index_select(2, torch.as_tensor(idx, device=dev)).float().cpu().double().numpy()
+            err = max(err, float(np.max(np.abs(yg - y_ref)) / np.max(np.abs(y_ref))))
+            if spent >= args.cpu_seconds:
+                break
+        out["cpu_baseline"] = {
+            "value": tc / spent, "unit": UNIT, "cores": used, "kind": "oracle",
+            "sample": f"{tc // (w.batch * w.seqlen)} of {w.dim} channels (random, seed 0) in {groups} group(s), "
+                      f"every batch row and step, R={w.rank}: {tc} tokens*channels in {spent:.1f} s of fp64 C "
+                      f"oracle time on {used} pthreads",
+            "parity_err_y_on_sample": err}
+    print(json.dumps(out), flush=True)
+
+
+def bench_mimo_decode(args, w, torch, dev):
+    import numpy as np
+
+    from selective_state_space_42_amd.inputs import channel_sample, make_mimo_inputs
+    from selective_state_space_42_amd.scan import ssm_mimo_step
+
+    log(f"generating {w.name} on {torch.cuda.get_device_name(dev)}")
+    inputs = make_mimo_inputs(w, device=dev)
+    per_step = ("u", "delta", "lam", "theta", "Bm", "Cm")
+    prev = {k: inputs[k][:, 0].contiguous() for k in ("u", "Bm")}
+    cur = {k: (v[:, 1].contiguous() if k in per_step and v is not None else v) for k, v in inputs.items()}
+    g = torch.Generator(device=dev).manual_seed(1)
+    h = torch.randn((w.batch, w.dim, w.dstate) + ((2,) if w.is_complex else ()), generator=g, device=dev)
+    h_start = h.clone()
+    y = torch.empty_like(cur["u"])
+    stream = torch.cuda.current_stream(dev)
+    trap = w.disc == "trap"
+
+    def step():
+        ssm_mimo_step(cur["u"], cur["delta"], cur["A"], cur["Bm"], cur["Cm"], cur["Dskip"], cur["theta"],
+                      cur["lam"], h=h, u_prev=prev["u"] if trap else None, B_prev=prev["Bm"] if trap else None,
+                      disc=w.disc, y=y, stream=stream.cuda_stream)
+
+    ms = _timed(torch, stream, step, args.steps, args.warmup)
+    log(f"timed {args.steps} MIMO decode steps: {ms * 1e3:.2f} us/step")
+    alg = mimo_decode_algorithmic_bytes(w)
+    achieved = alg / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": w.batch * w.dim / (ms * 1e-3), "unit": UNIT, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": 1, "dstate": w.dstate,
+                   "rank": w.rank, "disc": w.disc, "complex": w.is_complex, "io_dtype": w.io_dtype,
+                   "algo": "mimo_step"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profile(w.name, "mimo_step"),
+                     "algorithmic_bytes_per_launch": alg},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        log("timing the fp64 MIMO oracle on one decode step of a channel sample")
+        threads = max(1, min(os.cpu_count() or 1, 64))
+        idx = sorted(np.random.default_rng(0).permutation(w.dim)[:max(threads, 64)].tolist())
+        x = channel_sample(inputs, idx)
+        first = {k: (v[:, 0:1] if k in per_step and v is not None else v) for k, v in x.items()}
+        second = {k: (v[:, 1:2] if k in per_step and v is not None else v) for k, v in x.items()}
+        q0 = None
+        if trap:  # q of the previous step, the oracle's own sum over the ranks
+            _, _, q0 = oracle.scan_mimo(*(first[k] for k in ("u", "delta", "A", "Bm", "Cm", "Dskip", "theta",
+                                                              "lam")), disc=w.disc, is_complex=w.is_complex,
+                                        return_q=True)
+        h0 = h_start[:, idx].float().cpu().double().numpy()
+        spent, calls = 0.0, 0
+        while spent < args.cpu_seconds:
+            t0 = time.perf_counter()
+            oracle.scan_mimo(*(second[k] for k in ("u", "delta", "A", "Bm", "Cm", "Dskip", "theta", "lam")),
+                             disc=w.disc, is_complex=w.is_complex, h0=h0, q0=q0, nthreads=threads)
+            spent += time.perf_counter() - t0
+            calls += 1
+        tc = calls * w.batch * len(idx)
+        out["cpu_baseline"] = {
+            "value": tc / spent, "unit": UNIT, "cores": min(threads, len(idx)), "kind": "oracle",
+            "sample": f"{len(idx)} of {w.dim} channels (random, seed 0), every batch row, one MIMO decode step "
+                      f"(R={w.rank}) from a given state, repeated {calls} times: {tc} tokens*channels in "
+                      f"{spent:.1f} s of fp64 C oracle time"}
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration(torch, dev, nbytes: int, steps: int, warmup: int):
     """A plain copy of known size: reads and writes `nbytes` per launch."""
     n = (nbytes + 15) // 16 * 4
@@ -446,7 +622,8 @@ def main():
 
     import torch
 
-    from selective_state_space_42_amd.inputs import DECODE_WORKLOADS, SSD_WORKLOADS, WORKLOADS, make_inputs
+    from selective_state_space_42_amd.inputs import (DECODE_WORKLOADS, MIMO_DECODE_WORKLOADS, MIMO_WORKLOADS,
+                                                     SSD_WORKLOADS, WORKLOADS, make_inputs)
     from selective_state_space_42_amd.scan import make_desc, ssm_scan_fwd, ssm_scan_workspace_bytes
 
     dev = torch.device("cuda:0")
@@ -459,6 +636,12 @@ def main():
         return
     if args.workload in SSD_WORKLOADS:
         bench_ssd(args, SSD_WORKLOADS[args.workload], torch, dev)
+        return
+    if args.workload in MIMO_WORKLOADS:
+        bench_mimo(args, MIMO_WORKLOADS[args.workload], torch, dev)
+        return
+    if args.workload in MIMO_DECODE_WORKLOADS:
+        bench_mimo_decode(args, MIMO_DECODE_WORKLOADS[args.workload], torch, dev)
         return
     w = WORKLOADS[args.workload]
     if args.backward:

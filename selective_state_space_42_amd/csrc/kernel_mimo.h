@@ -13,10 +13,11 @@
 // those of the single-input scan (the same story's discretisation table and
 // complex-state section).
 //
-// Layout of the work: one lane per (channel, state); lpc lanes per channel
-// (a power of two >= max(N, R)), 64 / lpc channels per wave.  A lane reads
-// its state's row of B (and C), B[b, t, n, 0..R-1], as one contiguous run,
-// and the channel's R inputs as another.  The R partial sums Re(C[n, r] h[n])
+// Layout of the work: one lane per (channel, state pair); lpc lanes per
+// channel (a power of two >= max(N / 2, R)), 64 / lpc channels per wave.  A
+// lane reads each of its states' rows of B (and C), B[b, t, n, 0..R-1], as
+// one contiguous run, and the channel's R inputs as another; per-step
+// operands are reached through pointers advanced by a stride per step.  The R partial sums Re(C[n, r] h[n])
 // are reduced over the channel's lanes by a reduce-scatter: log2(R) halving
 // levels leave one output per lane group, then the remaining levels add.
 //
@@ -46,7 +47,7 @@
 
 namespace ssm {
 namespace mimo {
-constexpr int kGroup = 8;  // steps whose loads are issued together
+constexpr int kGroup = 4;  // steps whose loads are issued together
 }  // namespace mimo
 
 // NB contiguous bytes (a power of two >= 2, naturally aligned) read with the
@@ -88,16 +89,6 @@ __device__ __forceinline__ float run_elem(const Run<NB>& r, int i) {
     else
         return (i & 1) ? bf16_hi(r.w[i >> 1]) : bf16_lo(r.w[i >> 1]);
 }
-
-// The operands of one step of one lane, as loaded.
-template <typename T, bool CPLX, int R>
-struct MimoIn {
-    static constexpr int kES = sizeof(T), kCw = CPLX ? 2 : 1;
-    Run<kES> dt, lam, th;
-    Run<R * kES> x;         // u[b, t, d, 0 .. R-1]
-    Run<R * kCw * kES> bm;  // B[b, t, n, 0 .. R-1]
-    Run<R * kCw * kES> cm;  // C[b, t, n, 0 .. R-1]
-};
 
 // q = sum_r B[r] x[r] (complex B, real x)
 template <typename T, bool CPLX, int R>
@@ -156,20 +147,44 @@ __device__ __forceinline__ void mimo_advance(float dt, float lam, float th, floa
 
 // Sum over the channel's lpc lanes of R partial outputs, scattered: after
 // log2(R) halving levels at offsets lpc/2 .. lpc/R each lane holds the sum
-// for output mimo_out_index(); the remaining levels complete it.
+// for output mimo_out_index(); the remaining levels complete it.  Which half
+// a lane keeps at each level is fixed per lane: `upm` holds an all-ones word
+// per halving level for the lanes that keep the upper half, and the choice
+// is one bitfield select per value.
 template <int R>
-__device__ __forceinline__ float mimo_reduce_scatter(const float (&v)[R], int pr, int lpc) {
+struct MimoUpMask {
+    uint32_t m[R > 1 ? 31 - __builtin_clz(R) : 1];
+};
+
+template <int R>
+__device__ __forceinline__ MimoUpMask<R> mimo_up_mask(int pr, int lpc) {
+    MimoUpMask<R> u{};
+    int o = lpc >> 1, l = 0;
+#pragma unroll
+    for (int h = R / 2; h >= 1; h >>= 1, ++l) {
+        u.m[l] = (pr & o) ? ~0u : 0u;
+        asm volatile("" : "+v"(u.m[l]));  // opaque: kept as a mask, not re-derived per use
+        o >>= 1;
+    }
+    return u;
+}
+
+__device__ __forceinline__ float mimo_sel(uint32_t m, float a, float b) {  // m ? b : a, bitwise
+    return __uint_as_float((__float_as_uint(b) & m) | (__float_as_uint(a) & ~m));
+}
+
+template <int R>
+__device__ __forceinline__ float mimo_reduce_scatter(const float (&v)[R], const MimoUpMask<R>& up, int lpc) {
     float cur[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) cur[r] = v[r];
-    int o = lpc >> 1;
+    int o = lpc >> 1, l = 0;
 #pragma unroll
-    for (int h = R / 2; h >= 1; h >>= 1) {
-        const bool up = (pr & o) != 0;
+    for (int h = R / 2; h >= 1; h >>= 1, ++l) {
 #pragma unroll
         for (int i = 0; i < h; ++i) {
-            const float keep = up ? cur[h + i] : cur[i];
-            const float send = up ? cur[i] : cur[h + i];
+            const float keep = mimo_sel(up.m[l], cur[i], cur[h + i]);
+            const float send = mimo_sel(up.m[l], cur[h + i], cur[i]);
             cur[i] = keep + __shfl_xor(send, o, 64);
         }
         o >>= 1;
@@ -190,32 +205,60 @@ __device__ __forceinline__ int mimo_out_index(int pr, int lpc) {
     return r;
 }
 
-// x[r_own] without dynamic register indexing
-template <int R>
-__device__ __forceinline__ float mimo_pick(const float (&x)[R], int r_own) {
-    float v = x[0];
-#pragma unroll
-    for (int r = 1; r < R; ++r) v = r == r_own ? x[r] : v;
-    return v;
+// Per-lane pointers to one step's operands, advanced by a stride per step.
+// A lane holds two states, n0 = 2 pr and n1 = n0 + 1; a state past N reads
+// state n0's row again and is masked, and a missing theta (complex state,
+// theta = 0) reads delta's element instead and is ignored, so no load
+// needs a branch.
+template <typename T>
+struct MimoPtrs {
+    const T *dt, *lam, *x, *th0, *th1, *b0, *b1, *c0, *c1;
+    T* y;
+};
+
+struct MimoStrides {
+    int64_t tc, x, th, bn;  // per step: delta and lambda, u and y, theta, B and C
+};
+
+template <typename T>
+__device__ __forceinline__ void mimo_advance_ptrs(MimoPtrs<T>& q, const MimoStrides& s) {
+    q.dt += s.tc;
+    q.lam += s.tc;
+    q.x += s.x;
+    q.y += s.x;
+    q.th0 += s.th;
+    q.th1 += s.th;
+    q.b0 += s.bn;
+    q.b1 += s.bn;
+    q.c0 += s.bn;
+    q.c1 += s.bn;
 }
 
-// Every operand of step t for one lane.  Without theta (complex state, theta
-// = 0) the rotation slot reads delta's element instead and is ignored, so the
-// loads carry no branches.
+// The operands of one step of one lane, as loaded (raw bits).
+template <typename T, bool CPLX, int R>
+struct MimoIn {
+    static constexpr int kES = sizeof(T), kCw = CPLX ? 2 : 1;
+    Run<kES> dt, lam, th[2];
+    Run<R * kES> x;            // u[b, t, d, 0 .. R-1]
+    Run<R * kCw * kES> bm[2];  // B[b, t, n_j, 0 .. R-1]
+    Run<R * kCw * kES> cm[2];  // C[b, t, n_j, 0 .. R-1]
+};
+
 template <typename T, int DISC, bool CPLX, int R, bool WITH_C>
-__device__ __forceinline__ void mimo_load(const MimoParams& p, int64_t b, int64_t d, int64_t n, int64_t t,
-                                          MimoIn<T, CPLX, R>& in) {
-    constexpr int kCw = CPLX ? 2 : 1;
-    const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
-    const int64_t tc = (b * L + t) * D + d;
-    const int64_t bn = ((b * L + t) * N + n) * R * kCw;
-    const T* delta = static_cast<const T*>(p.delta);
-    load_run(delta + tc, in.dt);
-    if constexpr (DISC == kTrap) load_run(static_cast<const T*>(p.lambda) + tc, in.lam);
-    load_run(static_cast<const T*>(p.u) + tc * R, in.x);
-    if constexpr (CPLX) load_run(p.theta ? static_cast<const T*>(p.theta) + tc * N + n : delta + tc, in.th);
-    load_run(static_cast<const T*>(p.B) + bn, in.bm);
-    if constexpr (WITH_C) load_run(static_cast<const T*>(p.C) + bn, in.cm);
+__device__ __forceinline__ void mimo_load(const MimoPtrs<T>& q, MimoIn<T, CPLX, R>& in) {
+    load_run(q.dt, in.dt);
+    if constexpr (DISC == kTrap) load_run(q.lam, in.lam);
+    load_run(q.x, in.x);
+    if constexpr (CPLX) {
+        load_run(q.th0, in.th[0]);
+        load_run(q.th1, in.th[1]);
+    }
+    load_run(q.b0, in.bm[0]);
+    load_run(q.b1, in.bm[1]);
+    if constexpr (WITH_C) {
+        load_run(q.c0, in.cm[0]);
+        load_run(q.c1, in.cm[1]);
+    }
 }
 
 template <typename T, int DISC, bool CPLX, int R, bool OUT>
@@ -230,110 +273,160 @@ __global__ void __launch_bounds__(256) mimo_scan_kernel(MimoParams p) {
     if (c >= (OUT ? p.nchunks : p.nchunks - 1)) return;  // whole waves
     const int64_t ch_raw = (gw % wpc) * (64 / lpc) + lane / lpc;
     const int pr = lane & (lpc - 1);
-    const bool ch_ok = ch_raw < BD, ok = ch_ok && pr < N;
+    const int64_t n0_raw = 2 * pr;
+    const bool ch_ok = ch_raw < BD;
+    const bool ok[2] = {ch_ok && n0_raw < N, ch_ok && n0_raw + 1 < N};
     // lanes past the problem compute on valid addresses and write nothing
-    const int64_t ch = ch_ok ? ch_raw : BD - 1, n = pr < N ? pr : N - 1;
-    const int64_t b = ch / D, d = ch % D, sidx = ch * N + n;
+    const int64_t ch = ch_ok ? ch_raw : BD - 1, n0 = n0_raw < N ? n0_raw : N - 1;
+    const int64_t n1 = n0 + 1 < N ? n0 + 1 : n0;
+    const int64_t b = ch / D, d = ch % D;
+    const int64_t s0 = ch * N + n0, s1 = ch * N + n1;  // (b, d, n) in the layout of h0
     const int64_t t0 = c * p.chunk, t1 = t0 + p.chunk < L ? t0 + p.chunk : L;
 
-    const float a = p.A[d * N + n], a2 = prep_A(a);
-    const float dsk = p.Dskip ? p.Dskip[d] : 0.f;
+    const float a[2] = {p.A[d * N + n0], p.A[d * N + n1]};
+    const float a2[2] = {prep_A(a[0]), prep_A(a[1])};
+    // the skip term D u[r] joins the sum over the channel's lanes in one lane
+    const float dmask = (p.Dskip && pr == 0) ? p.Dskip[d] : 0.f;
     const int r_own = mimo_out_index<R>(pr, lpc);
     const bool writer = ch_ok && (pr & (lpc / R - 1)) == 0;
+    const MimoUpMask<R> upm = mimo_up_mask<R>(pr, lpc);
 
-    float hr = 0.f, hi = 0.f, qpr = 0.f, qpi = 0.f;
-    float Pr = 1.f, Pi = 0.f;  // LOCAL: product of the chunk's decays
-    if constexpr (OUT) {
-        if (c == 0) {
-            if (p.h0) {
-                hr = p.h0[sidx * kCw];
-                if constexpr (CPLX) hi = p.h0[sidx * 2 + 1];
-            }
-        } else {
-            const float* s = p.carry + ((c - 1) * BD * N + sidx) * 2 * kCw;
-            hr = s[kCw];
-            if constexpr (CPLX) hi = s[3];
-        }
-    }
-    if constexpr (DISC == kTrap) {
-        if (t0 == 0) {
-            if (p.q0) {
-                qpr = p.q0[sidx * kCw];
-                if constexpr (CPLX) qpi = p.q0[sidx * 2 + 1];
-            }
-        } else {  // q_{t0-1} from the inputs of step t0 - 1
-            MimoIn<T, CPLX, R> in;
-            mimo_load<T, DISC, CPLX, R, false>(p, b, d, n, t0 - 1, in);
-            float x[R];
+    float hr[2] = {0.f, 0.f}, hi[2] = {0.f, 0.f}, qpr[2] = {0.f, 0.f}, qpi[2] = {0.f, 0.f};
+    float Pr[2] = {1.f, 1.f}, Pi[2] = {0.f, 0.f};  // LOCAL: product of the chunk's decays
+    const int64_t sidx[2] = {s0, s1};
 #pragma unroll
-            for (int r = 0; r < R; ++r) x[r] = run_elem<T>(in.x, r);
-            mimo_q<T, CPLX, R>(in.bm, x, &qpr, &qpi);
+    for (int j = 0; j < 2; ++j) {
+        if constexpr (OUT) {
+            if (c == 0) {
+                if (p.h0) {
+                    hr[j] = p.h0[sidx[j] * kCw];
+                    if constexpr (CPLX) hi[j] = p.h0[sidx[j] * 2 + 1];
+                }
+            } else {
+                const float* sl = p.carry + ((c - 1) * BD * N + sidx[j]) * 2 * kCw;
+                hr[j] = sl[kCw];
+                if constexpr (CPLX) hi[j] = sl[3];
+            }
+        }
+        if constexpr (DISC == kTrap) {
+            if (t0 == 0 && p.q0) {
+                qpr[j] = p.q0[sidx[j] * kCw];
+                if constexpr (CPLX) qpi[j] = p.q0[sidx[j] * 2 + 1];
+            }
         }
     }
-    if (!ok) hr = hi = qpr = qpi = 0.f;
 
+    // pointers to step t0's operands
+    const T* delta = static_cast<const T*>(p.delta);
+    const int64_t tc0 = (b * L + t0) * D + d, bn0 = ((b * L + t0) * N + n0) * R * kCw;
+    const int64_t dn = (n1 - n0) * R * kCw;
+    MimoPtrs<T> q;
+    q.dt = delta + tc0;
+    q.lam = DISC == kTrap ? static_cast<const T*>(p.lambda) + tc0 : q.dt;
+    q.x = static_cast<const T*>(p.u) + tc0 * R;
+    q.y = static_cast<T*>(p.y) + tc0 * R + r_own;
     const bool has_th = CPLX && p.theta;
-    T* y = static_cast<T*>(p.y);
-    for (int64_t tg = t0; tg < t1; tg += kG) {
+    q.th0 = has_th ? static_cast<const T*>(p.theta) + tc0 * N + n0 : q.dt;
+    q.th1 = has_th ? q.th0 + (n1 - n0) : q.dt;
+    q.b0 = static_cast<const T*>(p.B) + bn0;
+    q.b1 = q.b0 + dn;
+    q.c0 = static_cast<const T*>(p.C) + bn0;
+    q.c1 = q.c0 + dn;
+    const MimoStrides st{D, D * R, has_th ? D * N : D, N * R * kCw};
+
+    if (DISC == kTrap && t0 > 0) {  // q_{t0-1} from the inputs of step t0 - 1
+        MimoPtrs<T> qp = q;
+        const MimoStrides back{-st.tc, -st.x, -st.th, -st.bn};
+        mimo_advance_ptrs(qp, back);
+        MimoIn<T, CPLX, R> in;
+        mimo_load<T, DISC, CPLX, R, false>(qp, in);
+        float x[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[r] = run_elem<T>(in.x, r);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mimo_q<T, CPLX, R>(in.bm[j], x, &qpr[j], &qpi[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        if (!ok[j]) hr[j] = hi[j] = qpr[j] = qpi[j] = 0.f;
+
+    T* yp = q.y;
+    // kG steps: their loads first, then their arithmetic (the compiler also
+    // issues the next group's loads during a group).  The tail group stops its
+    // pointers on the chunk's last step, so no load passes the chunk.
+    auto group = [&](int64_t tg, auto tail_tag) {
+        constexpr bool kTail = decltype(tail_tag)::value;
         MimoIn<T, CPLX, R> in[kG];
 #pragma unroll
         for (int k = 0; k < kG; ++k) {
-            const int64_t t = tg + k < t1 ? tg + k : t1 - 1;
-            mimo_load<T, DISC, CPLX, R, OUT>(p, b, d, n, t, in[k]);
+            mimo_load<T, DISC, CPLX, R, OUT>(q, in[k]);
+            if (!kTail || tg + k + 1 < t1) mimo_advance_ptrs(q, st);
         }
 #pragma unroll
         for (int k = 0; k < kG; ++k) {
-            if (tg + k >= t1) break;
+            if (kTail && tg + k >= t1) break;
             const float dt = run_elem<T>(in[k].dt, 0);
             const float lam = DISC == kTrap ? run_elem<T>(in[k].lam, 0) : 0.f;
-            const float th = has_th ? run_elem<T>(in[k].th, 0) : 0.f;
             float x[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) x[r] = run_elem<T>(in[k].x, r);
-            float qr, qi;
-            mimo_q<T, CPLX, R>(in[k].bm, x, &qr, &qi);
-            if (!ok) qr = qi = 0.f;
-            float ar, ai;
-            mimo_advance<DISC, CPLX, SC>(dt, lam, th, qr, qi, a, a2, hr, hi, qpr, qpi, &ar, &ai);
-            if constexpr (OUT) {
-                float part[R];
+            float part[R];
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    float v = run_elem<T>(in[k].cm, r * kCw) * hr;  // Re(C h), no conjugate
-                    if constexpr (CPLX) v = __builtin_fmaf(-run_elem<T>(in[k].cm, r * kCw + 1), hi, v);
-                    part[r] = ok ? v : 0.f;
+            for (int r = 0; r < R; ++r) part[r] = dmask * x[r];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float th = has_th ? run_elem<T>(in[k].th[j], 0) : 0.f;
+                float qr, qi;
+                mimo_q<T, CPLX, R>(in[k].bm[j], x, &qr, &qi);
+                if (!ok[j]) qr = qi = 0.f;
+                float ar, ai;
+                mimo_advance<DISC, CPLX, SC>(dt, lam, th, qr, qi, a[j], a2[j], hr[j], hi[j], qpr[j], qpi[j], &ar,
+                                             &ai);
+                if constexpr (OUT) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {  // Re(C h), no conjugate; a masked state's h is 0
+                        part[r] = __builtin_fmaf(run_elem<T>(in[k].cm[j], r * kCw), hr[j], part[r]);
+                        if constexpr (CPLX)
+                            part[r] = __builtin_fmaf(-run_elem<T>(in[k].cm[j], r * kCw + 1), hi[j], part[r]);
+                    }
+                } else {
+                    const float nr = ar * Pr[j] - ai * Pi[j];
+                    Pi[j] = ar * Pi[j] + ai * Pr[j];
+                    Pr[j] = nr;
                 }
-                const float s = mimo_reduce_scatter<R>(part, pr, lpc);
-                if (writer) {
-                    const int64_t tc = (b * L + tg + k) * D + d;
-                    Elem<T>::store(y, tc * R + r_own, s + dsk * mimo_pick<R>(x, r_own));
-                }
-            } else {
-                const float nr = ar * Pr - ai * Pi;
-                Pi = ar * Pi + ai * Pr;
-                Pr = nr;
+            }
+            if constexpr (OUT) {
+                const float sum = mimo_reduce_scatter<R>(part, upm, lpc);
+                if (writer) Elem<T>::store(yp, 0, sum);
+                yp += st.x;
             }
         }
-    }
+    };
+    int64_t tg = t0;
+    for (; tg + kG <= t1; tg += kG) group(tg, std::false_type{});
+    if (tg < t1) group(tg, std::true_type{});
 
-    if (!ok) return;
-    if constexpr (OUT) {
-        if (c == p.nchunks - 1) {
-            if (p.h_last) {
-                p.h_last[sidx * kCw] = hr;
-                if constexpr (CPLX) p.h_last[sidx * 2 + 1] = hi;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (!ok[j]) continue;
+        if constexpr (OUT) {
+            if (c == p.nchunks - 1) {
+                if (p.h_last) {
+                    p.h_last[sidx[j] * kCw] = hr[j];
+                    if constexpr (CPLX) p.h_last[sidx[j] * 2 + 1] = hi[j];
+                }
+                if (DISC == kTrap && p.q_last) {
+                    p.q_last[sidx[j] * kCw] = qpr[j];
+                    if constexpr (CPLX) p.q_last[sidx[j] * 2 + 1] = qpi[j];
+                }
             }
-            if (DISC == kTrap && p.q_last) {
-                p.q_last[sidx * kCw] = qpr;
-                if constexpr (CPLX) p.q_last[sidx * 2 + 1] = qpi;
-            }
+        } else {
+            float* sl = p.carry + (c * BD * N + sidx[j]) * 2 * kCw;
+            if constexpr (CPLX)
+                *reinterpret_cast<float4*>(sl) = make_float4(Pr[j], Pi[j], hr[j], hi[j]);
+            else
+                *reinterpret_cast<float2*>(sl) = make_float2(Pr[j], hr[j]);
         }
-    } else {
-        float* s = p.carry + (c * BD * N + sidx) * 2 * kCw;
-        if constexpr (CPLX)
-            *reinterpret_cast<float4*>(s) = make_float4(Pr, Pi, hr, hi);
-        else
-            *reinterpret_cast<float2*>(s) = make_float2(Pr, hr);
     }
 }
 
@@ -366,8 +459,10 @@ __global__ void __launch_bounds__(256) mimo_carry_kernel(MimoParams p) {
     }
 }
 
-// One decode step of the MIMO recurrence with the state in memory.
-template <typename T, int DISC, bool CPLX, int R>
+// One decode step of the MIMO recurrence with the state in memory; two
+// states per lane.  PAIRS: N even and h aligned for a lane's two states, so
+// the state moves with one vector load and store per lane.
+template <typename T, int DISC, bool CPLX, int R, bool PAIRS>
 __global__ void __launch_bounds__(256) mimo_step_kernel(MimoStepParams p) {
     constexpr int kCw = CPLX ? 2 : 1, kES = sizeof(T);
     constexpr int SC = std::is_same_v<T, uint16_t> ? kSinCosHw : kSinCosWide;
@@ -376,27 +471,47 @@ __global__ void __launch_bounds__(256) mimo_step_kernel(MimoStepParams p) {
     const int64_t gw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
     const int64_t ch_raw = gw * (64 / lpc) + lane / lpc;
     const int pr = lane & (lpc - 1);
-    const bool ch_ok = ch_raw < BD, ok = ch_ok && pr < N;
-    const int64_t ch = ch_ok ? ch_raw : BD - 1, n = pr < N ? pr : N - 1;
-    const int64_t b = ch / D, d = ch % D, sidx = ch * N + n;
-    const int64_t bn = (b * N + n) * R * kCw;
+    const int64_t n0_raw = 2 * pr;
+    const bool ch_ok = ch_raw < BD;
+    const bool ok[2] = {ch_ok && n0_raw < N, ch_ok && n0_raw + 1 < N};
+    const int64_t ch = ch_ok ? ch_raw : BD - 1, n0 = n0_raw < N ? n0_raw : N - 1;
+    const int64_t n1 = n0 + 1 < N ? n0 + 1 : n0;
+    const int64_t b = ch / D, d = ch % D;
+    const int64_t sidx[2] = {ch * N + n0, ch * N + n1};
+    const int64_t bn[2] = {(b * N + n0) * R * kCw, (b * N + n1) * R * kCw};
 
-    Run<kES> rdt, rlam, rth;
+    Run<kES> rdt, rlam, rth[2];
     Run<R * kES> rx, rxp;
-    Run<R * kCw * kES> rb, rc, rbp;
+    Run<R * kCw * kES> rb[2], rc[2], rbp[2];
     load_run(static_cast<const T*>(p.delta) + ch, rdt);
     load_run(static_cast<const T*>(p.u) + ch * R, rx);
-    load_run(static_cast<const T*>(p.B) + bn, rb);
-    load_run(static_cast<const T*>(p.C) + bn, rc);
-    if (CPLX && p.theta) load_run(static_cast<const T*>(p.theta) + sidx, rth);
+    const bool has_th = CPLX && p.theta;
     const bool prev = DISC == kTrap && p.u_prev;
     if (DISC == kTrap) load_run(static_cast<const T*>(p.lambda) + ch, rlam);
-    if (prev) {
-        load_run(static_cast<const T*>(p.u_prev) + ch * R, rxp);
-        load_run(static_cast<const T*>(p.B_prev) + bn, rbp);
+    if (prev) load_run(static_cast<const T*>(p.u_prev) + ch * R, rxp);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        load_run(static_cast<const T*>(p.B) + bn[j], rb[j]);
+        load_run(static_cast<const T*>(p.C) + bn[j], rc[j]);
+        if (has_th) load_run(static_cast<const T*>(p.theta) + sidx[j], rth[j]);
+        if (prev) load_run(static_cast<const T*>(p.B_prev) + bn[j], rbp[j]);
     }
-    float hr = p.h[sidx * kCw], hi = CPLX ? p.h[sidx * 2 + 1] : 0.f;
-    const float a = p.A[d * N + n], a2 = prep_A(a);
+    float hr[2], hi[2] = {0.f, 0.f};
+    if constexpr (PAIRS) {
+        if constexpr (CPLX) {
+            const float4 v = *reinterpret_cast<const float4*>(p.h + sidx[0] * 2);
+            hr[0] = v.x, hi[0] = v.y, hr[1] = v.z, hi[1] = v.w;
+        } else {
+            const float2 v = *reinterpret_cast<const float2*>(p.h + sidx[0]);
+            hr[0] = v.x, hr[1] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            hr[j] = p.h[sidx[j] * kCw];
+            if constexpr (CPLX) hi[j] = p.h[sidx[j] * 2 + 1];
+        }
+    }
 
     float x[R], xp[R];
 #pragma unroll
@@ -404,30 +519,46 @@ __global__ void __launch_bounds__(256) mimo_step_kernel(MimoStepParams p) {
         x[r] = run_elem<T>(rx, r);
         xp[r] = prev ? run_elem<T>(rxp, r) : 0.f;
     }
-    float qr, qi, qpr = 0.f, qpi = 0.f;
-    mimo_q<T, CPLX, R>(rb, x, &qr, &qi);
-    if (prev) mimo_q<T, CPLX, R>(rbp, xp, &qpr, &qpi);
     const float dt = run_elem<T>(rdt, 0);
     const float lam = DISC == kTrap ? run_elem<T>(rlam, 0) : 0.f;
-    const float th = (CPLX && p.theta) ? run_elem<T>(rth, 0) : 0.f;
-    float ar, ai;
-    mimo_advance<DISC, CPLX, SC>(dt, lam, th, qr, qi, a, a2, hr, hi, qpr, qpi, &ar, &ai);
-    if (ok) {
-        p.h[sidx * kCw] = hr;
-        if constexpr (CPLX) p.h[sidx * 2 + 1] = hi;
-    }
     float part[R];
+    const float dmask = (p.Dskip && pr == 0) ? p.Dskip[d] : 0.f;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        float v = run_elem<T>(rc, r * kCw) * hr;
-        if constexpr (CPLX) v = __builtin_fmaf(-run_elem<T>(rc, r * kCw + 1), hi, v);
-        part[r] = ok ? v : 0.f;
+    for (int r = 0; r < R; ++r) part[r] = dmask * x[r];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float qr, qi, qpr = 0.f, qpi = 0.f;
+        mimo_q<T, CPLX, R>(rb[j], x, &qr, &qi);
+        if (prev) mimo_q<T, CPLX, R>(rbp[j], xp, &qpr, &qpi);
+        const float a = p.A[d * N + (j ? n1 : n0)];
+        const float th = has_th ? run_elem<T>(rth[j], 0) : 0.f;
+        float ar, ai;
+        mimo_advance<DISC, CPLX, SC>(dt, lam, th, qr, qi, a, prep_A(a), hr[j], hi[j], qpr, qpi, &ar, &ai);
+        if (!ok[j]) hr[j] = hi[j] = 0.f;  // a masked state adds nothing below
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            part[r] = __builtin_fmaf(run_elem<T>(rc[j], r * kCw), hr[j], part[r]);
+            if constexpr (CPLX) part[r] = __builtin_fmaf(-run_elem<T>(rc[j], r * kCw + 1), hi[j], part[r]);
+        }
     }
-    const float s = mimo_reduce_scatter<R>(part, pr, lpc);
+    if constexpr (PAIRS) {
+        if (ok[0]) {
+            if constexpr (CPLX)
+                *reinterpret_cast<float4*>(p.h + sidx[0] * 2) = make_float4(hr[0], hi[0], hr[1], hi[1]);
+            else
+                *reinterpret_cast<float2*>(p.h + sidx[0]) = make_float2(hr[0], hr[1]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (!ok[j]) continue;
+            p.h[sidx[j] * kCw] = hr[j];
+            if constexpr (CPLX) p.h[sidx[j] * 2 + 1] = hi[j];
+        }
+    }
+    const float sum = mimo_reduce_scatter<R>(part, mimo_up_mask<R>(pr, lpc), lpc);
     const int r_own = mimo_out_index<R>(pr, lpc);
-    if (ch_ok && (pr & (lpc / R - 1)) == 0)
-        Elem<T>::store(static_cast<T*>(p.y), ch * R + r_own,
-                       s + (p.Dskip ? p.Dskip[d] : 0.f) * mimo_pick<R>(x, r_own));
+    if (ch_ok && (pr & (lpc / R - 1)) == 0) Elem<T>::store(static_cast<T*>(p.y), ch * R + r_own, sum);
 }
 
 }  // namespace ssm

@@ -26,8 +26,11 @@ hipError_t scan_r(const MimoParams& p, hipStream_t s) {
 template <typename T, int DISC, bool CPLX, int R>
 hipError_t step_r(const MimoStepParams& p, hipStream_t s) {
     const int64_t waves = (p.batch * p.dim * p.lpc + 63) / 64;
-    hipLaunchKernelGGL((mimo_step_kernel<T, DISC, CPLX, R>), dim3(static_cast<unsigned>((waves + 3) / 4)),
-                       dim3(256), 0, s, p);
+    const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+    if (p.pairs)
+        hipLaunchKernelGGL((mimo_step_kernel<T, DISC, CPLX, R, true>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((mimo_step_kernel<T, DISC, CPLX, R, false>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ struct MimoParams {
     int64_t batch, seqlen, dim, dstate;
     int64_t chunk;  // steps per time chunk
     int32_t nchunks;
-    int32_t lpc;  // lanes per channel: power of two, >= dstate and >= R, <= 64
+    int32_t lpc;  // lanes per channel: power of two, 2 lpc >= dstate, lpc >= R, lpc <= 32
 };
 
 struct MimoStepParams {
@@ -43,7 +43,8 @@ struct MimoStepParams {
     float* h;            // [B][D][N] or [B][D][N][2], read and overwritten
     void* y;             // [B][D][R]
     int64_t batch, dim, dstate;
-    int32_t lpc;
+    int32_t lpc;    // as for MimoParams
+    int32_t pairs;  // N even and h aligned to a lane's two states: one vector load and store each
 };
 
 // Enqueue the MIMO scan (time-chunk kernels, carry, output) or one decode

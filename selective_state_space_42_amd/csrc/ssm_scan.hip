@@ -217,20 +217,21 @@ int check_mimo_desc(const ssm_mimo_desc_t* d) {
     return SSM_OK;
 }
 
-// lanes per channel of the MIMO kernels: one per state, at least one per output
+// lanes per channel of the MIMO kernels: one per pair of states, at least one per output
 int mimo_lpc(const ssm_mimo_desc_t* d) {
-    const int l = next_pow2(d->dstate);
+    const int l = next_pow2((d->dstate + 1) / 2);
     return l < d->rank ? static_cast<int>(d->rank) : l;
 }
 
-// Time chunks of the MIMO scan.  Unless the caller fixes the chunk length,
-// the sequence is cut into as many chunks (of at least 64 steps) as it takes
-// to give the GPU about 2^18 lanes, four waves per SIMD on 256 compute units;
-// a problem wide enough on its own runs as one chunk.
+// Time chunks of the MIMO scan.  Every chunk but the last costs a second
+// sweep (its decay product and end state), so the sequence is cut only when
+// the problem is too narrow to give each SIMD of a 256-CU GPU a wave of its
+// own (2^16 lanes): then into as many chunks of at least 64 steps as reach
+// that.  The caller can fix the chunk length instead.
 void mimo_chunking(const ssm_mimo_desc_t* d, int64_t* chunk, int64_t* nchunks) {
     int64_t c = d->chunk;
     if (c == 0) {
-        constexpr int64_t kTargetLanes = int64_t(1) << 18;
+        constexpr int64_t kTargetLanes = int64_t(1) << 16;
         const int64_t lanes = d->batch * d->dim * mimo_lpc(d);
         int64_t want = (kTargetLanes + lanes - 1) / lanes;
         const int64_t most = (d->seqlen + 63) / 64;
@@ -533,6 +534,7 @@ int ssm_mimo_step(const ssm_mimo_desc_t* desc, const void* u, const void* delta,
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.theta = theta; p.lambda = lambda;
     p.u_prev = u_prev; p.B_prev = B_prev; p.h = h; p.y = y;
     p.batch = desc->batch; p.dim = desc->dim; p.dstate = desc->dstate; p.lpc = lpc;
+    p.pairs = desc->dstate % 2 == 0 && aligned(h, desc->is_complex ? 16 : 8);
     return hip_status(ssm::launch_mimo_step(p, desc->io_dtype == SSM_DTYPE_BF16, desc->disc, desc->is_complex != 0,
                                             static_cast<int>(desc->rank), static_cast<hipStream_t>(stream)));
 }

@@ -270,6 +270,9 @@ def test_mimo_workspace_follows_the_chunking():
     # a narrow, long problem is cut into chunks of at least 64 steps
     need = scan.ssm_mimo_workspace_bytes(mimo_desc(B=1, D=8, N=16, L=1 << 14))
     assert need == (256 - 1) * 8 * 16 * 16
+    # 2^16 lanes (8192 channels of 8 lanes) fill the GPU: one chunk
+    assert scan.ssm_mimo_workspace_bytes(mimo_desc(B=4, D=2048, N=16, L=8192)) == 0
+    assert scan.ssm_mimo_workspace_bytes(mimo_desc(B=2, D=2048, N=16, L=8192)) == 1 * 2 * 2048 * 16 * 16
     d = mimo_desc(L=100, chunk=16)
     assert call_mimo(d, ws=P, ws_bytes=scan.ssm_mimo_workspace_bytes(d) - 1) == WS_SMALL
     assert call_mimo(d, ws=0, ws_bytes=0) == WS_SMALL
