@@ -19,19 +19,32 @@
 // that recomputation (its hardware-challenges section, first and third
 // layers), which is the structure used here.
 //
-// Work decomposition: one lane per (channel, state), lpc lanes per channel
-// (a power of two >= N), like the sequential forward kernel.
+// Work decomposition: one lane per (channel, state), LPC = 16 (N <= 16) or 64
+// lanes per channel, 64 / LPC channels of one batch row per wave (a batch
+// row's last wave may be partly idle).  Every operand of step t of a lane is
+// a wave-uniform base (scalar registers, advanced per step) plus a small
+// fixed per-lane offset, so no access needs vector address arithmetic.
 //   1. bwd_ckpt_kernel sweeps forward once and stores the state before every
 //      segment of kSeg steps (the only state-sized data in memory: L/kSeg
 //      snapshots).
-//   2. bwd_main_kernel walks the segments from the last to the first: it
-//      recomputes the segment's states from its snapshot into wave-private
-//      LDS, then runs the reverse sweep over them.  Both sweeps issue their
-//      loads kGroup steps at a time.
-// Sums: du, ddelta, dlambda per (b, t, d) over the channel's lanes by
-// shuffles; dB, dC per (b, t, n) over channels, first across the wave's
+//   2. The sequence is cut into time chunks (whole segments) so that the
+//      reverse sweeps of a narrow problem still fill the GPU.  The adjoint
+//      entering chunk c from above, X_c = conj(alpha_{t1}) G_{t1} (t1 the
+//      chunk's end), is linear in the next chunk's: X_{c-1} = Q_c X_c + R_c
+//      with Q_c the product of conj(alpha) over chunk c and R_c its adjoint
+//      swept from zero.  bwd_adj_kernel computes (Q_c, R_c) for every chunk
+//      but the first, and bwd_adj_carry_kernel chains them from X = dh_last
+//      down (the combine of the fengwang.github.io essay, in reverse).
+//   3. bwd_main_kernel runs every chunk in parallel from its X_c, walking its
+//      segments from the last to the first: it recomputes a segment's states
+//      from its snapshot into wave-private LDS, then runs the reverse sweep
+//      over them.  The trapezoid's term that step t1 sends back to q_{t1-1}
+//      is (1 - lambda_{t1}) delta_{t1} X_c.  The sweeps issue their loads
+//      kGroup steps at a time.
+// Sums: du, ddelta, dlambda per (b, t, d) over the channel's lanes by DPP
+// butterflies; dB, dC per (b, t, n) over channels, first across the wave's
 // channels by shuffles, then one atomic add per wave; dA per (d, n) and dD
-// per d accumulated per lane over the whole sequence, one atomic add each.
+// per d accumulated per lane over the chunk, one atomic add each.
 // The atomically summed outputs are zeroed first by bwd_zero_kernel.
 // Arithmetic follows the forward kernels' policies (hardware 2^x; sin/cos by
 // hardware on fract(theta / 2 pi) for bf16 I/O, fp64-reduced polynomials for
@@ -72,8 +85,11 @@ struct BwdParams {
     float* dlambda;        // [B][L][D] (trapezoid)
     float* dh0;            // layout of h_last or NULL
     float* ckpt;           // [nseg][B][D][N] (x2 complex): state before each segment
+    float* adj;            // [nchunks][B][D][N] x (Q, R) complex (4 floats) or real (2): chunk adjoints
     int64_t batch, seqlen, dim, dstate;
-    int32_t lpc;
+    int64_t chunk;         // steps per time chunk (a multiple of kSeg)
+    int32_t nchunks;
+    int32_t lpc;           // lanes per channel (16 or 64), as the kernels are instantiated
 };
 
 __global__ void __launch_bounds__(256) bwd_zero_kernel(float* a, int64_t na, float* b, int64_t nb, float* c,
@@ -91,177 +107,159 @@ __global__ void __launch_bounds__(256) bwd_zero_kernel(float* a, int64_t na, flo
     }
 }
 
-// One step's operands of a lane (zero past N, past the channels and on a
-// masked step, which then leaves the state unchanged: alpha = 1, bterm = 0).
-struct BwdStep {
-    float x, dt, lam, ar, ai, br, bi, cr, ci, a, rho, em1;
-};
-
-// Lane geometry.  Every load uses clamped (always valid) indices and masks
-// its value afterwards, so loads carry no branches and the compiler can
-// issue a whole segment's loads together.
-struct BwdLane {
-    int64_t ch, b, d;  // b, d clamped to the last channel
-    int n, nc;         // nc clamped to N - 1
+// Lane geometry.  Waves never straddle batch rows, so a wave's lanes share
+// b and the wave-uniform values (b, its first channel d0, the time chunk c)
+// come from the wave index alone.
+template <int LPC>
+struct BwdGeo {
+    static constexpr int kCPW = 64 / LPC;  // channels per wave
+    int64_t b, d0, c;                      // uniform
+    int64_t d;                             // the lane's channel, clamped to D - 1
+    int n, nc;                             // state, clamped to N - 1
     bool ch_ok, ok;
 };
 
-__device__ __forceinline__ BwdLane bwd_lane(const BwdParams& p) {
-    BwdLane l;
-    const int lane = threadIdx.x & 63;
-    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
-    l.ch = wave * (64 / p.lpc) + lane / p.lpc;
-    l.n = lane & (p.lpc - 1);
-    l.ch_ok = l.ch < p.batch * p.dim;
-    l.ok = l.ch_ok && l.n < p.dstate;
-    const int64_t chc = l.ch_ok ? l.ch : p.batch * p.dim - 1;
-    l.b = chc / p.dim;
-    l.d = chc % p.dim;
-    l.nc = l.n < p.dstate ? l.n : static_cast<int>(p.dstate) - 1;
-    return l;
+template <int LPC>
+__device__ __forceinline__ int64_t bwd_waves_per_chunk(const BwdParams& p) {
+    return p.batch * ((p.dim + BwdGeo<LPC>::kCPW - 1) / BwdGeo<LPC>::kCPW);
 }
 
-// A lane's input pointers at the first step of a segment; step k of the
-// segment is k strides further (strides fit 32 bits, checked by the host).
+template <int LPC, bool CPLX>
+__device__ __forceinline__ BwdGeo<LPC> bwd_geo(const BwdParams& p, bool chunked) {
+    constexpr int kCPW = BwdGeo<LPC>::kCPW;
+    BwdGeo<LPC> g;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t wpb = (p.dim + kCPW - 1) / kCPW;  // waves per batch row
+    const int64_t wpc = p.batch * wpb;
+    g.c = chunked ? wave / wpc : 0;
+    const int64_t wv = chunked ? wave % wpc : wave;
+    g.b = wv / wpb;
+    g.d0 = (wv % wpb) * kCPW;
+    const int64_t d = g.d0 + lane / LPC;
+    g.n = lane & (LPC - 1);
+    g.ch_ok = d < p.dim && g.b < p.batch;
+    g.ok = g.ch_ok && g.n < p.dstate;
+    g.d = d < p.dim ? d : p.dim - 1;
+    g.nc = g.n < p.dstate ? g.n : static_cast<int>(p.dstate) - 1;
+    return g;
+}
+
+// the stored bits of element i (decoded by bwd_f)
 template <typename T>
-struct BwdPtrs {
-    const T *u, *dt, *lam, *th, *B, *C, *dy;
-    int32_t s_tc, s_th, s_bn;  // strides per step: D, D*N (theta), N*cw (B, C)
+__device__ __forceinline__ uint32_t bwd_bits(const T* p, int64_t i) {
+    if constexpr (std::is_same_v<T, float>)
+        return __float_as_uint(p[i]);
+    else
+        return p[i];
+}
+
+template <typename T>
+__device__ __forceinline__ float bwd_f(uint32_t raw) {
+    if constexpr (std::is_same_v<T, float>)
+        return __uint_as_float(raw);
+    else
+        return __uint_as_float(raw << 16);
+}
+
+// Per-lane pointers to step t's operands and gradient slots, and the
+// (uniform) number of elements each moves per step.
+template <typename T>
+struct BwdPtr {
+    const T *u, *dt, *lam, *dy, *th, *B, *C;
+    float *du, *ddt, *dlam, *dth, *dB, *dC;
+};
+struct BwdStride {
+    int64_t tc, th, bn;  // per-token arrays, theta, B and C
 };
 
-// Move a lane's pointers by `steps` steps.  The moved pointers are made
-// opaque to the compiler, and no memory access may cross this point, so an
-// unrolled sweep issues its loads a group of kGroup steps at a time (one
-// memory latency per group) instead of computing every step's addresses and
-// loads up front (which would hold a whole segment's operands in
-// registers).
-template <typename T>
-__device__ __forceinline__ void bwd_step_ptrs(BwdPtrs<T>& q, int steps) {
-    q.u += steps * q.s_tc;
-    q.dt += steps * q.s_tc;
-    q.lam += steps * q.s_tc;
-    q.dy += steps * q.s_tc;
-    q.th += steps * q.s_th;
-    q.B += steps * q.s_bn;
-    q.C += steps * q.s_bn;
-    asm volatile("" : "+v"(q.u), "+v"(q.dt), "+v"(q.lam), "+v"(q.dy), "+v"(q.th), "+v"(q.B), "+v"(q.C)::"memory");
-}
-
-template <typename T, bool CPLX>
-__device__ __forceinline__ BwdPtrs<T> bwd_ptrs(const BwdParams& p, const BwdLane& l, int64_t t0) {
-    const int64_t L = p.seqlen, D = p.dim, N = p.dstate, cw = CPLX ? 2 : 1;
-    const int64_t tc = (l.b * L + t0) * D + l.d;
-    const int64_t bn = ((l.b * L + t0) * N + l.nc) * cw;
-    BwdPtrs<T> q;
+template <typename T, bool CPLX, int LPC>
+__device__ __forceinline__ BwdPtr<T> bwd_ptr(const BwdParams& p, const BwdGeo<LPC>& g, int64_t t) {
+    const int64_t tc = (g.b * p.seqlen + t) * p.dim + g.d;
+    const int64_t th = tc * p.dstate + g.nc;
+    const int64_t bn = ((g.b * p.seqlen + t) * p.dstate + g.nc) * (CPLX ? 2 : 1);
+    BwdPtr<T> q;
     q.u = static_cast<const T*>(p.u) + tc;
     q.dt = static_cast<const T*>(p.delta) + tc;
-    q.lam = p.lambda ? static_cast<const T*>(p.lambda) + tc : q.u;
-    // without theta the rotation is zero: read u's element and mask it
-    q.th = p.theta ? static_cast<const T*>(p.theta) + tc * N + l.nc : q.u;
+    q.lam = p.lambda ? static_cast<const T*>(p.lambda) + tc : q.dt;
+    q.dy = static_cast<const T*>(p.dy) + tc;
+    q.th = p.theta ? static_cast<const T*>(p.theta) + th : q.dt;  // no theta: read delta, ignore it
     q.B = static_cast<const T*>(p.B) + bn;
     q.C = static_cast<const T*>(p.C) + bn;
-    q.dy = p.dy ? static_cast<const T*>(p.dy) + tc : q.u;
-    q.s_tc = static_cast<int32_t>(D);
-    q.s_th = p.theta ? static_cast<int32_t>(D * N) : static_cast<int32_t>(D);
-    q.s_bn = static_cast<int32_t>(N * cw);
+    q.du = p.du + tc;
+    q.ddt = p.ddelta + tc;
+    q.dlam = p.dlambda ? p.dlambda + tc : p.ddelta + tc;
+    q.dth = p.dtheta ? p.dtheta + th : p.ddelta + tc;
+    q.dB = p.dB + bn;
+    q.dC = p.dC + bn;
     return q;
 }
 
-// The loaded (unmasked) values of one step of a segment.
+template <bool CPLX>
+__device__ __forceinline__ BwdStride bwd_stride(const BwdParams& p) {
+    return BwdStride{p.dim, p.theta ? p.dim * p.dstate : p.dim, p.dstate * (CPLX ? 2 : 1)};
+}
+
+// Loaded operands of one step (raw bits).
+template <bool CPLX>
 struct BwdRaw {
-    float x, dt, lam, th, br, bi, cr, ci, dy;
+    uint32_t x, dt, lam, th, br, bi, cr, ci, dy;
 };
 
-// Loads of step k of the segment (k may be -1 for the step before it; any k
-// given must be a valid step).
-template <typename T, int DISC, bool CPLX>
-__device__ __forceinline__ BwdRaw bwd_raw(const BwdPtrs<T>& q, int k, bool with_dy) {
-    using E = Elem<T>;
-    BwdRaw r;
-    r.x = E::load(q.u, k * q.s_tc);
-    r.dt = E::load(q.dt, k * q.s_tc);
-    r.lam = DISC == kTrap ? E::load(q.lam, k * q.s_tc) : 0.f;
-    r.dy = with_dy ? E::load(q.dy, k * q.s_tc) : 0.f;
-    r.bi = r.ci = r.th = 0.f;
-    if constexpr (CPLX) {
-        r.br = E::load(q.B, k * q.s_bn);
-        r.bi = E::load(q.B, k * q.s_bn + 1);
-        r.cr = E::load(q.C, k * q.s_bn);
-        r.ci = E::load(q.C, k * q.s_bn + 1);
-        r.th = E::load(q.th, k * q.s_th);
+// the operands of step k steps after q's (FWD: what the forward recurrence
+// needs; else what the reverse step needs)
+template <typename T, int DISC, bool CPLX, bool FWD>
+__device__ __forceinline__ void bwd_load(const BwdPtr<T>& q, const BwdStride& st, int k, BwdRaw<CPLX>& r) {
+    const int64_t tc = k * st.tc, bn = k * st.bn;
+    r.x = bwd_bits(q.u, tc);
+    r.dt = bwd_bits(q.dt, tc);
+    if constexpr (DISC == kTrap) r.lam = bwd_bits(q.lam, tc);
+    r.br = bwd_bits(q.B, bn);
+    if constexpr (CPLX) r.bi = bwd_bits(q.B, bn + 1);
+    if constexpr (FWD) {
+        if constexpr (CPLX) r.th = bwd_bits(q.th, k * st.th);
     } else {
-        r.br = E::load(q.B, k * q.s_bn);
-        r.cr = E::load(q.C, k * q.s_bn);
+        r.dy = bwd_bits(q.dy, tc);
+        r.cr = bwd_bits(q.C, bn);
+        if constexpr (CPLX) r.ci = bwd_bits(q.C, bn + 1);
     }
-    return r;
 }
 
-// Operands of a step from its loaded values; act = false masks the step.
+// alpha of a step (ZOH, real: (rho, e^z - 1) instead of (re, im))
 template <typename T, int DISC, bool CPLX>
-__device__ __forceinline__ BwdStep bwd_cook(const BwdParams& p, const BwdRaw& r, const BwdLane& l, float a_lane,
-                                            bool act) {
+__device__ __forceinline__ float2 bwd_alpha(float dt, uint32_t th_raw, float a, float a2) {
     constexpr int SC = std::is_same_v<T, uint16_t> ? kSinCosHw : kSinCosWide;
-    const bool cm = l.ch_ok && act, om = l.ok && act;
-    BwdStep s;
-    s.x = cm ? r.x : 0.f;
-    s.dt = cm ? r.dt : 0.f;
-    s.lam = cm ? r.lam : 0.f;
-    s.a = om ? a_lane : 0.f;
-    s.br = om ? r.br : 0.f;
-    s.bi = om ? r.bi : 0.f;
-    s.cr = om ? r.cr : 0.f;
-    s.ci = om ? r.ci : 0.f;
-    const float th = (om && p.theta) ? r.th : 0.f;
-    s.em1 = 0.f;
-    if constexpr (DISC == kZOH)
-        exp_expm1(s.dt * s.a, s.dt * prep_A(s.a), &s.rho, &s.em1);
-    else
-        s.rho = exp_dA(s.dt, prep_A(s.a));
-    s.ar = s.rho;
-    s.ai = 0.f;
-    if constexpr (CPLX) {
-        float sn, cs;
-        sin_cos<SC>(th, &sn, &cs);
-        s.ar = s.rho * cs;
-        s.ai = s.rho * sn;
-    }
-    return s;
-}
-
-template <typename T, int DISC, bool CPLX>
-__device__ __forceinline__ BwdStep bwd_load(const BwdParams& p, const BwdPtrs<T>& q, const BwdLane& l, float a_lane,
-                                            int k, bool act) {
-    return bwd_cook<T, DISC, CPLX>(p, bwd_raw<T, DISC, CPLX>(q, k, false), l, a_lane, act);
-}
-
-// q = B u of step k of the segment (no transcendental); zero when masked
-template <typename T, bool CPLX>
-__device__ __forceinline__ void bwd_q(const BwdPtrs<T>& q, const BwdLane& l, int k, bool act, float* qr,
-                                      float* qi) {
-    using E = Elem<T>;
-    const float x = E::load(q.u, k * q.s_tc);
-    const bool om = l.ok && act;
-    const float br = E::load(q.B, k * q.s_bn);
-    const float bi = CPLX ? E::load(q.B, k * q.s_bn + 1) : 0.f;
-    *qr = om ? br * x : 0.f;
-    *qi = om ? bi * x : 0.f;
-}
-
-// b-term of a step from its operands and q_{t-1} = (qpr, qpi)
-template <int DISC>
-__device__ __forceinline__ void bwd_bterm(const BwdStep& s, float qpr, float qpi, float* br, float* bi) {
-    const float qr = s.br * s.x, qi = s.bi * s.x;
     if constexpr (DISC == kZOH) {
-        const float k = s.a != 0.f ? s.em1 / s.a : s.dt;
+        float rho, em1;
+        exp_expm1(dt * a, dt * a2, &rho, &em1);
+        return make_float2(rho, em1);
+    } else {
+        const float rho = exp_dA(dt, a2);
+        if constexpr (CPLX) {
+            float sn, cs;
+            sin_cos<SC>(bwd_f<T>(th_raw), &sn, &cs);
+            return make_float2(rho * cs, rho * sn);
+        } else {
+            return make_float2(rho, 0.f);
+        }
+    }
+}
+
+// b-term from q_t = (qr, qi), q_{t-1} = (qpr, qpi) and alpha
+template <int DISC>
+__device__ __forceinline__ void bwd_bterm(float dt, float lam, float a, float2 al, float qr, float qi, float qpr,
+                                          float qpi, float* br, float* bi) {
+    if constexpr (DISC == kZOH) {
+        const float k = a != 0.f ? al.y / a : dt;
         *br = k * qr;
         *bi = k * qi;
     } else if constexpr (DISC == kEuler) {
-        *br = s.dt * qr;
-        *bi = s.dt * qi;
+        *br = dt * qr;
+        *bi = dt * qi;
     } else {
-        const float g = s.lam * s.dt, e = (1.f - s.lam) * s.dt;
-        *br = g * qr + e * (s.ar * qpr - s.ai * qpi);
-        *bi = g * qi + e * (s.ar * qpi + s.ai * qpr);
+        const float g = lam * dt, e = (1.f - lam) * dt;
+        *br = g * qr + e * (al.x * qpr - al.y * qpi);
+        *bi = g * qi + e * (al.x * qpi + al.y * qpr);
     }
 }
 
@@ -278,164 +276,308 @@ __device__ __forceinline__ void bwd_assume_disjoint(const BwdParams& p) {
             if (in[i] && out[o]) __builtin_assume_separate_storage(in[i], out[o]);
 }
 
-template <typename T, int DISC, bool CPLX>
+template <int CTRL>
+__device__ __forceinline__ float bwd_dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over a channel's LPC lanes, every lane receiving it: within rows of 16
+// by DPP (quad swaps, then half-row and row mirrors), then across rows.
+template <int LPC>
+__device__ __forceinline__ float bwd_chan_sum(float v) {
+    v += bwd_dpp<0xB1>(v);   // lanes i ^ 1
+    v += bwd_dpp<0x4E>(v);   // lanes i ^ 2
+    v += bwd_dpp<0x141>(v);  // mirror within 8 lanes
+    v += bwd_dpp<0x140>(v);  // mirror within 16 lanes
+    if constexpr (LPC > 16) {
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+    }
+    return v;
+}
+
+// Forward sweep storing the state before every segment of kSeg steps (the
+// state after the last segment is not needed, so every swept segment is full).
+template <typename T, int DISC, bool CPLX, int LPC>
 __global__ void __launch_bounds__(256) bwd_ckpt_kernel(BwdParams p) {
-    constexpr int kSeg = bwd::kSeg;
-    const BwdLane l = bwd_lane(p);
+    constexpr int kSeg = bwd::kSeg, kG = bwd::kGroup;
+    const BwdGeo<LPC> g = bwd_geo<LPC, CPLX>(p, false);
+    if (g.b >= p.batch) return;  // whole waves
     const int64_t L = p.seqlen, N = p.dstate;
-    const int64_t s0 = (l.b * p.dim + l.d) * N + l.nc;  // (b, d, n)
-    const int64_t plane = p.batch * p.dim * N;           // one snapshot
+    const int64_t s0 = (g.b * p.dim + g.d) * N + g.nc;  // (b, d, n)
+    const int64_t plane = p.batch * p.dim * N;          // one snapshot
     const int64_t nseg = (L + kSeg - 1) / kSeg;
     float hr = 0.f, hi = 0.f, qpr = 0.f, qpi = 0.f;
-    if (l.ok && p.h0) {
+    if (g.ok && p.h0) {
         hr = CPLX ? p.h0[2 * s0] : p.h0[s0];
         hi = CPLX ? p.h0[2 * s0 + 1] : 0.f;
     }
-    const float a_lane = p.A[l.d * N + l.nc];
+    const float a = p.A[g.d * N + g.nc], a2 = prep_A(a);
+    const BwdStride st = bwd_stride<CPLX>(p);
+    const bool has_th = CPLX && p.theta;
+    BwdPtr<T> q = bwd_ptr<T, CPLX>(p, g, 0);
     for (int64_t sg = 0; sg < nseg; ++sg) {
-        const int64_t t0 = sg * kSeg;
-        if (l.ok) {
+        if (g.ok) {
             const int64_t k = sg * plane + s0;
             if constexpr (CPLX) {
-                p.ckpt[2 * k] = hr;
-                p.ckpt[2 * k + 1] = hi;
+                *reinterpret_cast<float2*>(p.ckpt + 2 * k) = make_float2(hr, hi);
             } else {
                 p.ckpt[k] = hr;
             }
         }
-        if (sg == nseg - 1) break;  // the state after the last segment is not needed
-        // a full segment (only the last may be ragged, and it is not swept)
-        const BwdPtrs<T> q = bwd_ptrs<T, CPLX>(p, l, t0);
-#pragma unroll 8
-        for (int k = 0; k < kSeg; ++k) {
-            const BwdStep s = bwd_load<T, DISC, CPLX>(p, q, l, a_lane, k, true);
-            float br, bi;
-            bwd_bterm<DISC>(s, qpr, qpi, &br, &bi);
-            qpr = s.br * s.x;
-            qpi = s.bi * s.x;
-            const float nr = s.ar * hr - s.ai * hi + br;
-            hi = s.ar * hi + s.ai * hr + bi;
-            hr = nr;
+        if (sg == nseg - 1) break;
+#pragma unroll 1
+        for (int g0 = 0; g0 < kSeg; g0 += kG) {
+            BwdRaw<CPLX> rw[kG];
+#pragma unroll
+            for (int j = 0; j < kG; ++j) bwd_load<T, DISC, CPLX, true>(q, st, j, rw[j]);
+            q.u += kG * st.tc, q.dt += kG * st.tc, q.lam += kG * st.tc, q.th += kG * st.th, q.B += kG * st.bn;
+#pragma unroll
+            for (int j = 0; j < kG; ++j) {
+                const float dt = bwd_f<T>(rw[j].dt), x = bwd_f<T>(rw[j].x);
+                const float lam = DISC == kTrap ? bwd_f<T>(rw[j].lam) : 0.f;
+                const float2 al = bwd_alpha<T, DISC, CPLX>(dt, has_th ? rw[j].th : 0u, a, a2);
+                const float qr = bwd_f<T>(rw[j].br) * x, qi = CPLX ? bwd_f<T>(rw[j].bi) * x : 0.f;
+                float br, bi;
+                bwd_bterm<DISC>(dt, lam, a, al, qr, qi, qpr, qpi, &br, &bi);
+                qpr = qr;
+                qpi = qi;
+                const float ar = al.x, ai = DISC == kZOH ? 0.f : al.y;
+                const float nr = ar * hr - ai * hi + br;
+                hi = ar * hi + ai * hr + bi;
+                hr = nr;
+            }
         }
     }
 }
 
-// sum over the channel's lanes (all lanes of the wave take part)
-__device__ __forceinline__ float chan_sum(float v, int lpc) {
-    for (int off = lpc >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+// (Q_c, R_c) of chunk c >= 1: the adjoint swept from zero over the chunk and
+// the product of conj(alpha) over it.
+template <typename T, int DISC, bool CPLX, int LPC>
+__global__ void __launch_bounds__(256) bwd_adj_kernel(BwdParams p) {
+    constexpr int kG = bwd::kGroup;
+    const BwdGeo<LPC> g = bwd_geo<LPC, CPLX>(p, true);
+    if (g.c == 0 || g.c >= p.nchunks) return;  // whole waves
+    const int64_t L = p.seqlen, N = p.dstate;
+    const int64_t t0 = g.c * p.chunk, t1 = t0 + p.chunk < L ? t0 + p.chunk : L;
+    const int nsteps = static_cast<int>(t1 - t0);
+    const float a = p.A[g.d * N + g.nc], a2 = prep_A(a);
+    float Gr = 0.f, Gi = 0.f, Qr = 1.f, Qi = 0.f;
+    const int ngroups = (nsteps + kG - 1) / kG;
+    const BwdStride st = bwd_stride<CPLX>(p);
+    const bool has_th = CPLX && p.theta;
+#pragma unroll 1
+    for (int grp = ngroups - 1; grp >= 0; --grp) {
+        BwdRaw<CPLX> rw[kG];
+        const BwdPtr<T> q = bwd_ptr<T, CPLX>(p, g, t0 + grp * kG);
+#pragma unroll
+        for (int j = 0; j < kG; ++j) {
+            const int k = grp * kG + j;
+            const int64_t kk = (k < nsteps ? k : nsteps - 1) - grp * kG;  // stay inside the chunk
+            rw[j].dt = bwd_bits(q.dt, kk * st.tc);
+            rw[j].dy = bwd_bits(q.dy, kk * st.tc);
+            rw[j].cr = bwd_bits(q.C, kk * st.bn);
+            if constexpr (CPLX) {
+                rw[j].ci = bwd_bits(q.C, kk * st.bn + 1);
+                rw[j].th = bwd_bits(q.th, kk * st.th);
+            }
+        }
+#pragma unroll
+        for (int j = kG - 1; j >= 0; --j) {
+            if (grp * kG + j >= nsteps) continue;  // uniform: past the chunk's end
+            const float2 al = bwd_alpha<T, DISC, CPLX>(bwd_f<T>(rw[j].dt), has_th ? rw[j].th : 0u, a, a2);
+            const float ar = al.x, ai = DISC == kZOH ? 0.f : al.y;
+            const float dy = bwd_f<T>(rw[j].dy);
+            Gr += dy * bwd_f<T>(rw[j].cr);  // dy conj(C)
+            if constexpr (CPLX) Gi -= dy * bwd_f<T>(rw[j].ci);
+            const float nr = ar * Gr + ai * Gi;  // conj(alpha) G
+            Gi = ar * Gi - ai * Gr;
+            Gr = nr;
+            const float qr = ar * Qr + ai * Qi;  // conj(alpha) Q
+            Qi = ar * Qi - ai * Qr;
+            Qr = qr;
+        }
+    }
+    if (!g.ok) return;
+    float* slot = p.adj + (g.c * p.batch * p.dim * N + (g.b * p.dim + g.d) * N + g.n) * (CPLX ? 4 : 2);
+    if constexpr (CPLX)
+        *reinterpret_cast<float4*>(slot) = make_float4(Qr, Qi, Gr, Gi);
+    else
+        *reinterpret_cast<float2*>(slot) = make_float2(Qr, Gr);
 }
 
-template <typename T, int DISC, bool CPLX>
+// X_c for every chunk, from X = dh_last down: X_{c-1} = Q_c X_c + R_c.  Slot c
+// ends holding X_c (complex (re, im) at offset 0; real at offset 0).
+template <bool CPLX>
+__global__ void __launch_bounds__(256) bwd_adj_carry_kernel(BwdParams p) {
+    constexpr int kW = CPLX ? 4 : 2;
+    const int64_t BDN = p.batch * p.dim * p.dstate;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= BDN) return;
+    float Xr = 0.f, Xi = 0.f;
+    if (p.dh_last) {
+        Xr = CPLX ? p.dh_last[2 * i] : p.dh_last[i];
+        Xi = CPLX ? p.dh_last[2 * i + 1] : 0.f;
+    }
+    for (int64_t c = p.nchunks - 1; c >= 0; --c) {
+        float* slot = p.adj + (c * BDN + i) * kW;
+        float Qr = 0.f, Qi = 0.f, Rr = 0.f, Ri = 0.f;
+        if (c > 0) {
+            if constexpr (CPLX) {
+                const float4 v = *reinterpret_cast<const float4*>(slot);
+                Qr = v.x, Qi = v.y, Rr = v.z, Ri = v.w;
+            } else {
+                const float2 v = *reinterpret_cast<const float2*>(slot);
+                Qr = v.x, Rr = v.y;
+            }
+        }
+        slot[0] = Xr;
+        if constexpr (CPLX) slot[1] = Xi;
+        const float nr = Qr * Xr - Qi * Xi + Rr;
+        Xi = Qr * Xi + Qi * Xr + Ri;
+        Xr = nr;
+    }
+}
+
+// The reverse sweep of one chunk (every chunk in parallel), segment by
+// segment from the last: recompute the segment's states and decays from its
+// snapshot into wave-private LDS, then sweep it backwards.
+template <typename T, int DISC, bool CPLX, int LPC>
 __global__ void __launch_bounds__(256) bwd_main_kernel(BwdParams p) {
-    constexpr int kSeg = bwd::kSeg, kG = bwd::kGroup;
-    // the segment's states h_t, per wave and lane (each wave uses only its own rows)
-    __shared__ float2 s_h[4][kSeg][64];
+    constexpr int kSeg = bwd::kSeg, kG = bwd::kGroup, kCPW = BwdGeo<LPC>::kCPW;
+    __shared__ float2 s_h[4][kSeg][64];  // h_t of the segment
+    __shared__ float2 s_a[4][kSeg][64];  // alpha_t (ZOH: (rho, e^z - 1))
     bwd_assume_disjoint(p);
-    const BwdLane l = bwd_lane(p);
+    const BwdGeo<LPC> g = bwd_geo<LPC, CPLX>(p, true);
+    if (g.c >= p.nchunks) return;  // whole waves; no barrier follows
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int lpc = p.lpc;
     const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
-    const int64_t s0 = (l.b * D + l.d) * N + l.nc;
+    const int64_t s0 = (g.b * D + g.d) * N + g.nc;
     const int64_t plane = p.batch * D * N;
-    const int64_t nseg = (L + kSeg - 1) / kSeg;
-    const float a_lane = p.A[l.d * N + l.nc];
-    const float skip = (l.ch_ok && p.Dskip) ? p.Dskip[l.d] : 0.f;
-    // the wave's channels share one batch row: dB, dC are summed across them first
-    const int64_t wave_ch0 = __shfl(l.ch, 0, 64);
-    const int64_t wave_chl = __shfl(l.ch, 63, 64);
-    const bool one_row = wave_ch0 / D == (wave_chl < p.batch * D ? wave_chl : p.batch * D - 1) / D;
+    const int64_t t_lo = g.c * p.chunk, t_hi = t_lo + p.chunk < L ? t_lo + p.chunk : L;
+    const int64_t sg_lo = t_lo / kSeg, sg_hi = (t_hi + kSeg - 1) / kSeg;
+    const float a = p.A[g.d * N + g.nc], a2 = prep_A(a);
+    const float skip = (g.ch_ok && p.Dskip) ? p.Dskip[g.d] : 0.f;
+    const bool lead = g.n == 0 && g.ch_ok;  // writes the per-(b, t, d) gradients
 
     float Gr = 0.f, Gi = 0.f;    // adjoint of the state after the current step
     float dqr = 0.f, dqi = 0.f;  // gradient reaching q_t from step t+1 (trapezoid)
     float accA = 0.f, accD = 0.f;
-    if (l.ok && p.dh_last) {
-        Gr = CPLX ? p.dh_last[2 * s0] : p.dh_last[s0];
-        Gi = CPLX ? p.dh_last[2 * s0 + 1] : 0.f;
+    if (g.ok) {
+        if (p.nchunks > 1) {  // X_c, from the carry kernel
+            const float* slot = p.adj + (g.c * plane + s0) * (CPLX ? 4 : 2);
+            Gr = slot[0];
+            Gi = CPLX ? slot[1] : 0.f;
+        } else if (p.dh_last) {
+            Gr = CPLX ? p.dh_last[2 * s0] : p.dh_last[s0];
+            Gi = CPLX ? p.dh_last[2 * s0 + 1] : 0.f;
+        }
     }
-    for (int64_t sg = nseg - 1; sg >= 0; --sg) {
+    const BwdStride st = bwd_stride<CPLX>(p);
+    const bool has_th = CPLX && p.theta;
+    if (DISC == kTrap && t_hi < L) {  // step t_hi's term on q_{t_hi - 1}: (1 - lambda) delta X_c
+        const BwdPtr<T> q1 = bwd_ptr<T, CPLX>(p, g, t_hi);
+        const float e1 = (1.f - bwd_f<T>(bwd_bits(q1.lam, 0))) * bwd_f<T>(bwd_bits(q1.dt, 0));
+        dqr = e1 * Gr;
+        dqi = e1 * Gi;
+    }
+
+#pragma unroll 1
+    for (int64_t sg = sg_hi - 1; sg >= sg_lo; --sg) {
         const int64_t t0 = sg * kSeg;
         const int len = static_cast<int>(L - t0 < kSeg ? L - t0 : kSeg);
         // state before the segment, and q_{t0-1} for the trapezoid
         float hpr = 0.f, hpi = 0.f;
-        if (l.ok) {
+        {
             const int64_t k = sg * plane + s0;
-            hpr = CPLX ? p.ckpt[2 * k] : p.ckpt[k];
-            hpi = CPLX ? p.ckpt[2 * k + 1] : 0.f;
+            if constexpr (CPLX) {
+                const float2 v = *reinterpret_cast<const float2*>(p.ckpt + 2 * k);
+                hpr = v.x, hpi = v.y;
+            } else {
+                hpr = p.ckpt[k];
+            }
         }
-        const BwdPtrs<T> q = bwd_ptrs<T, CPLX>(p, l, t0);
+        const BwdPtr<T> qs = bwd_ptr<T, CPLX>(p, g, t0);  // the segment's first step
         float q0r = 0.f, q0i = 0.f;
-        if (DISC == kTrap && t0 > 0) bwd_q<T, CPLX>(q, l, -1, true, &q0r, &q0i);
+        if (DISC == kTrap && t0 > 0) {
+            const float x = bwd_f<T>(bwd_bits(qs.u, -st.tc));
+            q0r = bwd_f<T>(bwd_bits(qs.B, -st.bn)) * x;
+            if constexpr (CPLX) q0i = bwd_f<T>(bwd_bits(qs.B, -st.bn + 1)) * x;
+        }
 
-        // forward over the segment, kG steps per load group: h_t into LDS
-        // (steps past the end are masked and leave the state unchanged)
+        // forward over the segment: h_t and alpha_t into LDS (steps past the
+        // end are not computed: the last segment of the sequence may be short)
         {
             float hr = hpr, hi = hpi, qpr = q0r, qpi = q0i;
-            BwdPtrs<T> qf = q;
+#pragma unroll 1
+            for (int g0 = 0; g0 < len; g0 += kG) {
+                BwdRaw<CPLX> rw[kG];
 #pragma unroll
-            for (int g0 = 0; g0 < kSeg; g0 += kG) {
-                if (g0 > 0) bwd_step_ptrs(qf, kG);
-                BwdRaw rw[kG];
-#pragma unroll
-                for (int j = 0; j < kG; ++j) rw[j] = bwd_raw<T, DISC, CPLX>(qf, (g0 + j < len ? g0 + j : len - 1) - g0, false);
+                for (int j = 0; j < kG; ++j) bwd_load<T, DISC, CPLX, true>(qs, st, g0 + j < len ? g0 + j : len - 1, rw[j]);
 #pragma unroll
                 for (int j = 0; j < kG; ++j) {
-                    const BwdStep st = bwd_cook<T, DISC, CPLX>(p, rw[j], l, a_lane, g0 + j < len);
+                    if (g0 + j >= len) break;  // uniform
+                    const float dt = bwd_f<T>(rw[j].dt), x = bwd_f<T>(rw[j].x);
+                    const float lam = DISC == kTrap ? bwd_f<T>(rw[j].lam) : 0.f;
+                    const float2 al = bwd_alpha<T, DISC, CPLX>(dt, has_th ? rw[j].th : 0u, a, a2);
+                    const float qr = bwd_f<T>(rw[j].br) * x, qi = CPLX ? bwd_f<T>(rw[j].bi) * x : 0.f;
                     float br, bi;
-                    bwd_bterm<DISC>(st, qpr, qpi, &br, &bi);
-                    qpr = st.br * st.x;
-                    qpi = st.bi * st.x;
-                    const float nr = st.ar * hr - st.ai * hi + br;
-                    hi = st.ar * hi + st.ai * hr + bi;
+                    bwd_bterm<DISC>(dt, lam, a, al, qr, qi, qpr, qpi, &br, &bi);
+                    qpr = qr;
+                    qpi = qi;
+                    const float ar = al.x, ai = DISC == kZOH ? 0.f : al.y;
+                    const float nr = ar * hr - ai * hi + br;
+                    hi = ar * hi + ai * hr + bi;
                     hr = nr;
                     s_h[w][g0 + j][lane] = make_float2(hr, hi);
+                    s_a[w][g0 + j][lane] = al;
                 }
             }
         }
 
-        // reverse sweep over the segment, one load group at a time (masked
-        // steps change nothing and store nothing)
-        BwdPtrs<T> qv = q;
-        bwd_step_ptrs(qv, kSeg - kG);
-        float2 hnext = s_h[w][kSeg - 1][lane];  // h_t of the step being processed
+        // reverse over the segment, one load group at a time
+        const int glast = (len - 1) / kG * kG;
+#pragma unroll 1
+        for (int g0 = glast; g0 >= 0; g0 -= kG) {
+            BwdRaw<CPLX> rw[kG];
 #pragma unroll
-        for (int g0 = kSeg - kG; g0 >= 0; g0 -= kG) {
-            if (g0 < kSeg - kG) bwd_step_ptrs(qv, -kG);
-            BwdRaw rw[kG];
-#pragma unroll
-            for (int j = 0; j < kG; ++j) rw[j] = bwd_raw<T, DISC, CPLX>(qv, (g0 + j < len ? g0 + j : len - 1) - g0, true);
+            for (int j = 0; j < kG; ++j) bwd_load<T, DISC, CPLX, false>(qs, st, g0 + j < len ? g0 + j : len - 1, rw[j]);
             // q_{t-1} of the group's first step: the step before the group
             float qbr = q0r, qbi = q0i;
-            if (DISC == kTrap && g0 > 0)
-                bwd_q<T, CPLX>(qv, l, g0 - 1 < len ? -1 : len - 1 - g0, g0 - 1 < len, &qbr, &qbi);
+            if (DISC == kTrap && g0 > 0) {
+                const float x = bwd_f<T>(bwd_bits(qs.u, (g0 - 1) * st.tc));
+                qbr = bwd_f<T>(bwd_bits(qs.B, (g0 - 1) * st.bn)) * x;
+                if constexpr (CPLX) qbi = bwd_f<T>(bwd_bits(qs.B, (g0 - 1) * st.bn + 1)) * x;
+            }
 #pragma unroll
             for (int j = kG - 1; j >= 0; --j) {
                 const int k = g0 + j;
-                const bool act = k < len;
-                const int64_t t = t0 + (act ? k : len - 1);
-                const int64_t tc = (l.b * L + t) * D + l.d;
-                const BwdStep s = bwd_cook<T, DISC, CPLX>(p, rw[j], l, a_lane, act);
-                const float g = (l.ch_ok && act) ? rw[j].dy : 0.f;
-                const float htr = hnext.x, hti = hnext.y;
-                const float2 hprev = k > 0 ? s_h[w][k - 1][lane] : make_float2(hpr, hpi);
-                hnext = hprev;
-                const float hpr_t = hprev.x, hpi_t = hprev.y;
+                if (k >= len) continue;  // uniform
+                const float dt = bwd_f<T>(rw[j].dt), x = bwd_f<T>(rw[j].x);
+                const float lam = DISC == kTrap ? bwd_f<T>(rw[j].lam) : 0.f;
+                const float dy = g.ch_ok ? bwd_f<T>(rw[j].dy) : 0.f;
+                const float br = bwd_f<T>(rw[j].br), bi = CPLX ? bwd_f<T>(rw[j].bi) : 0.f;
+                const float cr = bwd_f<T>(rw[j].cr), ci = CPLX ? bwd_f<T>(rw[j].ci) : 0.f;
+                const float2 al = s_a[w][k][lane];
+                const float ar = al.x, ai = DISC == kZOH ? 0.f : al.y;
+                const float2 ht = s_h[w][k][lane];
+                const float2 hp = k > 0 ? s_h[w][k - 1][lane] : make_float2(hpr, hpi);
                 // y_t = Re(C h_t) + D u_t
-                Gr += g * s.cr;
-                Gi -= g * s.ci;
-                float gCr = g * htr, gCi = -g * hti;
-                if (!l.ok) gCr = gCi = 0.f;
+                Gr += dy * cr;
+                Gi -= dy * ci;
+                float gCr = dy * ht.x, gCi = -dy * ht.y;
                 // h_t = alpha h_{t-1} + bterm:  dalpha = conj(h_{t-1}) G
-                float gar = hpr_t * Gr + hpi_t * Gi, gai = hpr_t * Gi - hpi_t * Gr;
+                float gar = hp.x * Gr + hp.y * Gi, gai = hp.x * Gi - hp.y * Gr;
                 float gqr = dqr, gqi = dqi;
                 float gdt = 0.f, glam = 0.f;
-                const float qr = s.br * s.x, qi = s.bi * s.x;
+                const float qr = br * x, qi = bi * x;
                 if constexpr (DISC == kZOH) {
-                    const float kap = s.a != 0.f ? s.em1 / s.a : s.dt;
+                    const float rho = al.x, em1 = al.y;
+                    const float kap = a != 0.f ? em1 / a : dt;
                     gqr += kap * Gr;
                     gqi += kap * Gi;
                     const float gk = Gr * qr + Gi * qi;
-                    const float z = s.dt * s.a;
+                    const float z = dt * a;
                     // d kappa / dA = (delta e^z - kappa)/A = delta^2 sum_m z^m (m+1)/(m+2)!; the
                     // closed form cancels for small z, so |z| < 1/2 takes the series (to m = 6:
                     // truncation below 4e-7 relative)
@@ -444,88 +586,82 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(BwdParams p) {
                         z * (1.f / 3.f +
                              z * (1.f / 8.f +
                                   z * (1.f / 30.f + z * (1.f / 144.f + z * (1.f / 840.f + z * (1.f / 5760.f))))));
-                    const float dk = fabsf(z) < 0.5f ? s.dt * s.dt * ser : (s.dt * s.rho - kap) / s.a;
-                    gdt += gk * s.rho;
+                    const float dk = fabsf(z) < 0.5f ? dt * dt * ser : (dt * rho - kap) / a;
+                    gdt += gk * rho;
                     accA += gk * dk;
                 } else if constexpr (DISC == kEuler) {
-                    gqr += s.dt * Gr;
-                    gqi += s.dt * Gi;
+                    gqr += dt * Gr;
+                    gqi += dt * Gi;
                     gdt += Gr * qr + Gi * qi;
                 } else {
                     // q_{t-1}: from the previous step's loads, or the step before the group
-                    const bool om = l.ok && act;
-                    const float qpr = j > 0 ? (om ? rw[j - 1].br * rw[j - 1].x : 0.f) : (act ? qbr : 0.f);
-                    const float qpi = j > 0 ? (om ? rw[j - 1].bi * rw[j - 1].x : 0.f) : (act ? qbi : 0.f);
-                    const float aqr = s.ar * qpr - s.ai * qpi, aqi = s.ar * qpi + s.ai * qpr;  // alpha q_{t-1}
-                    const float e = (1.f - s.lam) * s.dt;
-                    gqr += s.lam * s.dt * Gr;
-                    gqi += s.lam * s.dt * Gi;
-                    glam += Gr * (s.dt * qr - s.dt * aqr) + Gi * (s.dt * qi - s.dt * aqi);
-                    gdt += Gr * (s.lam * qr + (1.f - s.lam) * aqr) + Gi * (s.lam * qi + (1.f - s.lam) * aqi);
+                    float qpr = qbr, qpi = qbi;
+                    if (j > 0) {
+                        const float xp = bwd_f<T>(rw[j - 1].x);
+                        qpr = bwd_f<T>(rw[j - 1].br) * xp;
+                        qpi = CPLX ? bwd_f<T>(rw[j - 1].bi) * xp : 0.f;
+                    }
+                    const float aqr = ar * qpr - ai * qpi, aqi = ar * qpi + ai * qpr;  // alpha q_{t-1}
+                    const float e = (1.f - lam) * dt;
+                    gqr += lam * dt * Gr;
+                    gqi += lam * dt * Gi;
+                    glam += Gr * (dt * qr - dt * aqr) + Gi * (dt * qi - dt * aqi);
+                    gdt += Gr * (lam * qr + (1.f - lam) * aqr) + Gi * (lam * qi + (1.f - lam) * aqi);
                     gar += e * (qpr * Gr + qpi * Gi);  // conj(e q_{t-1}) G
                     gai += e * (qpr * Gi - qpi * Gr);
-                    dqr = e * (s.ar * Gr + s.ai * Gi);  // conj(e alpha) G, to q_{t-1}
-                    dqi = e * (s.ar * Gi - s.ai * Gr);
+                    dqr = e * (ar * Gr + ai * Gi);  // conj(e alpha) G, to q_{t-1}
+                    dqi = e * (ar * Gi - ai * Gr);
                 }
                 // q_t = B_t u_t
-                float gBr = s.x * gqr, gBi = s.x * gqi;
-                float gu = gqr * s.br + gqi * s.bi;
-                // alpha = exp(z + i theta): P = conj(dalpha) alpha
-                const float Pr = gar * s.ar + gai * s.ai, Pi = gar * s.ai - gai * s.ar;
-                gdt += Pr * s.a;
-                accA += Pr * s.dt;
+                float gBr = x * gqr, gBi = x * gqi;
+                float gu = gqr * br + gqi * bi;
+                // alpha = exp(z + i theta): P = conj(dalpha) alpha (ZOH: the real decay rho)
+                const float Pr = gar * ar + gai * ai, Pi = gar * ai - gai * ar;
+                gdt += Pr * a;
+                accA += Pr * dt;
                 // to h_{t-1}: G = conj(alpha) G
                 {
-                    const float nr = s.ar * Gr + s.ai * Gi;
-                    Gi = s.ar * Gi - s.ai * Gr;
+                    const float nr = ar * Gr + ai * Gi;
+                    Gi = ar * Gi - ai * Gr;
                     Gr = nr;
                 }
-                if (!l.ok) gu = gdt = glam = gBr = gBi = 0.f;
+                if (!g.ok) gu = gdt = glam = gBr = gBi = gCr = gCi = 0.f;
                 // per (b, t, d): sums over the channel's states
-                gu = chan_sum(gu, lpc);
-                gdt = chan_sum(gdt, lpc);
-                if constexpr (DISC == kTrap) glam = chan_sum(glam, lpc);
-                if (!act) continue;  // uniform: a masked step has nothing to store
-                if (CPLX && p.dtheta && l.ok) p.dtheta[tc * N + l.n] = -Pi;
-                if (l.n == 0 && l.ch_ok) {
-                    p.du[tc] = gu + g * skip;
-                    p.ddelta[tc] = gdt;
-                    if constexpr (DISC == kTrap) p.dlambda[tc] = glam;
-                    accD += g * s.x;
+                gu = bwd_chan_sum<LPC>(gu);
+                gdt = bwd_chan_sum<LPC>(gdt);
+                if constexpr (DISC == kTrap) glam = bwd_chan_sum<LPC>(glam);
+                const int64_t otc = k * st.tc, obn = k * st.bn;
+                if (CPLX && p.dtheta && g.ok) qs.dth[k * st.th] = -Pi;
+                if (lead) {
+                    qs.du[otc] = gu + dy * skip;
+                    qs.ddt[otc] = gdt;
+                    if constexpr (DISC == kTrap) qs.dlam[otc] = glam;
+                    accD += dy * x;
                 }
-                // per (b, t, n): sums over channels
-                const int64_t bn = (l.b * L + t) * N + l.n;
-                if (one_row) {
-                    for (int off = lpc; off < 64; off <<= 1) {
-                        gBr += __shfl_xor(gBr, off, 64);
-                        gCr += __shfl_xor(gCr, off, 64);
-                        if constexpr (CPLX) {
-                            gBi += __shfl_xor(gBi, off, 64);
-                            gCi += __shfl_xor(gCi, off, 64);
-                        }
-                    }
-                    if (lane < lpc && l.ok) {
-                        atomicAdd(&p.dB[CPLX ? 2 * bn : bn], gBr);
-                        atomicAdd(&p.dC[CPLX ? 2 * bn : bn], gCr);
-                        if constexpr (CPLX) {
-                            atomicAdd(&p.dB[2 * bn + 1], gBi);
-                            atomicAdd(&p.dC[2 * bn + 1], gCi);
-                        }
-                    }
-                } else if (l.ok) {
-                    atomicAdd(&p.dB[CPLX ? 2 * bn : bn], gBr);
-                    atomicAdd(&p.dC[CPLX ? 2 * bn : bn], gCr);
+                // per (b, t, n): sums over the wave's channels, then one atomic per wave
+#pragma unroll
+                for (int off = LPC; off < 64; off <<= 1) {
+                    gBr += __shfl_xor(gBr, off, 64);
+                    gCr += __shfl_xor(gCr, off, 64);
                     if constexpr (CPLX) {
-                        atomicAdd(&p.dB[2 * bn + 1], gBi);
-                        atomicAdd(&p.dC[2 * bn + 1], gCi);
+                        gBi += __shfl_xor(gBi, off, 64);
+                        gCi += __shfl_xor(gCi, off, 64);
+                    }
+                }
+                if (lane < LPC && g.n < N) {
+                    atomicAdd(qs.dB + obn, gBr);
+                    atomicAdd(qs.dC + obn, gCr);
+                    if constexpr (CPLX) {
+                        atomicAdd(qs.dB + obn + 1, gBi);
+                        atomicAdd(qs.dC + obn + 1, gCi);
                     }
                 }
             }
         }
     }
-    if (l.ok) {
-        atomicAdd(&p.dA[l.d * N + l.n], accA);
-        if (p.dh0) {
+    if (g.ok) {
+        atomicAdd(&p.dA[g.d * N + g.n], accA);
+        if (p.dh0 && g.c == 0) {
             if constexpr (CPLX) {
                 p.dh0[2 * s0] = Gr;
                 p.dh0[2 * s0 + 1] = Gi;
@@ -534,7 +670,8 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(BwdParams p) {
             }
         }
     }
-    if (l.n == 0 && l.ch_ok && p.dD) atomicAdd(&p.dD[l.d], accD);
+    if (lead && p.dD) atomicAdd(&p.dD[g.d], accD);
+    (void)kCPW;
 }
 
 }  // namespace ssm

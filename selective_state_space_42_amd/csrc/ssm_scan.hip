@@ -117,43 +117,93 @@ int launch_step(const ssm_scan_desc_t* d, const ssm::StepParams& p, hipStream_t 
     return pairs ? launch_step_k<T, true>(d, p, s) : launch_step_k<T, false>(d, p, s);
 }
 
-template <typename T, int DISC, bool CPLX>
-void launch_bwd_pair(const ssm::BwdParams& p, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((ssm::bwd_ckpt_kernel<T, DISC, CPLX>), grid, dim3(256), 0, s, p);
-    hipLaunchKernelGGL((ssm::bwd_main_kernel<T, DISC, CPLX>), grid, dim3(256), 0, s, p);
+// grid: one copy of the channel waves (the checkpoint sweep) and one per time
+// chunk (the adjoint and reverse sweeps)
+template <typename T, int DISC, bool CPLX, int LPC>
+void launch_bwd_kernels(const ssm::BwdParams& p, dim3 grid, dim3 chunk_grid, hipStream_t s) {
+    hipLaunchKernelGGL((ssm::bwd_ckpt_kernel<T, DISC, CPLX, LPC>), grid, dim3(256), 0, s, p);
+    if (p.nchunks > 1) {
+        hipLaunchKernelGGL((ssm::bwd_adj_kernel<T, DISC, CPLX, LPC>), chunk_grid, dim3(256), 0, s, p);
+        const int64_t bdn = p.batch * p.dim * p.dstate;
+        hipLaunchKernelGGL((ssm::bwd_adj_carry_kernel<CPLX>), dim3(static_cast<unsigned>((bdn + 255) / 256)),
+                           dim3(256), 0, s, p);
+    }
+    hipLaunchKernelGGL((ssm::bwd_main_kernel<T, DISC, CPLX, LPC>), chunk_grid, dim3(256), 0, s, p);
+}
+
+template <typename T, int LPC>
+void launch_bwd_modes(const ssm_scan_desc_t* d, const ssm::BwdParams& p, dim3 grid, dim3 cgrid, hipStream_t s) {
+    if (d->is_complex) {
+        if (d->disc == SSM_DISC_EXP_EULER)
+            launch_bwd_kernels<T, ssm::kEuler, true, LPC>(p, grid, cgrid, s);
+        else
+            launch_bwd_kernels<T, ssm::kTrap, true, LPC>(p, grid, cgrid, s);
+    } else {
+        if (d->disc == SSM_DISC_ZOH)
+            launch_bwd_kernels<T, ssm::kZOH, false, LPC>(p, grid, cgrid, s);
+        else if (d->disc == SSM_DISC_EXP_EULER)
+            launch_bwd_kernels<T, ssm::kEuler, false, LPC>(p, grid, cgrid, s);
+        else
+            launch_bwd_kernels<T, ssm::kTrap, false, LPC>(p, grid, cgrid, s);
+    }
+}
+
+// lanes per channel of the backward kernels: 16 (N <= 16) or 64
+int bwd_lpc(const ssm_scan_desc_t* d) { return d->dstate <= 16 ? 16 : 64; }
+
+// waves per time chunk: 64 / lpc channels of one batch row per wave
+int64_t bwd_waves(const ssm_scan_desc_t* d) {
+    const int64_t cpw = 64 / bwd_lpc(d);
+    return d->batch * ((d->dim + cpw - 1) / cpw);
 }
 
 template <typename T>
 int launch_bwd(const ssm_scan_desc_t* d, const ssm::BwdParams& p, hipStream_t s) {
-    const int64_t waves = (d->batch * d->dim + (64 / p.lpc) - 1) / (64 / p.lpc);
-    const int64_t blocks = (waves + 3) / 4;
-    if (blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+    const int64_t waves = bwd_waves(d);
+    const int64_t blocks = (waves + 3) / 4, chunk_blocks = (waves * p.nchunks + 3) / 4;
+    if (chunk_blocks > INT32_MAX || (d->batch * d->dim * d->dstate + 255) / 256 > INT32_MAX)
+        return SSM_ERR_UNSUPPORTED;
     const int64_t cw = d->is_complex ? 2 : 1;
     const int64_t na = d->dim * d->dstate, nb = d->batch * d->seqlen * d->dstate * cw, nd = p.dD ? d->dim : 0;
     int64_t zb = (na + 2 * nb + nd + 255) / 256;
     if (zb > 16384) zb = 16384;
     hipLaunchKernelGGL(ssm::bwd_zero_kernel, dim3(static_cast<unsigned>(zb)), dim3(256), 0, s, p.dA, na, p.dB, nb,
                        p.dC, nb, p.dD, nd);
-    const dim3 grid(static_cast<unsigned>(blocks));
-    if (d->is_complex) {
-        if (d->disc == SSM_DISC_EXP_EULER)
-            launch_bwd_pair<T, ssm::kEuler, true>(p, grid, s);
-        else
-            launch_bwd_pair<T, ssm::kTrap, true>(p, grid, s);
-    } else {
-        if (d->disc == SSM_DISC_ZOH)
-            launch_bwd_pair<T, ssm::kZOH, false>(p, grid, s);
-        else if (d->disc == SSM_DISC_EXP_EULER)
-            launch_bwd_pair<T, ssm::kEuler, false>(p, grid, s);
-        else
-            launch_bwd_pair<T, ssm::kTrap, false>(p, grid, s);
-    }
+    const dim3 grid(static_cast<unsigned>(blocks)), cgrid(static_cast<unsigned>(chunk_blocks));
+    if (p.lpc == 16)
+        launch_bwd_modes<T, 16>(d, p, grid, cgrid, s);
+    else
+        launch_bwd_modes<T, 64>(d, p, grid, cgrid, s);
     return hip_status(hipGetLastError());
 }
 
-size_t bwd_workspace(const ssm_scan_desc_t* d) {
+// Time chunks of the reverse sweep: as many (of at least 256 steps, whole
+// segments) as it takes to give the GPU about 2^19 lanes, eight waves per
+// SIMD on 256 compute units; one chunk for a problem that wide on its own.
+void bwd_chunking(const ssm_scan_desc_t* d, int64_t* chunk, int64_t* nchunks) {
+    constexpr int64_t kTargetLanes = int64_t(1) << 19, kMinChunk = 256;
+    const int64_t lanes = bwd_waves(d) * 64;
+    int64_t want = (kTargetLanes + lanes - 1) / lanes;
+    const int64_t most = (d->seqlen + kMinChunk - 1) / kMinChunk;
+    if (want > most) want = most;
+    if (want < 1) want = 1;
+    int64_t c = (d->seqlen + want - 1) / want;
+    c = (c + ssm::bwd::kSeg - 1) / ssm::bwd::kSeg * ssm::bwd::kSeg;
+    *chunk = c;
+    *nchunks = (d->seqlen + c - 1) / c;
+}
+
+// the snapshots, then the chunk adjoints (when there is more than one chunk)
+size_t bwd_ckpt_bytes(const ssm_scan_desc_t* d) {
     const int64_t nseg = (d->seqlen + ssm::bwd::kSeg - 1) / ssm::bwd::kSeg;
-    return static_cast<size_t>(nseg * d->batch * d->dim * d->dstate * (d->is_complex ? 8 : 4));
+    return static_cast<size_t>(ssm::round256(nseg * d->batch * d->dim * d->dstate * (d->is_complex ? 8 : 4)));
+}
+
+size_t bwd_workspace(const ssm_scan_desc_t* d) {
+    int64_t chunk, n;
+    bwd_chunking(d, &chunk, &n);
+    const int64_t adj = n > 1 ? n * d->batch * d->dim * d->dstate * (d->is_complex ? 16 : 8) : 0;
+    return bwd_ckpt_bytes(d) + static_cast<size_t>(adj);
 }
 
 int check_ssd_desc(const ssm_ssd_desc_t* d) {
@@ -416,8 +466,14 @@ int ssm_scan_bwd(const ssm_scan_desc_t* desc, const void* u, const void* delta, 
     p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB; p.dC = dC; p.dD = dD; p.dtheta = dtheta;
     p.dlambda = dlambda; p.dh0 = dh0;
     p.ckpt = static_cast<float*>(workspace);
+    p.adj = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_ckpt_bytes(desc));
     p.batch = desc->batch; p.seqlen = desc->seqlen; p.dim = desc->dim; p.dstate = desc->dstate;
-    p.lpc = next_pow2(desc->dstate);
+    int64_t chunk, nchunks;
+    bwd_chunking(desc, &chunk, &nchunks);
+    if (nchunks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+    p.chunk = chunk;
+    p.nchunks = static_cast<int32_t>(nchunks);
+    p.lpc = bwd_lpc(desc);
     hipStream_t s = static_cast<hipStream_t>(stream);
     return desc->io_dtype == SSM_DTYPE_F32 ? launch_bwd<float>(desc, p, s) : launch_bwd<uint16_t>(desc, p, s);
 }

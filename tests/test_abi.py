@@ -180,6 +180,12 @@ def test_backward_argument_rules():
     assert call_bwd(d, ws=0) == WS_SMALL
     assert call_bwd(d, ws_bytes=need - 1) == WS_SMALL
     assert call_bwd(d, ws=P + 64, ws_bytes=need) == INVALID            # not 256-byte aligned
+    # a narrow, long problem: 256 segments of snapshots plus 16 chunks of 256 steps, one
+    # (Q, R) adjoint pair each per (b, d, n)
+    d = desc(B=1, L=4096, D=8, N=16, cplx=True)
+    assert scan.ssm_scan_bwd_workspace_bytes(d) == 256 * 8 * 16 * 8 + 16 * 8 * 16 * 16
+    d = desc(B=1, L=4096, D=8, N=16)
+    assert scan.ssm_scan_bwd_workspace_bytes(d) == 256 * 8 * 16 * 4 + 16 * 8 * 16 * 8
 
 
 def call_ssd(desc, u=P, delta=P, A=P, B=P, C=P, D=0, y=P, h=0, ws=P, ws_bytes=1 << 40):
