@@ -36,7 +36,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert scan.ssm_scan_abi_version() == 3
+    header_version = int(re.search(r"#define SSM_SCAN_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert scan.ssm_scan_abi_version() == header_version == scan.ABI_VERSION == 3
     for code, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported configuration"),
                        (3, "workspace too small"), (4, "HIP runtime error"), (99, "unknown status")]:
         assert scan.ssm_scan_status_string(code) == text
