@@ -59,8 +59,8 @@
 namespace ssm {
 
 namespace bwd {
-constexpr int kSeg = 16;  // steps per recompute segment (states kept in LDS)
-constexpr int kGroup = 8;  // steps whose loads are issued together
+constexpr int kSeg = 12;  // steps per recompute segment (states kept in LDS)
+constexpr int kGroup = 4;  // steps whose loads are issued together
 }
 
 struct BwdParams {
