@@ -121,13 +121,27 @@ def mimo_decode_algorithmic_bytes(w) -> int:
             + 2 * 4 * B * D * N * (1 + cplx))             # h read and written
 
 
-def kernel_source_hash() -> str:
+# The device code behind each path, for telling whether committed counters
+# still describe the kernels that run.
+KERNEL_SOURCES = {
+    "chunked": ["kernel_chunked.h"],
+    "sequential": ["kernel_sequential.h"],
+    "step": ["kernel_step.h"],
+    "backward": ["kernel_backward.h"],
+    "ssd": ["kernel_ssd.h"],
+    "mimo": ["kernel_mimo.h", "mimo_launch.h", "mimo.hip"],
+    "mimo_step": ["kernel_mimo.h", "mimo_launch.h", "mimo.hip"],
+}
+
+
+def kernel_source_hash(algo: str) -> str:
+    """Hash of the device sources of one path (its kernel header and the shared
+    device helpers)."""
     csrc = os.path.join(ROOT, "selective_state_space_42_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".h", ".hip")):
-            h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in sorted(KERNEL_SOURCES[algo] + ["device_common.h", "device_math.h"]):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -138,7 +152,7 @@ def traffic_from_profile(workload: str, algo: str):
     except (OSError, ValueError):
         return None
     entry = rec.get(workload, {}).get(algo)
-    if not entry or entry.get("source_hash") != kernel_source_hash():
+    if not entry or entry.get("source_hash") != kernel_source_hash(algo):
         return None
     return entry.get("hbm_bytes_per_launch")
 
