@@ -270,9 +270,9 @@ typedef struct {
     int32_t reserved; /* 0 */
 } ssm_ssd_desc_t;
 
-/* Bytes of workspace ssm_ssd_fwd needs: two fp32 N x headdim states and one
- * decay per (batch, head, 64-step chunk); 0 for an invalid or unsupported
- * descriptor. */
+/* Bytes of workspace ssm_ssd_fwd needs: two bf16 N x headdim states and one
+ * fp32 decay per (batch, head, 64-step chunk); 0 for an invalid or
+ * unsupported descriptor. */
 size_t ssm_ssd_workspace_bytes(const ssm_ssd_desc_t *desc);
 
 /*

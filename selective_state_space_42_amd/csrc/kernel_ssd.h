@@ -27,7 +27,9 @@
 //   ssd_state_kernel  each chunk's local state contribution S_c (N x P) and
 //                     its decay e_c = exp(cum_{Q-1}), all chunks in parallel;
 //   ssd_pass_kernel   the states entering each chunk, H_in(c+1) = e_c H_in(c)
-//                     + S_c, one thread per state element walking the chunks;
+//                     + S_c, one thread per state element walking the chunks
+//                     (the running state in fp32; S and H_in are kept in bf16,
+//                     the precision the output products read H_in in);
 //   ssd_out_kernel    each chunk's outputs from its inputs and H_in(c).
 #pragma once
 
@@ -53,9 +55,9 @@ struct SsdParams {
     const float* Dskip; // [D] or NULL
     void* y;            // [B][L][D]
     float* h_last;      // [B][D][N] or NULL
-    float* S;           // [B][H][nC][N][P]  chunk contributions (workspace)
+    uint16_t* S;        // [B][H][nC][N][P]  chunk contributions, bf16 (workspace)
     float* E;           // [B][H][nC]        chunk decays (workspace)
-    float* Hin;         // [B][H][nC][N][P]  state entering each chunk (workspace)
+    uint16_t* Hin;      // [B][H][nC][N][P]  state entering each chunk, bf16 (workspace)
     int64_t batch, seqlen, dim, dstate, heads, nchunks;
 };
 
@@ -74,6 +76,7 @@ typedef short ssd_bf16x4 __attribute__((ext_vector_type(4)));
 typedef float ssd_f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ uint16_t ssd_bf16(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+__device__ __forceinline__ float ssd_widen(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
 
 // One 32 x 32 block of A . B with K = 8 * ksteps on the bf16 MFMA units, both
 // operands in LDS with k contiguous: a_rows[i][k] (rows i0 ..) and b_cols[j][k]
@@ -162,11 +165,11 @@ __global__ void __launch_bounds__(256) ssd_state_kernel(SsdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
         ssd_mfma_block<kQ + kPad>(s_bw, s_xt, n0, p0, kQ / 8, lane, acc);
-        float* S = p.S + (bh * nC + c) * N * kP;
+        uint16_t* S = p.S + (bh * nC + c) * N * kP;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int n = ssd_acc_row(n0, lane, r);
-            if (n < N) S[n * kP + p0 + (lane & 31)] = acc[r];
+            if (n < N) S[n * kP + p0 + (lane & 31)] = ssd_bf16(acc[r]);
         }
     }
     if (tid == 0) p.E[bh * nC + c] = __builtin_amdgcn_exp2f(s_cum[kQ - 1]);
@@ -178,8 +181,8 @@ __global__ void __launch_bounds__(256) ssd_pass_kernel(SsdParams p) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;  // (b, h, n, pp)
     if (i >= p.batch * H * N * kP) return;
     const int64_t bh = i / (N * kP), np = i % (N * kP);
-    const float* S = p.S + bh * nC * N * kP + np;
-    float* Hin = p.Hin + bh * nC * N * kP + np;
+    const uint16_t* S = p.S + bh * nC * N * kP + np;
+    uint16_t* Hin = p.Hin + bh * nC * N * kP + np;
     const float* E = p.E + bh * nC;
     float st = 0.f;
     int64_t c = 0;
@@ -188,18 +191,18 @@ __global__ void __launch_bounds__(256) ssd_pass_kernel(SsdParams p) {
         float s[8], e[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            s[k] = S[(c + k) * N * kP];
+            s[k] = ssd_widen(S[(c + k) * N * kP]);
             e[k] = E[c + k];
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            Hin[(c + k) * N * kP] = st;
+            Hin[(c + k) * N * kP] = ssd_bf16(st);
             st = fmaf(e[k], st, s[k]);
         }
     }
     for (; c < nC; ++c) {
-        Hin[c * N * kP] = st;
-        st = fmaf(E[c], st, S[c * N * kP]);
+        Hin[c * N * kP] = ssd_bf16(st);
+        st = fmaf(E[c], st, ssd_widen(S[c * N * kP]));
     }
     if (p.h_last) {
         const int64_t b = bh / H, h = bh % H, n = np / kP, pp = np % kP;
@@ -236,10 +239,10 @@ __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
         s_b[t][n] = ok ? ssd_bf16(E::load(Bm, (b * L + t0 + t) * N + n)) : uint16_t(0);
         s_c[t][n] = ok ? ssd_bf16(E::load(Cm, (b * L + t0 + t) * N + n)) : uint16_t(0);
     }
-    const float* Hin = p.Hin + (bh * nC + c) * N * kP;
+    const uint16_t* Hin = p.Hin + (bh * nC + c) * N * kP;
     for (int i = tid; i < npad * kP; i += 256) {
         const int n = i / kP, pp = i % kP;
-        s_ht[pp][n] = n < N ? ssd_bf16(Hin[n * kP + pp]) : uint16_t(0);
+        s_ht[pp][n] = n < N ? Hin[n * kP + pp] : uint16_t(0);
     }
     const float a2 = p.A[h] * kSsdLog2e;  // cumulative decays in log2 units
     if (tid < kQ) {

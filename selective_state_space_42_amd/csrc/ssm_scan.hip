@@ -224,7 +224,7 @@ int check_ssd_desc(const ssm_ssd_desc_t* d) {
 size_t ssd_workspace(const ssm_ssd_desc_t* d) {
     const int64_t H = d->dim / d->headdim, nC = (d->seqlen + ssm::ssd::kQ - 1) / ssm::ssd::kQ;
     const int64_t planes = d->batch * H * nC;
-    return static_cast<size_t>(2 * ssm::round256(planes * d->dstate * d->headdim * 4) + ssm::round256(planes * 4));
+    return static_cast<size_t>(2 * ssm::round256(planes * d->dstate * d->headdim * 2) + ssm::round256(planes * 4));
 }
 
 // Pointer checks shared by the scan and the step: required inputs present,
@@ -505,9 +505,9 @@ int ssm_ssd_fwd(const ssm_ssd_desc_t* desc, const void* u, const void* delta, co
     p.nchunks = (desc->seqlen + ssm::ssd::kQ - 1) / ssm::ssd::kQ;
     const int64_t planes = p.batch * p.heads * p.nchunks;
     char* ws = static_cast<char*>(workspace);
-    const uint64_t plane_bytes = ssm::round256(planes * p.dstate * ssm::ssd::kP * 4);
-    p.S = reinterpret_cast<float*>(ws);
-    p.Hin = reinterpret_cast<float*>(ws + plane_bytes);
+    const uint64_t plane_bytes = ssm::round256(planes * p.dstate * ssm::ssd::kP * 2);
+    p.S = reinterpret_cast<uint16_t*>(ws);
+    p.Hin = reinterpret_cast<uint16_t*>(ws + plane_bytes);
     p.E = reinterpret_cast<float*>(ws + 2 * plane_bytes);
     if (planes > INT32_MAX) return SSM_ERR_UNSUPPORTED;
     const int64_t pass_threads = p.batch * p.heads * p.dstate * ssm::ssd::kP;

@@ -216,7 +216,7 @@ def test_ssd_argument_rules():
     assert call_ssd(ssd_desc(), y=P + 8) == INVALID
     d = ssd_desc(B=2, L=100, D=128, N=16)
     need = scan.ssm_ssd_workspace_bytes(d)
-    assert need == 2 * (2 * 2 * 2 * 16 * 64 * 4) + 256           # 2 rows x 2 heads x 2 chunks
+    assert need == 2 * (2 * 2 * 2 * 16 * 64 * 2) + 256           # 2 rows x 2 heads x 2 chunks, bf16 states
     assert call_ssd(d, ws=0) == WS_SMALL
     assert call_ssd(d, ws_bytes=need - 1) == WS_SMALL
     assert call_ssd(d, ws=P + 64, ws_bytes=need) == INVALID
