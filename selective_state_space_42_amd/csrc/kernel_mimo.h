@@ -480,22 +480,36 @@ __global__ void __launch_bounds__(256) mimo_step_kernel(MimoStepParams p) {
     const int64_t sidx[2] = {ch * N + n0, ch * N + n1};
     const int64_t bn[2] = {(b * N + n0) * R * kCw, (b * N + n1) * R * kCw};
 
+    // Every load is issued up front and without branches: a missing theta
+    // or previous step reads delta's or this step's element instead and is
+    // masked afterwards (a branch around a load would make the compiler wait
+    // for all earlier loads at the join).
+    const float dsk = p.Dskip ? p.Dskip[d] : 0.f;  // the one branch, before the other loads
+    const T* delta = static_cast<const T*>(p.delta);
+    const T* uu = static_cast<const T*>(p.u);
+    const T* Bm = static_cast<const T*>(p.B);
+    const bool has_th = CPLX && p.theta;
+    const bool prev = DISC == kTrap && p.u_prev;
+    const T* thp = has_th ? static_cast<const T*>(p.theta) : nullptr;
+    const T* upp = prev ? static_cast<const T*>(p.u_prev) : uu;
+    const T* bpp = prev ? static_cast<const T*>(p.B_prev) : Bm;
     Run<kES> rdt, rlam, rth[2];
     Run<R * kES> rx, rxp;
     Run<R * kCw * kES> rb[2], rc[2], rbp[2];
-    load_run(static_cast<const T*>(p.delta) + ch, rdt);
-    load_run(static_cast<const T*>(p.u) + ch * R, rx);
-    const bool has_th = CPLX && p.theta;
-    const bool prev = DISC == kTrap && p.u_prev;
-    if (DISC == kTrap) load_run(static_cast<const T*>(p.lambda) + ch, rlam);
-    if (prev) load_run(static_cast<const T*>(p.u_prev) + ch * R, rxp);
+    load_run(delta + ch, rdt);
+    load_run(uu + ch * R, rx);
+    if constexpr (DISC == kTrap) {
+        load_run(static_cast<const T*>(p.lambda) + ch, rlam);
+        load_run(upp + ch * R, rxp);
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        load_run(static_cast<const T*>(p.B) + bn[j], rb[j]);
+        load_run(Bm + bn[j], rb[j]);
         load_run(static_cast<const T*>(p.C) + bn[j], rc[j]);
-        if (has_th) load_run(static_cast<const T*>(p.theta) + sidx[j], rth[j]);
-        if (prev) load_run(static_cast<const T*>(p.B_prev) + bn[j], rbp[j]);
+        if constexpr (CPLX) load_run(has_th ? thp + sidx[j] : delta + ch, rth[j]);
+        if constexpr (DISC == kTrap) load_run(bpp + bn[j], rbp[j]);
     }
+    const float a_n[2] = {p.A[d * N + n0], p.A[d * N + n1]};
     float hr[2], hi[2] = {0.f, 0.f};
     if constexpr (PAIRS) {
         if constexpr (CPLX) {
@@ -522,15 +536,15 @@ __global__ void __launch_bounds__(256) mimo_step_kernel(MimoStepParams p) {
     const float dt = run_elem<T>(rdt, 0);
     const float lam = DISC == kTrap ? run_elem<T>(rlam, 0) : 0.f;
     float part[R];
-    const float dmask = (p.Dskip && pr == 0) ? p.Dskip[d] : 0.f;
+    const float dmask = pr == 0 ? dsk : 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) part[r] = dmask * x[r];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         float qr, qi, qpr = 0.f, qpi = 0.f;
         mimo_q<T, CPLX, R>(rb[j], x, &qr, &qi);
-        if (prev) mimo_q<T, CPLX, R>(rbp[j], xp, &qpr, &qpi);
-        const float a = p.A[d * N + (j ? n1 : n0)];
+        if constexpr (DISC == kTrap) mimo_q<T, CPLX, R>(rbp[j], xp, &qpr, &qpi);  // zero without a previous step
+        const float a = a_n[j];
         const float th = has_th ? run_elem<T>(rth[j], 0) : 0.f;
         float ar, ai;
         mimo_advance<DISC, CPLX, SC>(dt, lam, th, qr, qi, a, prep_A(a), hr[j], hi[j], qpr, qpi, &ar, &ai);

@@ -56,14 +56,17 @@ struct StepLane {
     float a[2], th[2], br[2], bi[2], cr[2], ci[2], pbr[2], pbi[2], hr[2], hi[2];
 };
 
-template <typename T, int DISC, bool CPLX, bool PAIRS>
+// TH: theta is given (complex state).  Every load is unconditional (a
+// branch around a load makes the compiler wait for all earlier loads at the
+// join): without a previous step, B_prev is read from B and masked later.
+template <typename T, int DISC, bool CPLX, bool PAIRS, bool TH>
 __device__ __forceinline__ void step_load(const StepParams& p, int64_t ch, int64_t b, int64_t d, int64_t n0,
                                           StepLane& v) {
     using E = Elem<T>;
     const int64_t N = p.dstate;
     const T* Bm = static_cast<const T*>(p.B);
     const T* Cm = static_cast<const T*>(p.C);
-    const T* Bp = static_cast<const T*>(p.B_prev);
+    const T* Bp = static_cast<const T*>(p.B_prev ? p.B_prev : p.B);
     const T* theta = static_cast<const T*>(p.theta);
     const int64_t s = ch * N + n0, bn = b * N + n0;
     if constexpr (PAIRS) {
@@ -77,17 +80,17 @@ __device__ __forceinline__ void step_load(const StepParams& p, int64_t ch, int64
             E::load_pair(Bm, 2 * bn + 2, &v.br[1], &v.bi[1]);
             E::load_pair(Cm, 2 * bn, &v.cr[0], &v.ci[0]);
             E::load_pair(Cm, 2 * bn + 2, &v.cr[1], &v.ci[1]);
-            if (Bp) {
+            if constexpr (DISC == kTrap) {
                 E::load_pair(Bp, 2 * bn, &v.pbr[0], &v.pbi[0]);
                 E::load_pair(Bp, 2 * bn + 2, &v.pbr[1], &v.pbi[1]);
             }
-            if (theta) E::load_pair(theta, s, &v.th[0], &v.th[1]);
+            if constexpr (TH) E::load_pair(theta, s, &v.th[0], &v.th[1]);
         } else {
             const float2 h = *reinterpret_cast<const float2*>(p.h + s);
             v.hr[0] = h.x, v.hr[1] = h.y;
             E::load_pair(Bm, bn, &v.br[0], &v.br[1]);
             E::load_pair(Cm, bn, &v.cr[0], &v.cr[1]);
-            if (Bp) E::load_pair(Bp, bn, &v.pbr[0], &v.pbr[1]);
+            if constexpr (DISC == kTrap) E::load_pair(Bp, bn, &v.pbr[0], &v.pbr[1]);
         }
     } else {
 #pragma unroll
@@ -101,29 +104,28 @@ __device__ __forceinline__ void step_load(const StepParams& p, int64_t ch, int64
                 v.bi[j] = E::load(Bm, 2 * (bn + j) + 1);
                 v.cr[j] = E::load(Cm, 2 * (bn + j));
                 v.ci[j] = E::load(Cm, 2 * (bn + j) + 1);
-                if (Bp) {
+                if constexpr (DISC == kTrap) {
                     v.pbr[j] = E::load(Bp, 2 * (bn + j));
                     v.pbi[j] = E::load(Bp, 2 * (bn + j) + 1);
                 }
-                if (theta) v.th[j] = E::load(theta, s + j);
+                if constexpr (TH) v.th[j] = E::load(theta, s + j);
             } else {
                 v.hr[j] = p.h[s + j];
                 v.br[j] = E::load(Bm, bn + j);
                 v.cr[j] = E::load(Cm, bn + j);
-                if (Bp) v.pbr[j] = E::load(Bp, bn + j);
+                if constexpr (DISC == kTrap) v.pbr[j] = E::load(Bp, bn + j);
             }
         }
     }
 }
 
-template <typename T, int DISC, bool CPLX, bool PAIRS>
+template <typename T, int DISC, bool CPLX, bool PAIRS, bool TH>
 __global__ void __launch_bounds__(256) scan_step_kernel(StepParams p) {
     using E = Elem<T>;
     constexpr int SC = std::is_same_v<T, uint16_t> ? kSinCosHw : kSinCosWide;
     const T* u = static_cast<const T*>(p.u);
     const T* delta = static_cast<const T*>(p.delta);
     const T* lambda = static_cast<const T*>(p.lambda);
-    const T* u_prev = static_cast<const T*>(p.u_prev);
     T* y = static_cast<T*>(p.y);
 
     const int lane = threadIdx.x & 63;
@@ -138,17 +140,24 @@ __global__ void __launch_bounds__(256) scan_step_kernel(StepParams p) {
     const int64_t b = ch_ok ? ch / D : 0;
     const int64_t d = ch_ok ? ch % D : 0;
 
-    float x = 0.f, dt = 0.f, lam = 0.f, xp = 0.f;
-    if (ch_ok) {
-        x = E::load(u, ch);
-        dt = E::load(delta, ch);
-        if constexpr (DISC == kTrap) {
-            lam = E::load(lambda, ch);
-            if (u_prev) xp = E::load(u_prev, ch);
-        }
+    // per-channel inputs, unconditionally (a missing u_prev reads u, masked)
+    const T* up = static_cast<const T*>(p.u_prev ? p.u_prev : p.u);
+    const int64_t chc = ch_ok ? ch : 0;
+    const float dsk = (p.Dskip ? p.Dskip : p.A)[d];  // masked below without D
+    float x = E::load(u, chc), dt = E::load(delta, chc), lam = 0.f, xp = 0.f;
+    if constexpr (DISC == kTrap) {
+        lam = E::load(lambda, chc);
+        xp = E::load(up, chc);
     }
     StepLane v{};
-    if (ok) step_load<T, DISC, CPLX, PAIRS>(p, ch, b, d, n0, v);
+    step_load<T, DISC, CPLX, PAIRS, TH>(p, ch_ok ? ch : 0, b, d, ok ? n0 : 0, v);
+    if (!ch_ok) x = dt = lam = xp = 0.f;
+    if (!p.u_prev) xp = 0.f;
+    const float skip = p.Dskip ? dsk : 0.f;
+    if (!ok) {  // states past N (or past the channels) take no part
+#pragma unroll
+        for (int j = 0; j < 2; ++j) v.a[j] = v.th[j] = v.br[j] = v.bi[j] = v.cr[j] = v.ci[j] = v.pbr[j] = v.pbi[j] = v.hr[j] = v.hi[j] = 0.f;
+    }
 
     float part = 0.f;
     float nr[2], ni[2];
@@ -209,7 +218,7 @@ __global__ void __launch_bounds__(256) scan_step_kernel(StepParams p) {
         }
     }
     for (int off = lpc >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-    if (pr == 0 && ch_ok) E::store(y, ch, part + (p.Dskip ? p.Dskip[d] : 0.f) * x);
+    if (pr == 0 && ch_ok) E::store(y, ch, part + skip * x);
 }
 
 }  // namespace ssm

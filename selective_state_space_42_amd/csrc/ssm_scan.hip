@@ -90,18 +90,26 @@ int launch_step_k(const ssm_scan_desc_t* d, const ssm::StepParams& p, hipStream_
     const int64_t blocks = (waves + 3) / 4;
     if (blocks > INT32_MAX) return SSM_ERR_UNSUPPORTED;
     const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+    const bool th = p.theta != nullptr;
     if (d->is_complex) {
-        if (d->disc == SSM_DISC_EXP_EULER)
-            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kEuler, true, PAIRS>), grid, block, 0, s, p);
-        else
-            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kTrap, true, PAIRS>), grid, block, 0, s, p);
+        if (d->disc == SSM_DISC_EXP_EULER) {
+            if (th)
+                hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kEuler, true, PAIRS, true>), grid, block, 0, s, p);
+            else
+                hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kEuler, true, PAIRS, false>), grid, block, 0, s, p);
+        } else {
+            if (th)
+                hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kTrap, true, PAIRS, true>), grid, block, 0, s, p);
+            else
+                hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kTrap, true, PAIRS, false>), grid, block, 0, s, p);
+        }
     } else {
         if (d->disc == SSM_DISC_ZOH)
-            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kZOH, false, PAIRS>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kZOH, false, PAIRS, false>), grid, block, 0, s, p);
         else if (d->disc == SSM_DISC_EXP_EULER)
-            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kEuler, false, PAIRS>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kEuler, false, PAIRS, false>), grid, block, 0, s, p);
         else
-            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kTrap, false, PAIRS>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((ssm::scan_step_kernel<T, ssm::kTrap, false, PAIRS, false>), grid, block, 0, s, p);
     }
     return hip_status(hipGetLastError());
 }
