@@ -14,12 +14,16 @@
 // complex-state section).
 //
 // Layout of the work: one lane per (channel, state pair); lpc lanes per
-// channel (a power of two >= max(N / 2, R)), 64 / lpc channels per wave.  A
-// lane reads each of its states' rows of B (and C), B[b, t, n, 0..R-1], as
-// one contiguous run, and the channel's R inputs as another; per-step
-// operands are reached through pointers advanced by a stride per step.  The R partial sums Re(C[n, r] h[n])
-// are reduced over the channel's lanes by a reduce-scatter: log2(R) halving
-// levels leave one output per lane group, then the remaining levels add.
+// channel (a power of two >= max(N / 2, R)), 64 / lpc channels per wave and
+// 256 / lpc channels of one batch row per workgroup.  B and C, shared by a
+// batch row's channels, are staged in LDS as fp32 by the whole workgroup a
+// group of steps at a time, so each row is read from memory once per
+// workgroup and widened once; a lane then reads each of its states' rows,
+// B[b, t, n, 0..R-1], as one contiguous LDS run.  The channel's R inputs and
+// the other per-channel operands are reached through pointers advanced by a
+// stride per step.  The R partial sums Re(C[n, r] h[n]) are reduced over the
+// channel's lanes by a reduce-scatter: log2(R) halving levels leave one
+// output per lane group, then the remaining levels add.
 //
 // Long sequences are cut into time chunks so that short, wide and long,
 // narrow problems both fill the GPU:
@@ -90,16 +94,16 @@ __device__ __forceinline__ float run_elem(const Run<NB>& r, int i) {
         return (i & 1) ? bf16_hi(r.w[i >> 1]) : bf16_lo(r.w[i >> 1]);
 }
 
-// q = sum_r B[r] x[r] (complex B, real x)
-template <typename T, bool CPLX, int R>
-__device__ __forceinline__ void mimo_q(const Run<R * (CPLX ? 2 : 1) * sizeof(T)>& bm, const float (&x)[R], float* qr,
+// q = sum_r B[r] x[r] (complex B, real x); BT is the element type of B's run
+template <typename BT, bool CPLX, int R>
+__device__ __forceinline__ void mimo_q(const Run<R * (CPLX ? 2 : 1) * sizeof(BT)>& bm, const float (&x)[R], float* qr,
                                        float* qi) {
     constexpr int kCw = CPLX ? 2 : 1;
     float sr = 0.f, si = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        sr = __builtin_fmaf(run_elem<T>(bm, r * kCw), x[r], sr);
-        if constexpr (CPLX) si = __builtin_fmaf(run_elem<T>(bm, r * kCw + 1), x[r], si);
+        sr = __builtin_fmaf(run_elem<BT>(bm, r * kCw), x[r], sr);
+        if constexpr (CPLX) si = __builtin_fmaf(run_elem<BT>(bm, r * kCw + 1), x[r], si);
     }
     *qr = sr;
     *qi = si;
@@ -205,19 +209,19 @@ __device__ __forceinline__ int mimo_out_index(int pr, int lpc) {
     return r;
 }
 
-// Per-lane pointers to one step's operands, advanced by a stride per step.
-// A lane holds two states, n0 = 2 pr and n1 = n0 + 1; a state past N reads
-// state n0's row again and is masked, and a missing theta (complex state,
-// theta = 0) reads delta's element instead and is ignored, so no load
-// needs a branch.
+// Per-lane pointers to one step's per-channel operands, advanced by a stride
+// per step.  A lane holds two states, n0 = 2 pr and n1 = n0 + 1; a state
+// past N reads state n0's element again and is masked, and a missing theta
+// (complex state, theta = 0) reads delta's element instead and is ignored,
+// so no load needs a branch.
 template <typename T>
 struct MimoPtrs {
-    const T *dt, *lam, *x, *th0, *th1, *b0, *b1, *c0, *c1;
+    const T *dt, *lam, *x, *th0, *th1;
     T* y;
 };
 
 struct MimoStrides {
-    int64_t tc, x, th, bn;  // per step: delta and lambda, u and y, theta, B and C
+    int64_t tc, x, th;  // per step: delta and lambda, u and y, theta
 };
 
 template <typename T>
@@ -228,24 +232,17 @@ __device__ __forceinline__ void mimo_advance_ptrs(MimoPtrs<T>& q, const MimoStri
     q.y += s.x;
     q.th0 += s.th;
     q.th1 += s.th;
-    q.b0 += s.bn;
-    q.b1 += s.bn;
-    q.c0 += s.bn;
-    q.c1 += s.bn;
 }
 
-// The operands of one step of one lane, as loaded (raw bits).
-template <typename T, bool CPLX, int R>
+// The per-channel operands of one step of one lane, as loaded (raw bits).
+template <typename T, int R>
 struct MimoIn {
-    static constexpr int kES = sizeof(T), kCw = CPLX ? 2 : 1;
-    Run<kES> dt, lam, th[2];
-    Run<R * kES> x;            // u[b, t, d, 0 .. R-1]
-    Run<R * kCw * kES> bm[2];  // B[b, t, n_j, 0 .. R-1]
-    Run<R * kCw * kES> cm[2];  // C[b, t, n_j, 0 .. R-1]
+    Run<sizeof(T)> dt, lam, th[2];
+    Run<R * sizeof(T)> x;  // u[b, t, d, 0 .. R-1]
 };
 
-template <typename T, int DISC, bool CPLX, int R, bool WITH_C>
-__device__ __forceinline__ void mimo_load(const MimoPtrs<T>& q, MimoIn<T, CPLX, R>& in) {
+template <typename T, int DISC, bool CPLX, int R>
+__device__ __forceinline__ void mimo_load(const MimoPtrs<T>& q, MimoIn<T, R>& in) {
     load_run(q.dt, in.dt);
     if constexpr (DISC == kTrap) load_run(q.lam, in.lam);
     load_run(q.x, in.x);
@@ -253,35 +250,78 @@ __device__ __forceinline__ void mimo_load(const MimoPtrs<T>& q, MimoIn<T, CPLX, 
         load_run(q.th0, in.th[0]);
         load_run(q.th1, in.th[1]);
     }
-    load_run(q.b0, in.bm[0]);
-    load_run(q.b1, in.bm[1]);
-    if constexpr (WITH_C) {
-        load_run(q.c0, in.cm[0]);
-        load_run(q.c1, in.cm[1]);
+}
+
+// B and C of a group of kGroup steps, staged in LDS as fp32 by the whole
+// workgroup: its channels all belong to one batch row, so they share these
+// rows, and each is read from memory once per workgroup instead of once per
+// wave.  A row holds E = N * R * (2 | 1) values; thread t holds values
+// t + 256 i (i < kEC) of every (step, array) row between the loads and the
+// LDS stores.  Rows past the chunk and values past E read zero through the
+// buffer resource, so no load needs a branch.
+template <typename T, bool CPLX, int R, int NA>
+struct MimoStage {
+    static constexpr int kEC = (64 * R * (CPLX ? 2 : 1) + 255) / 256;  // per thread and row, at N = 64
+    uint32_t v[mimo::kGroup][NA][kEC];
+};
+
+template <typename T, bool CPLX, int R, int NA>
+__device__ __forceinline__ void mimo_stage_load(MimoStage<T, CPLX, R, NA>& sg, const T* const (&arr)[NA],
+                                                int64_t row0, int rows, int E, const uint32_t (&eoff)[MimoStage<T, CPLX, R, NA>::kEC]) {
+    constexpr uint32_t es = sizeof(T);
+    const uint32_t rowb = static_cast<uint32_t>(E) * es;
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+        const rsrc_t rs = make_rsrc(arr[a] + row0 * E, static_cast<uint32_t>(rows) * rowb);
+#pragma unroll
+        for (int k = 0; k < mimo::kGroup; ++k)
+#pragma unroll
+            for (int i = 0; i < MimoStage<T, CPLX, R, NA>::kEC; ++i)
+                sg.v[k][a][i] = Buf<T>::load_raw(rs, eoff[i] + k * rowb);
     }
 }
 
+template <typename T, bool CPLX, int R, int NA>
+__device__ __forceinline__ void mimo_stage_store(const MimoStage<T, CPLX, R, NA>& sg, float* sb, int E, int tid) {
+#pragma unroll
+    for (int k = 0; k < mimo::kGroup; ++k)
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int i = 0; i < MimoStage<T, CPLX, R, NA>::kEC; ++i) {
+                const int e = tid + 256 * i;
+                if (e < E) sb[(k * NA + a) * E + e] = Buf<T>::widen(sg.v[k][a][i]);
+            }
+}
+
+// LDS of one workgroup: two buffers of kGroup steps x (B, C) rows of fp32.
+extern __shared__ __attribute__((aligned(16))) float mimo_smem[];
+
+// One workgroup = 256 lanes = 256 / lpc channels of one batch row and one
+// time chunk; the grid covers (chunk, batch row, channel block).
 template <typename T, int DISC, bool CPLX, int R, bool OUT>
 __global__ void __launch_bounds__(256) mimo_scan_kernel(MimoParams p) {
-    constexpr int kCw = CPLX ? 2 : 1, kG = mimo::kGroup;
+    constexpr int kCw = CPLX ? 2 : 1, kG = mimo::kGroup, kRun = R * kCw;
+    constexpr int NA = OUT ? 2 : 1;  // staged arrays: B, and C when forming outputs
+    using Stage = MimoStage<T, CPLX, R, NA>;
     constexpr int SC = std::is_same_v<T, uint16_t> ? kSinCosHw : kSinCosWide;
-    const int lane = threadIdx.x & 63, lpc = p.lpc;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lpc = p.lpc;
     const int64_t L = p.seqlen, D = p.dim, N = p.dstate, BD = p.batch * p.dim;
-    const int64_t gw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
-    const int64_t wpc = (BD * lpc + 63) / 64;  // waves per chunk
-    const int64_t c = gw / wpc;
-    if (c >= (OUT ? p.nchunks : p.nchunks - 1)) return;  // whole waves
-    const int64_t ch_raw = (gw % wpc) * (64 / lpc) + lane / lpc;
+    const int64_t wpr = (D * lpc + 255) / 256;  // workgroups per batch row
+    const int64_t blk = blockIdx.x;
+    const int64_t c = blk / (p.batch * wpr), b = (blk / wpr) % p.batch;
+    const int64_t d_raw = (blk % wpr) * (256 / lpc) + wave * (64 / lpc) + lane / lpc;
     const int pr = lane & (lpc - 1);
     const int64_t n0_raw = 2 * pr;
-    const bool ch_ok = ch_raw < BD;
+    const bool ch_ok = d_raw < D;
     const bool ok[2] = {ch_ok && n0_raw < N, ch_ok && n0_raw + 1 < N};
     // lanes past the problem compute on valid addresses and write nothing
-    const int64_t ch = ch_ok ? ch_raw : BD - 1, n0 = n0_raw < N ? n0_raw : N - 1;
+    const int64_t d = ch_ok ? d_raw : D - 1, n0 = n0_raw < N ? n0_raw : N - 1;
     const int64_t n1 = n0 + 1 < N ? n0 + 1 : n0;
-    const int64_t b = ch / D, d = ch % D;
+    const int64_t ch = b * D + d;
     const int64_t s0 = ch * N + n0, s1 = ch * N + n1;  // (b, d, n) in the layout of h0
     const int64_t t0 = c * p.chunk, t1 = t0 + p.chunk < L ? t0 + p.chunk : L;
+    const int E = static_cast<int>(N) * kRun;
 
     const float a[2] = {p.A[d * N + n0], p.A[d * N + n1]};
     const float a2[2] = {prep_A(a[0]), prep_A(a[1])};
@@ -316,10 +356,29 @@ __global__ void __launch_bounds__(256) mimo_scan_kernel(MimoParams p) {
         }
     }
 
-    // pointers to step t0's operands
+    const T* Bm = static_cast<const T*>(p.B);
+    const T* Cm = static_cast<const T*>(p.C);
+    if (DISC == kTrap && t0 > 0) {  // q_{t0-1} from the inputs of step t0 - 1
+        Run<R * sizeof(T)> rx;
+        load_run(static_cast<const T*>(p.u) + ((b * L + t0 - 1) * D + d) * R, rx);
+        float x[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[r] = run_elem<T>(rx, r);
+        const int64_t nn[2] = {n0, n1};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            Run<kRun * sizeof(T)> rb;
+            load_run(Bm + ((b * L + t0 - 1) * N + nn[j]) * kRun, rb);
+            mimo_q<T, CPLX, R>(rb, x, &qpr[j], &qpi[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        if (!ok[j]) hr[j] = hi[j] = qpr[j] = qpi[j] = 0.f;
+
+    // pointers to step t0's per-channel operands
     const T* delta = static_cast<const T*>(p.delta);
-    const int64_t tc0 = (b * L + t0) * D + d, bn0 = ((b * L + t0) * N + n0) * R * kCw;
-    const int64_t dn = (n1 - n0) * R * kCw;
+    const int64_t tc0 = (b * L + t0) * D + d;
     MimoPtrs<T> q;
     q.dt = delta + tc0;
     q.lam = DISC == kTrap ? static_cast<const T*>(p.lambda) + tc0 : q.dt;
@@ -328,43 +387,39 @@ __global__ void __launch_bounds__(256) mimo_scan_kernel(MimoParams p) {
     const bool has_th = CPLX && p.theta;
     q.th0 = has_th ? static_cast<const T*>(p.theta) + tc0 * N + n0 : q.dt;
     q.th1 = has_th ? q.th0 + (n1 - n0) : q.dt;
-    q.b0 = static_cast<const T*>(p.B) + bn0;
-    q.b1 = q.b0 + dn;
-    q.c0 = static_cast<const T*>(p.C) + bn0;
-    q.c1 = q.c0 + dn;
-    const MimoStrides st{D, D * R, has_th ? D * N : D, N * R * kCw};
+    const MimoStrides st{D, D * R, has_th ? D * N : D};
 
-    if (DISC == kTrap && t0 > 0) {  // q_{t0-1} from the inputs of step t0 - 1
-        MimoPtrs<T> qp = q;
-        const MimoStrides back{-st.tc, -st.x, -st.th, -st.bn};
-        mimo_advance_ptrs(qp, back);
-        MimoIn<T, CPLX, R> in;
-        mimo_load<T, DISC, CPLX, R, false>(qp, in);
-        float x[R];
+    // staging of B (and C): this thread's values of a row, and the two buffers
+    const T* arr[NA];
+    arr[0] = Bm;
+    if constexpr (OUT) arr[NA - 1] = Cm;
+    uint32_t eoff[Stage::kEC];
 #pragma unroll
-        for (int r = 0; r < R; ++r) x[r] = run_elem<T>(in.x, r);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) mimo_q<T, CPLX, R>(in.bm[j], x, &qpr[j], &qpi[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-        if (!ok[j]) hr[j] = hi[j] = qpr[j] = qpi[j] = 0.f;
+    for (int i = 0; i < Stage::kEC; ++i)
+        eoff[i] = tid + 256 * i < E ? static_cast<uint32_t>(tid + 256 * i) * sizeof(T) : kOutOfRange;
+    const int bstride = kG * NA * E;  // floats per buffer
+    auto rows_at = [&](int64_t tg) { return static_cast<int>(t1 - tg < kG ? t1 - tg : kG); };
+    Stage sg;
+    mimo_stage_load<T, CPLX, R, NA>(sg, arr, b * L + t0, rows_at(t0), E, eoff);
+    mimo_stage_store<T, CPLX, R, NA>(sg, mimo_smem, E, tid);
+    __syncthreads();
 
     T* yp = q.y;
-    // kG steps: their loads first, then their arithmetic (the compiler also
-    // issues the next group's loads during a group).  The tail group stops its
-    // pointers on the chunk's last step, so no load passes the chunk.
-    auto group = [&](int64_t tg, auto tail_tag) {
+    // kG steps: their per-channel loads first, then their arithmetic with B
+    // and C from LDS.  The tail group stops its pointers on the chunk's last
+    // step, so no load passes the chunk.
+    auto group = [&](int64_t tg, int boff, auto tail_tag) {
         constexpr bool kTail = decltype(tail_tag)::value;
-        MimoIn<T, CPLX, R> in[kG];
+        MimoIn<T, R> in[kG];
 #pragma unroll
         for (int k = 0; k < kG; ++k) {
-            mimo_load<T, DISC, CPLX, R, OUT>(q, in[k]);
+            mimo_load<T, DISC, CPLX, R>(q, in[k]);
             if (!kTail || tg + k + 1 < t1) mimo_advance_ptrs(q, st);
         }
 #pragma unroll
         for (int k = 0; k < kG; ++k) {
             if (kTail && tg + k >= t1) break;
+            const float* rowB = mimo_smem + boff + (k * NA) * E;
             const float dt = run_elem<T>(in[k].dt, 0);
             const float lam = DISC == kTrap ? run_elem<T>(in[k].lam, 0) : 0.f;
             float x[R];
@@ -373,21 +428,25 @@ __global__ void __launch_bounds__(256) mimo_scan_kernel(MimoParams p) {
             float part[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) part[r] = dmask * x[r];
+            const int64_t nn[2] = {n0, n1};
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const float th = has_th ? run_elem<T>(in[k].th[j], 0) : 0.f;
+                Run<kRun * 4> bm;
+                load_run(rowB + nn[j] * kRun, bm);
                 float qr, qi;
-                mimo_q<T, CPLX, R>(in[k].bm[j], x, &qr, &qi);
+                mimo_q<float, CPLX, R>(bm, x, &qr, &qi);
                 if (!ok[j]) qr = qi = 0.f;
                 float ar, ai;
                 mimo_advance<DISC, CPLX, SC>(dt, lam, th, qr, qi, a[j], a2[j], hr[j], hi[j], qpr[j], qpi[j], &ar,
                                              &ai);
                 if constexpr (OUT) {
+                    Run<kRun * 4> cm;
+                    load_run(rowB + E + nn[j] * kRun, cm);
 #pragma unroll
                     for (int r = 0; r < R; ++r) {  // Re(C h), no conjugate; a masked state's h is 0
-                        part[r] = __builtin_fmaf(run_elem<T>(in[k].cm[j], r * kCw), hr[j], part[r]);
-                        if constexpr (CPLX)
-                            part[r] = __builtin_fmaf(-run_elem<T>(in[k].cm[j], r * kCw + 1), hi[j], part[r]);
+                        part[r] = __builtin_fmaf(run_elem<float>(cm, r * kCw), hr[j], part[r]);
+                        if constexpr (CPLX) part[r] = __builtin_fmaf(-run_elem<float>(cm, r * kCw + 1), hi[j], part[r]);
                     }
                 } else {
                     const float nr = ar * Pr[j] - ai * Pi[j];
@@ -402,9 +461,20 @@ __global__ void __launch_bounds__(256) mimo_scan_kernel(MimoParams p) {
             }
         }
     };
-    int64_t tg = t0;
-    for (; tg + kG <= t1; tg += kG) group(tg, std::false_type{});
-    if (tg < t1) group(tg, std::true_type{});
+    // every thread runs the same groups (t0, t1 are the workgroup's), so the
+    // barriers match; the next group's rows load during this group
+    int buf = 0;
+    for (int64_t tg = t0; tg < t1; tg += kG) {
+        const bool more = tg + kG < t1;
+        if (more) mimo_stage_load<T, CPLX, R, NA>(sg, arr, b * L + tg + kG, rows_at(tg + kG), E, eoff);
+        if (tg + kG <= t1)
+            group(tg, buf * bstride, std::false_type{});
+        else
+            group(tg, buf * bstride, std::true_type{});
+        if (more) mimo_stage_store<T, CPLX, R, NA>(sg, mimo_smem + (buf ^ 1) * bstride, E, tid);
+        __syncthreads();
+        buf ^= 1;
+    }
 
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -428,6 +498,12 @@ __global__ void __launch_bounds__(256) mimo_scan_kernel(MimoParams p) {
                 *reinterpret_cast<float2*>(sl) = make_float2(Pr[j], hr[j]);
         }
     }
+}
+
+// Bytes of LDS a mimo_scan_kernel workgroup takes: two buffers of kGroup
+// steps of the B (and C) rows in fp32.
+inline size_t mimo_scan_lds_bytes(int64_t dstate, int R, bool cplx, bool out) {
+    return static_cast<size_t>(2 * mimo::kGroup * (out ? 2 : 1) * dstate * R * (cplx ? 2 : 1) * 4);
 }
 
 // H_in(c + 1) = P_c H_in(c) + h_loc(c) per (b, d, n), written over h_loc(c).

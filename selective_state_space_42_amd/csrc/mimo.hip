@@ -8,18 +8,17 @@ namespace {
 template <typename T, int DISC, bool CPLX, int R>
 hipError_t scan_r(const MimoParams& p, hipStream_t s) {
     const int64_t BD = p.batch * p.dim;
-    const int64_t wpc = (BD * p.lpc + 63) / 64;  // waves per time chunk
+    const int64_t wgc = p.batch * ((p.dim * p.lpc + 255) / 256);  // workgroups per time chunk
     if (p.nchunks > 1) {
-        const int64_t w = wpc * (p.nchunks - 1);
-        hipLaunchKernelGGL((mimo_scan_kernel<T, DISC, CPLX, R, false>), dim3(static_cast<unsigned>((w + 3) / 4)),
-                           dim3(256), 0, s, p);
+        hipLaunchKernelGGL((mimo_scan_kernel<T, DISC, CPLX, R, false>),
+                           dim3(static_cast<unsigned>(wgc * (p.nchunks - 1))), dim3(256),
+                           mimo_scan_lds_bytes(p.dstate, R, CPLX, false), s, p);
         const int64_t bdn = BD * p.dstate;
         hipLaunchKernelGGL((mimo_carry_kernel<CPLX>), dim3(static_cast<unsigned>((bdn + 255) / 256)), dim3(256), 0,
                            s, p);
     }
-    const int64_t w = wpc * p.nchunks;
-    hipLaunchKernelGGL((mimo_scan_kernel<T, DISC, CPLX, R, true>), dim3(static_cast<unsigned>((w + 3) / 4)),
-                       dim3(256), 0, s, p);
+    hipLaunchKernelGGL((mimo_scan_kernel<T, DISC, CPLX, R, true>), dim3(static_cast<unsigned>(wgc * p.nchunks)),
+                       dim3(256), mimo_scan_lds_bytes(p.dstate, R, CPLX, true), s, p);
     return hipGetLastError();
 }
 

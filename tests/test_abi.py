@@ -275,12 +275,14 @@ def test_mimo_workspace_follows_the_chunking():
     # a fixed chunk of 16 steps over 100: 7 chunks, 6 carried (P, h) pairs per (b, d, n)
     assert scan.ssm_mimo_workspace_bytes(mimo_desc(B=2, D=3, N=5, L=100, chunk=16)) == 6 * 2 * 3 * 5 * 16
     assert scan.ssm_mimo_workspace_bytes(mimo_desc(B=2, D=3, N=5, L=100, chunk=16, cplx=False)) == 6 * 2 * 3 * 5 * 8
-    # a narrow, long problem is cut into chunks of at least 64 steps
+    # the sequence is cut until there are 2^21 lanes, into chunks of at least 128 steps
     need = scan.ssm_mimo_workspace_bytes(mimo_desc(B=1, D=8, N=16, L=1 << 14))
-    assert need == (256 - 1) * 8 * 16 * 16
-    # 2^16 lanes (8192 channels of 8 lanes) fill the GPU: one chunk
-    assert scan.ssm_mimo_workspace_bytes(mimo_desc(B=4, D=2048, N=16, L=8192)) == 0
-    assert scan.ssm_mimo_workspace_bytes(mimo_desc(B=2, D=2048, N=16, L=8192)) == 1 * 2 * 2048 * 16 * 16
+    assert need == (128 - 1) * 8 * 16 * 16                               # 128 chunks of 128 steps
+    # 2^16 lanes (8192 channels of 8 lanes): 32 chunks of 256 steps
+    assert scan.ssm_mimo_workspace_bytes(mimo_desc(B=4, D=2048, N=16, L=8192)) == 31 * 4 * 2048 * 16 * 16
+    assert scan.ssm_mimo_workspace_bytes(mimo_desc(B=2, D=2048, N=16, L=8192)) == 63 * 2 * 2048 * 16 * 16
+    # 2^21 lanes: one chunk
+    assert scan.ssm_mimo_workspace_bytes(mimo_desc(B=64, D=4096, N=16, L=8192)) == 0
     d = mimo_desc(L=100, chunk=16)
     assert call_mimo(d, ws=P, ws_bytes=scan.ssm_mimo_workspace_bytes(d) - 1) == WS_SMALL
     assert call_mimo(d, ws=0, ws_bytes=0) == WS_SMALL
