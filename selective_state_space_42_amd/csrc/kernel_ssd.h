@@ -59,6 +59,7 @@ struct SsdParams {
     float* E;           // [B][H][nC]        chunk decays (workspace)
     uint16_t* Hin;      // [B][H][nC][N][P]  state entering each chunk, bf16 (workspace)
     int64_t batch, seqlen, dim, dstate, heads, nchunks;
+    int32_t bc_vec;     // N a multiple of 8 and B, C 16-byte aligned: rows move in 16-byte pieces
 };
 
 // Inclusive prefix sum of s[0 .. kQ) in place by one wave (lanes 0 .. 63).
@@ -95,30 +96,48 @@ __device__ __forceinline__ void ssd_mfma_block(const uint16_t (*a_rows)[kStride]
     }
 }
 
-// X of one (chunk, head) into LDS transposed (rows p, columns t), zero past
-// the sequence end: 16-byte loads of 8 channels each (the head's 64 channels
-// of a step are one 128-byte row).
-template <typename T>
-__device__ __forceinline__ void ssd_load_xt(const T* u, int64_t row0, int64_t D, int len, int tid,
-                                            uint16_t (*s_xt)[ssd::kQ + ssd::kPad]) {
-    static_assert(sizeof(T) == 2, "bf16 rows");
-    for (int i = tid; i < ssd::kQ * ssd::kP / 8; i += 256) {
-        const int t = i / (ssd::kP / 8), p8 = (i % (ssd::kP / 8)) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (t < len) v = *reinterpret_cast<const uint4*>(u + (row0 + t) * D + p8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            s_xt[p8 + 2 * q][t] = static_cast<uint16_t>(w[q]);
-            s_xt[p8 + 2 * q + 1][t] = static_cast<uint16_t>(w[q] >> 16);
-        }
-    }
-}
-
 constexpr float kSsdLog2e = 1.4426950408889634f;
 
 // row of element r of a lane's 32 x 32 accumulator block
 __device__ __forceinline__ int ssd_acc_row(int i0, int lane, int r) { return i0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// NMAX: the largest N the instantiation handles (16 or 64); it sizes the LDS
+// tiles, so small state sizes leave room for more resident workgroups.
+// The 16-byte pieces of X (the head's 64 channels of a step are one 128-byte
+// row) and of the B or C rows of a chunk (8 states each) that one thread
+// loads, all issued before any is used so that a workgroup waits for memory
+// once.  Rows past the sequence end read the chunk's last valid row instead
+// (no branch around a load) and are zeroed when stored to LDS.
+template <typename T>
+__device__ __forceinline__ uint4 ssd_ld16(const T* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+template <typename T>
+__device__ __forceinline__ void ssd_load_x(const T* u, int64_t row0, int64_t D, int len, int tid,
+                                           uint4 (&xv)[ssd::kQ * ssd::kP / 8 / 256]) {
+#pragma unroll
+    for (int q = 0; q < ssd::kQ * ssd::kP / 8 / 256; ++q) {
+        const int i = tid + 256 * q, t = i / (ssd::kP / 8), p8 = (i % (ssd::kP / 8)) * 8;
+        xv[q] = ssd_ld16(u + (row0 + (t < len ? t : len - 1)) * D + p8);
+    }
+}
+
+// X transposed into LDS (rows p, columns t) from the pieces of ssd_load_x
+__device__ __forceinline__ void ssd_store_xt(const uint4 (&xv)[ssd::kQ * ssd::kP / 8 / 256], int len, int tid,
+                                             uint16_t (*s_xt)[ssd::kQ + ssd::kPad]) {
+#pragma unroll
+    for (int q = 0; q < ssd::kQ * ssd::kP / 8 / 256; ++q) {
+        const int i = tid + 256 * q, t = i / (ssd::kP / 8), p8 = (i % (ssd::kP / 8)) * 8;
+        const bool ok = t < len;
+        const uint32_t w[4] = {ok ? xv[q].x : 0u, ok ? xv[q].y : 0u, ok ? xv[q].z : 0u, ok ? xv[q].w : 0u};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            s_xt[p8 + 2 * k][t] = static_cast<uint16_t>(w[k]);
+            s_xt[p8 + 2 * k + 1][t] = static_cast<uint16_t>(w[k] >> 16);
+        }
+    }
+}
 
 // NMAX: the largest N the instantiation handles (16 or 64); it sizes the LDS
 // tiles, so small state sizes leave room for more resident workgroups.
@@ -140,22 +159,54 @@ __global__ void __launch_bounds__(256) ssd_state_kernel(SsdParams p) {
     const T* u = static_cast<const T*>(p.u);
     const T* Bm = static_cast<const T*>(p.B);
     const T* dl = static_cast<const T*>(p.delta);
-    ssd_load_xt<T>(u + h * kP, b * L + t0, D, len, tid, s_xt);
+    // every global load first: X, B (16-byte pieces when bc_vec), delta
+    uint4 xv[kQ * kP / 8 / 256];
+    ssd_load_x<T>(u + h * kP, b * L + t0, D, len, tid, xv);
+    constexpr int kBV = (kQ * NMAX / 8 + 255) / 256;  // B pieces per thread at N = NMAX
+    const int nv = static_cast<int>(N / 8), pieces = kQ * nv;
+    uint4 bv[kBV];
+    if (p.bc_vec) {
+#pragma unroll
+        for (int q = 0; q < kBV; ++q) {
+            const int i = tid + 256 * q < pieces ? tid + 256 * q : pieces - 1, t = i / nv, n8 = (i % nv) * 8;
+            bv[q] = ssd_ld16(Bm + (b * L + t0 + (t < len ? t : len - 1)) * N + n8);
+        }
+    }
+    const int tl = lane < len ? lane : len - 1;
+    const float dt_raw = E::load(dl, (b * L + t0 + tl) * H + h);
     // cumulative decays in log2 units: exp(cum) = 2^(cum log2 e) on the hardware exp2
     const float a2 = p.A[h] * kSsdLog2e;
     if (tid < kQ) {
-        const float dt = tid < len ? E::load(dl, (b * L + t0 + tid) * H + h) : 0.f;
-        s_w[tid] = dt;
+        const float dt = tid < len ? dt_raw : 0.f;
         s_cum[tid] = dt * a2;
         ssd_cumsum_wave(s_cum, tid);
         s_w[tid] = dt * __builtin_amdgcn_exp2f(s_cum[kQ - 1] - s_cum[tid]);  // exp(cum_{Q-1} - cum_t) delta_t
     }
+    ssd_store_xt(xv, len, tid, s_xt);
     __syncthreads();
     const int nrows = N <= 32 ? 32 : kRows;
-    for (int i = tid; i < nrows * kQ; i += 256) {
-        const int n = i / kQ, t = i % kQ;
-        const float v = (n < N && t < len) ? E::load(Bm, (b * L + t0 + t) * N + n) * s_w[t] : 0.f;
-        s_bw[n][t] = ssd_bf16(v);
+    if (p.bc_vec) {
+        // rows n >= N of s_bw stay as they are: they only feed result rows n >= N, which are not stored
+#pragma unroll
+        for (int q = 0; q < kBV; ++q) {
+            const int i = tid + 256 * q;
+            if (i < pieces) {
+                const int t = i / nv, n8 = (i % nv) * 8;
+                const float w = t < len ? s_w[t] : 0.f;
+                const uint32_t x[4] = {bv[q].x, bv[q].y, bv[q].z, bv[q].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    s_bw[n8 + 2 * k][t] = ssd_bf16(bf16_lo(x[k]) * w);
+                    s_bw[n8 + 2 * k + 1][t] = ssd_bf16(bf16_hi(x[k]) * w);
+                }
+            }
+        }
+    } else {
+        for (int i = tid; i < nrows * kQ; i += 256) {
+            const int n = i / kQ, t = i % kQ;
+            const float v = (n < N && t < len) ? E::load(Bm, (b * L + t0 + t) * N + n) * s_w[t] : 0.f;
+            s_bw[n][t] = ssd_bf16(v);
+        }
     }
     __syncthreads();
     // wave w: rows n0 = 32 (w / 2) (if present), columns p0 = 32 (w % 2)
@@ -232,24 +283,79 @@ __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
     const T* Bm = static_cast<const T*>(p.B);
     const T* Cm = static_cast<const T*>(p.C);
     const T* dl = static_cast<const T*>(p.delta);
-    ssd_load_xt<T>(u + h * kP, b * L + t0, D, len, tid, s_xt);
-    for (int i = tid; i < kQ * npad; i += 256) {
-        const int t = i / npad, n = i % npad;
-        const bool ok = t < len && n < N;
-        s_b[t][n] = ok ? ssd_bf16(E::load(Bm, (b * L + t0 + t) * N + n)) : uint16_t(0);
-        s_c[t][n] = ok ? ssd_bf16(E::load(Cm, (b * L + t0 + t) * N + n)) : uint16_t(0);
-    }
     const uint16_t* Hin = p.Hin + (bh * nC + c) * N * kP;
-    for (int i = tid; i < npad * kP; i += 256) {
-        const int n = i / kP, pp = i % kP;
-        s_ht[pp][n] = n < N ? Hin[n * kP + pp] : uint16_t(0);
+    // every global load first (one wait for memory): X; B, C and H_in in
+    // 16-byte pieces when bc_vec; delta; D of this lane's output column
+    uint4 xv[kQ * kP / 8 / 256];
+    ssd_load_x<T>(u + h * kP, b * L + t0, D, len, tid, xv);
+    constexpr int kBV = (2 * kQ * NMAX / 8 + 255) / 256;  // B and C pieces per thread at N = NMAX
+    constexpr int kHV = (NMAX * kP / 8 + 255) / 256;      // H_in pieces per thread at N = NMAX
+    const int nv = static_cast<int>(N / 8), bpieces = kQ * nv, hpieces = static_cast<int>(N) * (kP / 8);
+    uint4 bcv[kBV], hv[kHV];
+    if (p.bc_vec) {
+#pragma unroll
+        for (int q = 0; q < kBV; ++q) {
+            int i = tid + 256 * q < 2 * bpieces ? tid + 256 * q : 2 * bpieces - 1;
+            const T* src = i < bpieces ? Bm : Cm;
+            i = i < bpieces ? i : i - bpieces;
+            const int t = i / nv, n8 = (i % nv) * 8;
+            bcv[q] = ssd_ld16(src + (b * L + t0 + (t < len ? t : len - 1)) * N + n8);
+        }
+#pragma unroll
+        for (int q = 0; q < kHV; ++q) {
+            const int i = tid + 256 * q < hpieces ? tid + 256 * q : hpieces - 1;
+            hv[q] = ssd_ld16(Hin + i * 8);
+        }
     }
+    const int tl = lane < len ? lane : len - 1;
+    const float dt_raw = E::load(dl, (b * L + t0 + tl) * H + h);
+    const int j = 32 * (wave & 1) + (lane & 31);  // this lane's output column
+    const float* dsp = p.Dskip ? p.Dskip + h * kP + j : p.A;
+    const float dsv = *dsp;
+    const float dsk = p.Dskip ? dsv : 0.f;
     const float a2 = p.A[h] * kSsdLog2e;  // cumulative decays in log2 units
     if (tid < kQ) {
-        const float dt = tid < len ? E::load(dl, (b * L + t0 + tid) * H + h) : 0.f;
+        const float dt = tid < len ? dt_raw : 0.f;
         s_dt[tid] = dt;
         s_cum[tid] = dt * a2;
         ssd_cumsum_wave(s_cum, tid);
+    }
+    ssd_store_xt(xv, len, tid, s_xt);
+    if (p.bc_vec) {
+#pragma unroll
+        for (int q = 0; q < kBV; ++q) {
+            int i = tid + 256 * q;
+            if (i < 2 * bpieces) {
+                uint16_t (*dst)[NMAX + kPad] = i < bpieces ? s_b : s_c;
+                i = i < bpieces ? i : i - bpieces;
+                const int t = i / nv, n8 = (i % nv) * 8;
+                *reinterpret_cast<uint4*>(&dst[t][n8]) = t < len ? bcv[q] : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kHV; ++q) {
+            const int i = tid + 256 * q;
+            if (i < hpieces) {
+                const int n = i / (kP / 8), pp8 = (i % (kP / 8)) * 8;
+                const uint32_t x[4] = {hv[q].x, hv[q].y, hv[q].z, hv[q].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    s_ht[pp8 + 2 * k][n] = static_cast<uint16_t>(x[k]);
+                    s_ht[pp8 + 2 * k + 1][n] = static_cast<uint16_t>(x[k] >> 16);
+                }
+            }
+        }
+    } else {
+        for (int i = tid; i < kQ * npad; i += 256) {
+            const int t = i / npad, n = i % npad;
+            const bool ok = t < len && n < N;
+            s_b[t][n] = ok ? ssd_bf16(E::load(Bm, (b * L + t0 + t) * N + n)) : uint16_t(0);
+            s_c[t][n] = ok ? ssd_bf16(E::load(Cm, (b * L + t0 + t) * N + n)) : uint16_t(0);
+        }
+        for (int i = tid; i < npad * kP; i += 256) {
+            const int n = i / kP, pp = i % kP;
+            s_ht[pp][n] = n < N ? Hin[n * kP + pp] : uint16_t(0);
+        }
     }
     __syncthreads();
     // G = C B^T: wave w forms block (rows t 32 (w / 2), columns s 32 (w % 2)) and
@@ -277,8 +383,6 @@ __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
     for (int r = 0; r < 16; ++r) acc[r] = inter[r] = 0.f;
     ssd_mfma_block<kQ + kPad>(s_m, s_xt, i0, j0, (i0 + 32) / 8, lane, acc);  // causal: k < i0 + 32
     ssd_mfma_block<NMAX + kPad>(s_c, s_ht, i0, j0, npad / 8, lane, inter);
-    const int j = j0 + (lane & 31);
-    const float dsk = p.Dskip ? p.Dskip[h * kP + j] : 0.f;
     float v[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {

@@ -514,6 +514,7 @@ int ssm_ssd_fwd(const ssm_ssd_desc_t* desc, const void* u, const void* delta, co
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.y = y; p.h_last = h_last;
     p.batch = desc->batch; p.seqlen = desc->seqlen; p.dim = desc->dim; p.dstate = desc->dstate;
     p.heads = desc->dim / desc->headdim;
+    p.bc_vec = desc->dstate % 8 == 0 && aligned(B, 16) && aligned(C, 16);
     p.nchunks = (desc->seqlen + ssm::ssd::kQ - 1) / ssm::ssd::kQ;
     const int64_t planes = p.batch * p.heads * p.nchunks;
     char* ws = static_cast<char*>(workspace);

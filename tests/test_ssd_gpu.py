@@ -47,9 +47,31 @@ def test_ssd_lengths(L):
     _check(BASE.scaled(batch=2, dim=128, seqlen=L), seed=41, label=f"L={L}")
 
 
-@pytest.mark.parametrize("N", [1, 5, 33, 64])
+@pytest.mark.parametrize("N", [1, 5, 8, 24, 33, 40, 64])
 def test_ssd_state_sizes(N):
+    """N a multiple of 8 moves B, C and the chunk states in 16-byte pieces (24 and
+    40 leave part of the last round of pieces unused); other N element by element."""
     _check(BASE.scaled(batch=2, dim=192, seqlen=150, dstate=N), seed=42, label=f"N={N}")
+
+
+def test_ssd_unaligned_b_and_c_take_the_element_path():
+    """B and C one element off 16-byte alignment take the element-by-element
+    staging; its result is bit-identical to the 16-byte pieces' (both stage
+    the same bf16 values)."""
+    w = BASE.scaled(batch=2, dim=128, seqlen=333)
+    inp = make_ssd_inputs(w, seed=44, device="cuda")
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        out = buf[1:].view(t.shape)
+        out.copy_(t)
+        return out
+
+    args = (inp["u"], inp["delta"], inp["A"])
+    y, h = ssm_ssd_fwd(*args, inp["Bm"], inp["Cm"], inp["Dskip"], headdim=w.headdim)
+    y2, h2 = ssm_ssd_fwd(*args, shifted(inp["Bm"]), shifted(inp["Cm"]), inp["Dskip"], headdim=w.headdim)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(h, h2)
 
 
 def test_ssd_matches_the_general_scan_kernel():
