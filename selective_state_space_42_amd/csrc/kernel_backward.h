@@ -42,9 +42,13 @@
 //      is (1 - lambda_{t1}) delta_{t1} X_c.  The sweeps issue their loads
 //      kGroup steps at a time.
 // Sums: du, ddelta, dlambda per (b, t, d) over the channel's lanes by DPP
-// butterflies; dB, dC per (b, t, n) over channels, first across the wave's
-// channels by shuffles, then one atomic add per wave; dA per (d, n) and dD
-// per d accumulated per lane over the chunk, one atomic add each.
+// butterflies; dB, dC per (b, t, n) over channels: across the wave's
+// channels by lane permutes, then, when a workgroup's four waves share the
+// batch row and chunk, by LDS atomics over its 16 channels, flushed with one
+// global atomic add per (t, n) per segment; otherwise one atomic add per
+// wave.  dA
+// per (d, n) and dD per d are accumulated per lane over the chunk, one
+// atomic add each.
 // The atomically summed outputs are zeroed first by bwd_zero_kernel.
 // Arithmetic follows the forward kernels' policies (hardware 2^x; sin/cos by
 // hardware on fract(theta / 2 pi) for bf16 I/O, fp64-reduced polynomials for
@@ -90,6 +94,8 @@ struct BwdParams {
     int64_t chunk;         // steps per time chunk (a multiple of kSeg)
     int32_t nchunks;
     int32_t lpc;           // lanes per channel (16 or 64), as the kernels are instantiated
+    int32_t wg_sum;        // LPC = 16 and a batch row's waves a multiple of 4: every workgroup's
+                           // waves share (b, chunk), and dB, dC are summed in LDS per segment
 };
 
 __global__ void __launch_bounds__(256) bwd_zero_kernel(float* a, int64_t na, float* b, int64_t nb, float* c,
@@ -296,6 +302,17 @@ __device__ __forceinline__ float bwd_chan_sum(float v) {
     return v;
 }
 
+// Sum over the wave's four rows of 16 lanes (the four channels of LPC = 16),
+// every lane receiving its column's sum: the upper and lower 32 lanes are
+// swapped and added, then the odd and even rows (gfx950 permlane swaps, no
+// LDS traffic).
+__device__ __forceinline__ float bwd_rows_sum(float v) {
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float s = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Forward sweep storing the state before every segment of kSeg steps (the
 // state after the last segment is not needed, so every swept segment is full).
 template <typename T, int DISC, bool CPLX, int LPC>
@@ -445,11 +462,22 @@ __global__ void __launch_bounds__(256) bwd_adj_carry_kernel(BwdParams p) {
 template <typename T, int DISC, bool CPLX, int LPC>
 __global__ void __launch_bounds__(256) bwd_main_kernel(BwdParams p) {
     constexpr int kSeg = bwd::kSeg, kG = bwd::kGroup, kCPW = BwdGeo<LPC>::kCPW;
+    constexpr int kCw = CPLX ? 2 : 1;
+    constexpr bool kWgSum = LPC == 16;  // the LDS sums of dB and dC exist for one state per lane up to 16
     __shared__ float2 s_h[4][kSeg][64];  // h_t of the segment
     __shared__ float2 s_a[4][kSeg][64];  // alpha_t (ZOH: (rho, e^z - 1))
+    // the workgroup's sums of (dB, dC) per step of the segment and state
+    __shared__ float s_bc[kWgSum ? kSeg : 1][kWgSum ? LPC : 1][2 * kCw];
     bwd_assume_disjoint(p);
     const BwdGeo<LPC> g = bwd_geo<LPC, CPLX>(p, true);
-    if (g.c >= p.nchunks) return;  // whole waves; no barrier follows
+    // With wg_sum every wave of the workgroup is in the grid and shares
+    // (b, chunk), so all run the same segments and meet the same barriers.
+    const bool wg_sum = kWgSum && p.wg_sum;
+    if (g.c >= p.nchunks) return;  // whole waves, never with wg_sum (the grid is whole workgroups then)
+    if (wg_sum) {
+        for (int i = threadIdx.x; i < kSeg * LPC * 2 * kCw; i += 256) (&s_bc[0][0][0])[i] = 0.f;
+        __syncthreads();
+    }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
     const int64_t s0 = (g.b * D + g.d) * N + g.nc;
@@ -638,25 +666,55 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(BwdParams p) {
                     if constexpr (DISC == kTrap) qs.dlam[otc] = glam;
                     accD += dy * x;
                 }
-                // per (b, t, n): sums over the wave's channels, then one atomic per wave
-#pragma unroll
-                for (int off = LPC; off < 64; off <<= 1) {
-                    gBr += __shfl_xor(gBr, off, 64);
-                    gCr += __shfl_xor(gCr, off, 64);
+                // per (b, t, n): sums over the wave's channels (LPC = 16: its four
+                // rows; LPC = 64: one channel), then over the workgroup's 16
+                // channels by LDS atomics flushed once per segment (wg_sum), or
+                // one global atomic per wave
+                if constexpr (LPC == 16) {
+                    gBr = bwd_rows_sum(gBr);
+                    gCr = bwd_rows_sum(gCr);
                     if constexpr (CPLX) {
-                        gBi += __shfl_xor(gBi, off, 64);
-                        gCi += __shfl_xor(gCi, off, 64);
+                        gBi = bwd_rows_sum(gBi);
+                        gCi = bwd_rows_sum(gCi);
                     }
                 }
-                if (lane < LPC && g.n < N) {
-                    atomicAdd(qs.dB + obn, gBr);
-                    atomicAdd(qs.dC + obn, gCr);
-                    if constexpr (CPLX) {
-                        atomicAdd(qs.dB + obn + 1, gBi);
-                        atomicAdd(qs.dC + obn + 1, gCi);
+                if (kWgSum && wg_sum) {
+                    if (lane < LPC) {
+                        float* acc = &s_bc[kWgSum ? k : 0][kWgSum ? g.n : 0][0];
+                        atomicAdd(acc, gBr);
+                        atomicAdd(acc + kCw, gCr);
+                        if constexpr (CPLX) {
+                            atomicAdd(acc + 1, gBi);
+                            atomicAdd(acc + kCw + 1, gCi);
+                        }
+                    }
+                } else {
+                    if (lane < LPC && g.n < N) {
+                        atomicAdd(qs.dB + obn, gBr);
+                        atomicAdd(qs.dC + obn, gCr);
+                        if constexpr (CPLX) {
+                            atomicAdd(qs.dB + obn + 1, gBi);
+                            atomicAdd(qs.dC + obn + 1, gCi);
+                        }
                     }
                 }
             }
+        }
+        if (kWgSum && wg_sum) {
+            // every wave's adds of the segment are in; each sum goes out by one
+            // atomic and is cleared by the thread that read it, then the next
+            // segment may add again
+            __syncthreads();
+            const int per_k = static_cast<int>(N) * 2 * kCw;
+            for (int i = threadIdx.x; i < len * per_k; i += 256) {
+                const int k = i / per_k, r = i % per_k, n = r / (2 * kCw), comp = r % (2 * kCw);
+                float* cell = &s_bc[kWgSum ? k : 0][kWgSum ? n : 0][comp];
+                const float v = *cell;
+                *cell = 0.f;
+                float* dst = comp < kCw ? p.dB : p.dC;
+                atomicAdd(dst + ((g.b * L + t0 + k) * N + n) * kCw + comp % kCw, v);
+            }
+            __syncthreads();
         }
     }
     if (g.ok) {

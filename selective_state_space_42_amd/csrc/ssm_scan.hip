@@ -486,6 +486,7 @@ int ssm_scan_bwd(const ssm_scan_desc_t* desc, const void* u, const void* delta, 
     p.chunk = chunk;
     p.nchunks = static_cast<int32_t>(nchunks);
     p.lpc = bwd_lpc(desc);
+    p.wg_sum = p.lpc == 16 && ((desc->dim + 3) / 4) % 4 == 0;  // a batch row's waves (4 channels each) fill workgroups
     hipStream_t s = static_cast<hipStream_t>(stream);
     return desc->io_dtype == SSM_DTYPE_F32 ? launch_bwd<float>(desc, p, s) : launch_bwd<uint16_t>(desc, p, s);
 }

@@ -100,6 +100,32 @@ def test_backward_time_chunks(mode):
     _compare(w, inp, dy, dh_last=dh, h0=h0, label=f"chunks {mode}")
 
 
+@pytest.mark.parametrize("mode", ["real_zoh_f32", "real_trap_bf16", "complex_trap_f32", "complex_trap_bf16"])
+def test_backward_workgroup_sums(mode):
+    """D a multiple of 16: each workgroup's four waves share the batch row and
+    time chunk, and dB, dC are summed over its channels in LDS per segment
+    (compared in full here).  Ragged segments, two time chunks, N = 16."""
+    w = MODES[mode].scaled(batch=2, dim=32, seqlen=333)
+    inp = make_inputs(w, seed=26, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(8)
+    dy = torch.randn(inp["u"].shape, generator=gen, device="cuda").to(inp["u"].dtype)
+    _compare(w, inp, dy, label=f"wg sums {mode}")
+
+
+@pytest.mark.parametrize("mode", ["real_trap_f32", "complex_trap_bf16"])
+def test_backward_workgroup_sums_time_chunks_odd_n(mode):
+    """The LDS sums with four time chunks, N = 7 (lanes past N add zeros),
+    nonzero h0 and dh_last."""
+    w = MODES[mode].scaled(batch=1, dim=16, seqlen=1000, dstate=7)
+    inp = make_inputs(w, seed=27, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    shape = (w.batch, w.dim, w.dstate) + ((2,) if w.is_complex else ())
+    dy = torch.randn(inp["u"].shape, generator=gen, device="cuda").to(inp["u"].dtype)
+    dh = torch.randn(shape, generator=gen, device="cuda")
+    h0 = torch.randn(shape, generator=gen, device="cuda")
+    _compare(w, inp, dy, dh_last=dh, h0=h0, label=f"wg sums chunks {mode}")
+
+
 @pytest.mark.parametrize("N", [1, 33, 64])
 def test_backward_state_sizes(N):
     w = MODES["complex_trap_f32"].scaled(batch=2, dim=6, seqlen=45, dstate=N)
