@@ -536,25 +536,31 @@ __global__ void __launch_bounds__(256) mimo_carry_kernel(MimoParams p) {
 }
 
 // One decode step of the MIMO recurrence with the state in memory; two
-// states per lane.  PAIRS: N even and h aligned for a lane's two states, so
-// the state moves with one vector load and store per lane.
+// states per lane.  A workgroup holds 256 / lpc channels of one batch row,
+// whose B, C (and B_prev) rows it stages in LDS as fp32 once: each lane
+// then reads its states' runs from LDS instead of every lane loading them.
+// PAIRS: N even and h aligned for a lane's two states, so the state moves
+// with one vector load and store per lane.
 template <typename T, int DISC, bool CPLX, int R, bool PAIRS>
 __global__ void __launch_bounds__(256) mimo_step_kernel(MimoStepParams p) {
-    constexpr int kCw = CPLX ? 2 : 1, kES = sizeof(T);
+    constexpr int kCw = CPLX ? 2 : 1, kES = sizeof(T), kRun = R * kCw;
+    constexpr int NA = DISC == kTrap ? 3 : 2;  // staged rows: B, C (and B_prev)
+    constexpr int kEC = (64 * kRun + 255) / 256;  // staged values per thread and row at N = 64
     constexpr int SC = std::is_same_v<T, uint16_t> ? kSinCosHw : kSinCosWide;
-    const int lane = threadIdx.x & 63, lpc = p.lpc;
-    const int64_t D = p.dim, N = p.dstate, BD = p.batch * p.dim;
-    const int64_t gw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
-    const int64_t ch_raw = gw * (64 / lpc) + lane / lpc;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lpc = p.lpc;
+    const int64_t D = p.dim, N = p.dstate;
+    const int64_t wpr = (D * lpc + 255) / 256;  // workgroups per batch row
+    const int64_t b = blockIdx.x / wpr;
+    const int64_t d_raw = (blockIdx.x % wpr) * (256 / lpc) + wave * (64 / lpc) + lane / lpc;
     const int pr = lane & (lpc - 1);
     const int64_t n0_raw = 2 * pr;
-    const bool ch_ok = ch_raw < BD;
+    const bool ch_ok = d_raw < D;
     const bool ok[2] = {ch_ok && n0_raw < N, ch_ok && n0_raw + 1 < N};
-    const int64_t ch = ch_ok ? ch_raw : BD - 1, n0 = n0_raw < N ? n0_raw : N - 1;
+    const int64_t d = ch_ok ? d_raw : D - 1, n0 = n0_raw < N ? n0_raw : N - 1;
     const int64_t n1 = n0 + 1 < N ? n0 + 1 : n0;
-    const int64_t b = ch / D, d = ch % D;
+    const int64_t ch = b * D + d;
     const int64_t sidx[2] = {ch * N + n0, ch * N + n1};
-    const int64_t bn[2] = {(b * N + n0) * R * kCw, (b * N + n1) * R * kCw};
+    const int E = static_cast<int>(N) * kRun;
 
     // Every load is issued up front and without branches: a missing theta
     // or previous step reads delta's or this step's element instead and is
@@ -563,15 +569,26 @@ __global__ void __launch_bounds__(256) mimo_step_kernel(MimoStepParams p) {
     const float dsk = p.Dskip ? p.Dskip[d] : 0.f;  // the one branch, before the other loads
     const T* delta = static_cast<const T*>(p.delta);
     const T* uu = static_cast<const T*>(p.u);
-    const T* Bm = static_cast<const T*>(p.B);
     const bool has_th = CPLX && p.theta;
     const bool prev = DISC == kTrap && p.u_prev;
     const T* thp = has_th ? static_cast<const T*>(p.theta) : nullptr;
     const T* upp = prev ? static_cast<const T*>(p.u_prev) : uu;
-    const T* bpp = prev ? static_cast<const T*>(p.B_prev) : Bm;
+    // the batch row's B, C (and B_prev; B when there is no previous step,
+    // whose term is masked) through buffer resources: values past E read 0
+    const T* rows[3] = {static_cast<const T*>(p.B), static_cast<const T*>(p.C),
+                        prev ? static_cast<const T*>(p.B_prev) : static_cast<const T*>(p.B)};
+    uint32_t sv[NA][kEC];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+        const rsrc_t rs = make_rsrc(rows[a] + b * E, static_cast<uint32_t>(E) * kES);
+#pragma unroll
+        for (int i = 0; i < kEC; ++i) {
+            const int e = tid + 256 * i;
+            sv[a][i] = Buf<T>::load_raw(rs, e < E ? static_cast<uint32_t>(e) * kES : kOutOfRange);
+        }
+    }
     Run<kES> rdt, rlam, rth[2];
     Run<R * kES> rx, rxp;
-    Run<R * kCw * kES> rb[2], rc[2], rbp[2];
     load_run(delta + ch, rdt);
     load_run(uu + ch * R, rx);
     if constexpr (DISC == kTrap) {
@@ -579,12 +596,8 @@ __global__ void __launch_bounds__(256) mimo_step_kernel(MimoStepParams p) {
         load_run(upp + ch * R, rxp);
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        load_run(Bm + bn[j], rb[j]);
-        load_run(static_cast<const T*>(p.C) + bn[j], rc[j]);
+    for (int j = 0; j < 2; ++j)
         if constexpr (CPLX) load_run(has_th ? thp + sidx[j] : delta + ch, rth[j]);
-        if constexpr (DISC == kTrap) load_run(bpp + bn[j], rbp[j]);
-    }
     const float a_n[2] = {p.A[d * N + n0], p.A[d * N + n1]};
     float hr[2], hi[2] = {0.f, 0.f};
     if constexpr (PAIRS) {
@@ -602,6 +615,15 @@ __global__ void __launch_bounds__(256) mimo_step_kernel(MimoStepParams p) {
             if constexpr (CPLX) hi[j] = p.h[sidx[j] * 2 + 1];
         }
     }
+    // stage the rows (widened) and wait for the whole workgroup's
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int i = 0; i < kEC; ++i) {
+            const int e = tid + 256 * i;
+            if (e < E) mimo_smem[a * E + e] = Buf<T>::widen(sv[a][i]);
+        }
+    __syncthreads();
 
     float x[R], xp[R];
 #pragma unroll
@@ -615,11 +637,19 @@ __global__ void __launch_bounds__(256) mimo_step_kernel(MimoStepParams p) {
     const float dmask = pr == 0 ? dsk : 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) part[r] = dmask * x[r];
+    const int64_t nn[2] = {n0, n1};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+        Run<kRun * 4> rb, rc;
+        load_run(mimo_smem + nn[j] * kRun, rb);
+        load_run(mimo_smem + E + nn[j] * kRun, rc);
         float qr, qi, qpr = 0.f, qpi = 0.f;
-        mimo_q<T, CPLX, R>(rb[j], x, &qr, &qi);
-        if constexpr (DISC == kTrap) mimo_q<T, CPLX, R>(rbp[j], xp, &qpr, &qpi);  // zero without a previous step
+        mimo_q<float, CPLX, R>(rb, x, &qr, &qi);
+        if constexpr (DISC == kTrap) {  // zero without a previous step (xp = 0)
+            Run<kRun * 4> rbp;
+            load_run(mimo_smem + 2 * E + nn[j] * kRun, rbp);
+            mimo_q<float, CPLX, R>(rbp, xp, &qpr, &qpi);
+        }
         const float a = a_n[j];
         const float th = has_th ? run_elem<T>(rth[j], 0) : 0.f;
         float ar, ai;
@@ -627,8 +657,8 @@ __global__ void __launch_bounds__(256) mimo_step_kernel(MimoStepParams p) {
         if (!ok[j]) hr[j] = hi[j] = 0.f;  // a masked state adds nothing below
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            part[r] = __builtin_fmaf(run_elem<T>(rc[j], r * kCw), hr[j], part[r]);
-            if constexpr (CPLX) part[r] = __builtin_fmaf(-run_elem<T>(rc[j], r * kCw + 1), hi[j], part[r]);
+            part[r] = __builtin_fmaf(run_elem<float>(rc, r * kCw), hr[j], part[r]);
+            if constexpr (CPLX) part[r] = __builtin_fmaf(-run_elem<float>(rc, r * kCw + 1), hi[j], part[r]);
         }
     }
     if constexpr (PAIRS) {
@@ -649,6 +679,12 @@ __global__ void __launch_bounds__(256) mimo_step_kernel(MimoStepParams p) {
     const float sum = mimo_reduce_scatter<R>(part, mimo_up_mask<R>(pr, lpc), lpc);
     const int r_own = mimo_out_index<R>(pr, lpc);
     if (ch_ok && (pr & (lpc / R - 1)) == 0) Elem<T>::store(static_cast<T*>(p.y), ch * R + r_own, sum);
+}
+
+// Bytes of LDS a mimo_step_kernel workgroup takes: the B, C (and B_prev)
+// rows of one batch row in fp32.
+inline size_t mimo_step_lds_bytes(int64_t dstate, int R, bool cplx, bool trap) {
+    return static_cast<size_t>((trap ? 3 : 2) * dstate * R * (cplx ? 2 : 1) * 4);
 }
 
 }  // namespace ssm

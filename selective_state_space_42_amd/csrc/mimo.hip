@@ -24,12 +24,12 @@ hipError_t scan_r(const MimoParams& p, hipStream_t s) {
 
 template <typename T, int DISC, bool CPLX, int R>
 hipError_t step_r(const MimoStepParams& p, hipStream_t s) {
-    const int64_t waves = (p.batch * p.dim * p.lpc + 63) / 64;
-    const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+    const dim3 grid(static_cast<unsigned>(p.batch * ((p.dim * p.lpc + 255) / 256)));
+    const size_t lds = mimo_step_lds_bytes(p.dstate, R, CPLX, DISC == kTrap);
     if (p.pairs)
-        hipLaunchKernelGGL((mimo_step_kernel<T, DISC, CPLX, R, true>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((mimo_step_kernel<T, DISC, CPLX, R, true>), grid, dim3(256), lds, s, p);
     else
-        hipLaunchKernelGGL((mimo_step_kernel<T, DISC, CPLX, R, false>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((mimo_step_kernel<T, DISC, CPLX, R, false>), grid, dim3(256), lds, s, p);
     return hipGetLastError();
 }
 

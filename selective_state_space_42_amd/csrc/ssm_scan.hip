@@ -598,7 +598,7 @@ int ssm_mimo_step(const ssm_mimo_desc_t* desc, const void* u, const void* delta,
     const size_t ba = desc->rank * cw * es < 16 ? desc->rank * cw * es : 16;
     if ((u_prev && !aligned(u_prev, ua)) || (B_prev && !aligned(B_prev, ba))) return SSM_ERR_INVALID_ARGUMENT;
     const int lpc = mimo_lpc(desc);
-    if (((desc->batch * desc->dim * lpc + 63) / 64 + 3) / 4 > INT32_MAX) return SSM_ERR_UNSUPPORTED;
+    if (desc->batch * ((desc->dim * lpc + 255) / 256) > INT32_MAX) return SSM_ERR_UNSUPPORTED;
 
     ssm::MimoStepParams p{};
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.theta = theta; p.lambda = lambda;

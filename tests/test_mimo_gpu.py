@@ -202,3 +202,23 @@ def test_mimo_decode_full_size_sampled():
     w = MIMO_DECODE_WORKLOADS["mimo_decode_complex_trap_bf16_b256_d2560_n16_r4"]
     idx = sorted(np.random.default_rng(5).choice(w.dim, 16, replace=False).tolist())
     _decode_check(w, seed=19, steps=3, d_index=idx, label="mimo decode full size")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mimo_decode_first_step_without_previous(dtype):
+    """A trapezoidal step with no previous step (u_prev = B_prev = NULL: the
+    q_{t-1} term is zero, as at the start of a sequence without q0), D = 40:
+    a batch row's second workgroup holds 8 channels and 24 idle ones."""
+    w = _work("trap", True, dtype, batch=2, dim=40, seqlen=1, dstate=16)
+    inp = make_mimo_inputs(w, seed=20, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(10)
+    h = torch.randn((w.batch, w.dim, w.dstate, 2), generator=g, device="cuda")
+    h_start = h.clone()
+    x = _step_slice(inp, 0)
+    y = ssm_mimo_step(x["u"], x["delta"], x["A"], x["Bm"], x["Cm"], x["Dskip"], x["theta"], x["lam"], h=h,
+                      disc="trap")
+    torch.cuda.synchronize()
+    ref_y, ref_h, _ = _oracle(w, channel_sample(inp, range(w.dim)), h0=_host(h_start))
+    err_y, err_h = _errs(w, y[:, None], h, ref_y, ref_h)
+    print(f"first step {dtype} err_y={err_y:.3e} err_h={err_h:.3e}", flush=True)
+    assert err_y <= TOL[dtype] and err_h <= TOL[dtype], (err_y, err_h)
