@@ -541,7 +541,8 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(BwdParams p) {
             for (int g0 = 0; g0 < len; g0 += kG) {
                 BwdRaw<CPLX> rw[kG];
 #pragma unroll
-                for (int j = 0; j < kG; ++j) bwd_load<T, DISC, CPLX, true>(qs, st, g0 + j < len ? g0 + j : len - 1, rw[j]);
+                for (int j = 0; j < kG; ++j)
+                    bwd_load<T, DISC, CPLX, true>(qs, st, g0 + j < len ? g0 + j : len - 1, rw[j]);
 #pragma unroll
                 for (int j = 0; j < kG; ++j) {
                     if (g0 + j >= len) break;  // uniform

@@ -267,7 +267,8 @@ struct MimoStage {
 
 template <typename T, bool CPLX, int R, int NA>
 __device__ __forceinline__ void mimo_stage_load(MimoStage<T, CPLX, R, NA>& sg, const T* const (&arr)[NA],
-                                                int64_t row0, int rows, int E, const uint32_t (&eoff)[MimoStage<T, CPLX, R, NA>::kEC]) {
+                                                int64_t row0, int rows, int E,
+                                                const uint32_t (&eoff)[MimoStage<T, CPLX, R, NA>::kEC]) {
     constexpr uint32_t es = sizeof(T);
     const uint32_t rowb = static_cast<uint32_t>(E) * es;
 #pragma unroll

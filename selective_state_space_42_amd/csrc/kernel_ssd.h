@@ -99,7 +99,9 @@ __device__ __forceinline__ void ssd_mfma_block(const uint16_t (*a_rows)[kStride]
 constexpr float kSsdLog2e = 1.4426950408889634f;
 
 // row of element r of a lane's 32 x 32 accumulator block
-__device__ __forceinline__ int ssd_acc_row(int i0, int lane, int r) { return i0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+__device__ __forceinline__ int ssd_acc_row(int i0, int lane, int r) {
+    return i0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
 
 // NMAX: the largest N the instantiation handles (16 or 64); it sizes the LDS
 // tiles, so small state sizes leave room for more resident workgroups.
@@ -400,7 +402,8 @@ __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
     T* y = static_cast<T*>(p.y) + h * kP;
     for (int i = tid; i < kQ * kP / 8; i += 256) {
         const int t = i / (kP / 8), p8 = (i % (kP / 8)) * 8;
-        if (t < len) *reinterpret_cast<uint4*>(y + (b * L + t0 + t) * D + p8) = *reinterpret_cast<const uint4*>(&s_y[t][p8]);
+        if (t < len)
+            *reinterpret_cast<uint4*>(y + (b * L + t0 + t) * D + p8) = *reinterpret_cast<const uint4*>(&s_y[t][p8]);
     }
 }
 

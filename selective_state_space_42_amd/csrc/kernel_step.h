@@ -4,7 +4,8 @@
 // For every (b, d, n):  h[n] <- alpha[n] h[n] + bterm[n],  y = Re(sum_n C[n] h[n]) + D u.
 // The trapezoid's term for the previous step, q_{t-1}[n] = B_{t-1}[n] u_{t-1},
 // is formed from the previous step's B and u (per (b, n) and per (b, d)), so
-// the only per-element memory traffic is the state itself and theta.  This is the same recurrence and discretisations as the scan
+// the only per-element memory traffic is the state itself and theta.  This
+// is the same recurrence and discretisations as the scan
 // (the fengwang.github.io essay's scan section; the discretisation table of
 // the ai.tomabc.com Mamba-3 story), one step at a time: recurrent inference
 // carries a fixed-size state from token to token (the ai.tomabc.com story's
@@ -156,7 +157,8 @@ __global__ void __launch_bounds__(256) scan_step_kernel(StepParams p) {
     const float skip = p.Dskip ? dsk : 0.f;
     if (!ok) {  // states past N (or past the channels) take no part
 #pragma unroll
-        for (int j = 0; j < 2; ++j) v.a[j] = v.th[j] = v.br[j] = v.bi[j] = v.cr[j] = v.ci[j] = v.pbr[j] = v.pbi[j] = v.hr[j] = v.hi[j] = 0.f;
+        for (int j = 0; j < 2; ++j)
+            v.a[j] = v.th[j] = v.br[j] = v.bi[j] = v.cr[j] = v.ci[j] = v.pbr[j] = v.pbi[j] = v.hr[j] = v.hi[j] = 0.f;
     }
 
     float part = 0.f;
