@@ -203,7 +203,7 @@ int ssm_scan_step(const ssm_scan_desc_t *desc, const void *u, const void *delta,
 
 /* Bytes of workspace ssm_scan_bwd needs for `desc`: the state before every
  * 12-step segment, ceil(L/12) * B * D * N * (8 complex, 4 real) bytes
- * (e.g. 3.58 GB for B=4, L=8192, D=2560, N=16 complex), rounded up to 256,
+ * (e.g. 0.90 GB for B=4, L=8192, D=2560, N=16 complex), rounded up to 256,
  * plus, when the sequence is cut into time chunks (problems with fewer than
  * about 2^19 (channel, state) lanes, chunks of at least 256 steps), one
  * adjoint pair per chunk and (b, d, n): chunks * B * D * N * (16 complex,
