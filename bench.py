@@ -630,8 +630,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this scan shards along channels with no communication, "
-              "and multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only (use --gpus 1): the scan shards along batch rows and channels "
+              "with no communication between GPUs, so N GPUs each run this one-GPU measurement on their share.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
