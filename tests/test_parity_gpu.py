@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from parity_util import TOL, check_workload, rel_err, rel_err_complex, run_gpu
-from selective_state_space_42_amd.inputs import WORKLOADS
+from selective_state_space_42_amd.inputs import WORKLOADS, make_inputs
 from selective_state_space_42_amd.scan import ScanError
 
 pytestmark = pytest.mark.gpu
@@ -97,6 +97,32 @@ def test_wide_rotation_angles(mode, scale, algo):
     range) and past many revolutions."""
     w = MODES[mode].scaled(name=f"{mode}_theta{scale:g}", batch=2, dim=19, seqlen=300, theta_scale=scale)
     _run(w, algo)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("mode", ["real_zoh_f32", "real_trap_f32", "complex_euler_f32", "complex_trap_bf16"])
+def test_degenerate_values(mode, algo):
+    """Degenerate values the method admits, mixed into ordinary inputs: A = 0
+    for some states (no decay; ZOH's weight becomes delta), delta = 0 at some
+    steps (the state is held and nothing enters), lambda exactly 0 and 1 (the
+    trapezoid's two one-sided rules) and theta = 0 for some states."""
+    w = MODES[mode].scaled(name=f"{mode}_degenerate", batch=2, dim=21, seqlen=257)
+    inp = make_inputs(w, 31, device="cuda")
+    A = inp["A"].clone()
+    A[::3, 1::4] = 0.0
+    delta = inp["delta"].clone()
+    delta[:, 5::17] = 0
+    inputs = dict(inp, A=A, delta=delta)
+    if inp["lam"] is not None:
+        lam = inp["lam"].clone()
+        lam[:, ::11] = 0
+        lam[:, 3::11] = 1
+        inputs["lam"] = lam
+    if inp["theta"] is not None:
+        theta = inp["theta"].clone()
+        theta[..., ::5] = 0
+        inputs["theta"] = theta
+    _run(w, algo, inputs=inputs)
 
 
 GOLDEN = sorted(glob.glob(os.path.join(os.path.dirname(__file__), "golden", "*.npz")))
