@@ -263,8 +263,9 @@ __global__ void __launch_bounds__(256) ssd_pass_kernel(SsdParams p) {
     }
 }
 
+// Six workgroups per CU: LDS of about 19 KB (N <= 16) and at most 80 VGPRs.
 template <typename T, int NMAX>
-__global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
+__global__ void __launch_bounds__(256, 6) ssd_out_kernel(SsdParams p) {
     using namespace ssd;
     using E = Elem<T>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -274,13 +275,19 @@ __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
     const int len = static_cast<int>(L - t0 < kQ ? L - t0 : kQ);
     const int npad = static_cast<int>((N + 7) / 8 * 8);  // K of the products over n
     // bf16 MFMA operands, k contiguous: C and B rows (k = n), H_in transposed
-    // (rows p, k = n), X transposed (rows p, k = s), M (rows t, k = s)
-    __shared__ __align__(16) uint16_t s_c[kQ][NMAX + kPad];
-    __shared__ __align__(16) uint16_t s_b[kQ][NMAX + kPad];
-    __shared__ __align__(16) uint16_t s_ht[kP][NMAX + kPad];
-    __shared__ __align__(16) uint16_t s_xt[kP][kQ + kPad];
-    __shared__ __align__(16) uint16_t s_m[kQ][kQ + kPad];
+    // (rows p, k = n), X transposed (rows p, k = s), M (rows t, k = s).  M
+    // (and later the output tile) takes the space of C, B and H_in, which are
+    // dead once every wave has formed its G and C H_in blocks.
+    static_assert(kP == kQ, "H_in rows share the C and B tiles' shape");
+    constexpr int kRowN = NMAX + kPad, kRowQ = kQ + kPad;
+    constexpr int kUnion = 3 * kQ * kRowN > kQ * kRowQ ? 3 * kQ * kRowN : kQ * kRowQ;
+    __shared__ __align__(16) uint16_t s_u[kUnion];
+    __shared__ __align__(16) uint16_t s_xt[kP][kRowQ];
     __shared__ float s_cum[kQ], s_dt[kQ];
+    uint16_t (*s_c)[kRowN] = reinterpret_cast<uint16_t (*)[kRowN]>(s_u);
+    uint16_t (*s_b)[kRowN] = reinterpret_cast<uint16_t (*)[kRowN]>(s_u + kQ * kRowN);
+    uint16_t (*s_ht)[kRowN] = reinterpret_cast<uint16_t (*)[kRowN]>(s_u + 2 * kQ * kRowN);
+    uint16_t (*s_m)[kRowQ] = reinterpret_cast<uint16_t (*)[kRowQ]>(s_u);
     const T* u = static_cast<const T*>(p.u);
     const T* Bm = static_cast<const T*>(p.B);
     const T* Cm = static_cast<const T*>(p.C);
@@ -328,7 +335,7 @@ __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
         for (int q = 0; q < kBV; ++q) {
             int i = tid + 256 * q;
             if (i < 2 * bpieces) {
-                uint16_t (*dst)[NMAX + kPad] = i < bpieces ? s_b : s_c;
+                uint16_t (*dst)[kRowN] = i < bpieces ? s_b : s_c;
                 i = i < bpieces ? i : i - bpieces;
                 const int t = i / nv, n8 = (i % nv) * 8;
                 *reinterpret_cast<uint4*>(&dst[t][n8]) = t < len ? bcv[q] : make_uint4(0, 0, 0, 0);
@@ -360,31 +367,29 @@ __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
         }
     }
     __syncthreads();
-    // G = C B^T: wave w forms block (rows t 32 (w / 2), columns s 32 (w % 2)) and
-    // turns it into M = G o exp(cum_t - cum_s) o delta_s (zero above the
-    // diagonal); the block above the diagonal is never read
-    const int gi = 32 * (wave >> 1), gs = 32 * (wave & 1);
-    if (gs <= gi) {
-        ssd_f32x16 g;
+    // wave w: G = C B^T block (rows t 32 (w / 2), columns s 32 (w % 2); the
+    // block above the diagonal is never read) and the same block of C H_in,
+    // then, once C, B and H_in are dead, M = G o exp(cum_t - cum_s) o delta_s
+    // (zero above the diagonal) over their space
+    const int i0 = 32 * (wave >> 1), j0 = 32 * (wave & 1);
+    ssd_f32x16 g, acc, inter;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) g[r] = 0.f;
-        ssd_mfma_block<NMAX + kPad>(s_c, s_b, gi, gs, npad / 8, lane, g);
-        const int sc = gs + (lane & 31);
+    for (int r = 0; r < 16; ++r) g[r] = acc[r] = inter[r] = 0.f;
+    if (j0 <= i0) ssd_mfma_block<kRowN>(s_c, s_b, i0, j0, npad / 8, lane, g);
+    ssd_mfma_block<kRowN>(s_c, s_ht, i0, j0, npad / 8, lane, inter);
+    __syncthreads();
+    if (j0 <= i0) {
+        const int sc = j0 + (lane & 31);
         const float cs = s_cum[sc], ds = s_dt[sc];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int t = ssd_acc_row(gi, lane, r);
+            const int t = ssd_acc_row(i0, lane, r);
             s_m[t][sc] = ssd_bf16(sc <= t ? g[r] * __builtin_amdgcn_exp2f(s_cum[t] - cs) * ds : 0.f);
         }
     }
     __syncthreads();
     // Y = M X + diag(exp(cum)) C H_in: wave w computes rows i0, columns j0
-    const int i0 = 32 * (wave >> 1), j0 = 32 * (wave & 1);
-    ssd_f32x16 acc, inter;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = inter[r] = 0.f;
-    ssd_mfma_block<kQ + kPad>(s_m, s_xt, i0, j0, (i0 + 32) / 8, lane, acc);  // causal: k < i0 + 32
-    ssd_mfma_block<NMAX + kPad>(s_c, s_ht, i0, j0, npad / 8, lane, inter);
+    ssd_mfma_block<kRowQ>(s_m, s_xt, i0, j0, (i0 + 32) / 8, lane, acc);  // causal: k < i0 + 32
     float v[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -395,7 +400,7 @@ __global__ void __launch_bounds__(256) ssd_out_kernel(SsdParams p) {
     // the output tile goes through LDS (rows t, columns p; M's space, free once
     // every wave has finished its products) and out as 16-byte row pieces
     __syncthreads();
-    uint16_t (*s_y)[kQ + kPad] = s_m;
+    uint16_t (*s_y)[kRowQ] = s_m;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s_y[ssd_acc_row(i0, lane, r)][j] = ssd_bf16(v[r]);
     __syncthreads();
