@@ -202,8 +202,8 @@ int ssm_scan_step(const ssm_scan_desc_t *desc, const void *u, const void *delta,
                   const void *u_prev, const void *B_prev, float *h, void *y, void *stream);
 
 /* Bytes of workspace ssm_scan_bwd needs for `desc`: the state before every
- * 12-step segment, ceil(L/12) * B * D * N * (8 complex, 4 real) bytes
- * (e.g. 0.90 GB for B=4, L=8192, D=2560, N=16 complex), rounded up to 256,
+ * 8-step segment, ceil(L/8) * B * D * N * (8 complex, 4 real) bytes
+ * (e.g. 1.34 GB for B=4, L=8192, D=2560, N=16 complex), rounded up to 256,
  * plus, when the sequence is cut into time chunks (problems with fewer than
  * about 2^19 (channel, state) lanes, chunks of at least 256 steps), one
  * adjoint pair per chunk and (b, d, n): chunks * B * D * N * (16 complex,

@@ -63,7 +63,7 @@
 namespace ssm {
 
 namespace bwd {
-constexpr int kSeg = 12;  // steps per recompute segment (states kept in LDS)
+constexpr int kSeg = 8;   // steps per recompute segment (states kept in LDS)
 constexpr int kGroup = 4;  // steps whose loads are issued together
 }
 
@@ -459,8 +459,12 @@ __global__ void __launch_bounds__(256) bwd_adj_carry_kernel(BwdParams p) {
 // The reverse sweep of one chunk (every chunk in parallel), segment by
 // segment from the last: recompute the segment's states and decays from its
 // snapshot into wave-private LDS, then sweep it backwards.
+// At most 128 VGPRs so that four workgroups fit a CU (with 8-step segments
+// the LDS takes 34 KB); the few values that spill cost less than the lost
+// occupancy (measured 15.4 against 16.2 ms on a 4 x 2560 x 8192 x 16 complex
+// problem, which 12-step segments at three workgroups per CU took).
 template <typename T, int DISC, bool CPLX, int LPC>
-__global__ void __launch_bounds__(256) bwd_main_kernel(BwdParams p) {
+__global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p) {
     constexpr int kSeg = bwd::kSeg, kG = bwd::kGroup, kCPW = BwdGeo<LPC>::kCPW;
     constexpr int kCw = CPLX ? 2 : 1;
     constexpr bool kWgSum = LPC == 16;  // the LDS sums of dB and dC exist for one state per lane up to 16

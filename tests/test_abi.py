@@ -177,17 +177,17 @@ def test_backward_argument_rules():
     assert call_bwd(desc(N=65)) == UNSUPPORTED
     d = desc(B=2, L=100, D=8, N=16, cplx=True)
     need = scan.ssm_scan_bwd_workspace_bytes(d)
-    assert need == 9 * 2 * 8 * 16 * 8                                  # ceil(100/12) snapshots of the state
+    assert need == 13 * 2 * 8 * 16 * 8                                 # ceil(100/8) snapshots of the state
     assert call_bwd(d, ws=0) == WS_SMALL
     assert call_bwd(d, ws_bytes=need - 1) == WS_SMALL
     assert call_bwd(d, ws=P + 64, ws_bytes=need) == INVALID            # not 256-byte aligned
-    # a narrow, long problem: 342 segments of snapshots (rounded up to 256 bytes) plus 16
-    # chunks of 264 steps (whole segments), one (Q, R) adjoint pair each per (b, d, n)
+    # a narrow, long problem: 512 segments of snapshots (rounded up to 256 bytes) plus 16
+    # chunks of 256 steps (whole segments), one (Q, R) adjoint pair each per (b, d, n)
     r256 = lambda v: (v + 255) // 256 * 256
     d = desc(B=1, L=4096, D=8, N=16, cplx=True)
-    assert scan.ssm_scan_bwd_workspace_bytes(d) == r256(342 * 8 * 16 * 8) + 16 * 8 * 16 * 16
+    assert scan.ssm_scan_bwd_workspace_bytes(d) == r256(512 * 8 * 16 * 8) + 16 * 8 * 16 * 16
     d = desc(B=1, L=4096, D=8, N=16)
-    assert scan.ssm_scan_bwd_workspace_bytes(d) == r256(342 * 8 * 16 * 4) + 16 * 8 * 16 * 8
+    assert scan.ssm_scan_bwd_workspace_bytes(d) == r256(512 * 8 * 16 * 4) + 16 * 8 * 16 * 8
 
 
 def call_ssd(desc, u=P, delta=P, A=P, B=P, C=P, D=0, y=P, h=0, ws=P, ws_bytes=1 << 40):

@@ -63,7 +63,7 @@ def _compare(w, inp, dy, dh_last=None, h0=None, label=""):
 
 @pytest.mark.parametrize("mode", list(MODES))
 def test_backward_small_ragged(mode):
-    """B=2, D=37, L=333 (twenty-seven 12-step segments and a ragged one, in two
+    """B=2, D=37, L=333 (forty-one 8-step segments and a ragged one, in two
     time chunks of the reverse sweep, the second ragged), N=16."""
     w = MODES[mode].scaled(batch=2, dim=37, seqlen=333)
     inp = make_inputs(w, seed=21, device="cuda")
@@ -87,7 +87,7 @@ def test_backward_with_state_gradients(mode):
 
 @pytest.mark.parametrize("mode", ["real_zoh_f32", "real_trap_f32", "complex_trap_f32", "complex_trap_bf16"])
 def test_backward_time_chunks(mode):
-    """A narrow, long problem: the reverse sweep runs in four time chunks of 252
+    """A narrow, long problem: the reverse sweep runs in four time chunks of 256
     steps (the last ragged) chained by the adjoint carry, with nonzero h0 and
     dh_last and odd N."""
     w = MODES[mode].scaled(batch=1, dim=5, seqlen=1000, dstate=7)
