@@ -126,6 +126,35 @@ def test_backward_workgroup_sums_time_chunks_odd_n(mode):
     _compare(w, inp, dy, dh_last=dh, h0=h0, label=f"wg sums chunks {mode}")
 
 
+def _degenerate(inp):
+    """A = 0 for some states, delta = 0 at some steps, lambda exactly 0 and 1,
+    theta = 0 for some states, mixed into ordinary inputs."""
+    out = dict(inp)
+    out["A"] = inp["A"].clone()
+    out["A"][::3, 1::4] = 0.0
+    out["delta"] = inp["delta"].clone()
+    out["delta"][:, 5::17] = 0
+    if inp["lam"] is not None:
+        out["lam"] = inp["lam"].clone()
+        out["lam"][:, ::11] = 0
+        out["lam"][:, 3::11] = 1
+    if inp["theta"] is not None:
+        out["theta"] = inp["theta"].clone()
+        out["theta"][..., ::5] = 0
+    return out
+
+
+@pytest.mark.parametrize("mode", ["real_zoh_f32", "real_trap_f32", "complex_trap_f32", "complex_trap_bf16"])
+def test_backward_degenerate_values(mode):
+    """Degenerate values (ZOH's dA at A = 0 comes from its series), D = 32 so
+    the workgroup sums of dB and dC run."""
+    w = MODES[mode].scaled(batch=2, dim=32, seqlen=150)
+    inp = _degenerate(make_inputs(w, seed=28, device="cuda"))
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    dy = torch.randn(inp["u"].shape, generator=gen, device="cuda").to(inp["u"].dtype)
+    _compare(w, inp, dy, label=f"degenerate {mode}")
+
+
 @pytest.mark.parametrize("N", [1, 33, 64])
 def test_backward_state_sizes(N):
     w = MODES["complex_trap_f32"].scaled(batch=2, dim=6, seqlen=45, dstate=N)

@@ -222,3 +222,29 @@ def test_mimo_decode_first_step_without_previous(dtype):
     err_y, err_h = _errs(w, y[:, None], h, ref_y, ref_h)
     print(f"first step {dtype} err_y={err_y:.3e} err_h={err_h:.3e}", flush=True)
     assert err_y <= TOL[dtype] and err_h <= TOL[dtype], (err_y, err_h)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc,cplx", [("zoh", False), ("trap", True)])
+def test_mimo_degenerate_values(disc, cplx, dtype):
+    """A = 0 for some states (ZOH's weight becomes delta), delta = 0 at some
+    steps, lambda exactly 0 and 1, theta = 0 for some states; five chunks."""
+    w = _work(disc, cplx, dtype, batch=2, dim=40, seqlen=150, dstate=16)
+    inp = dict(make_mimo_inputs(w, seed=21, device="cuda"))
+    inp["A"] = inp["A"].clone()
+    inp["A"][::3, 1::4] = 0.0
+    inp["delta"] = inp["delta"].clone()
+    inp["delta"][:, 5::17] = 0
+    if inp["lam"] is not None:
+        inp["lam"] = inp["lam"].clone()
+        inp["lam"][:, ::11] = 0
+        inp["lam"][:, 3::11] = 1
+    if inp["theta"] is not None:
+        inp["theta"] = inp["theta"].clone()
+        inp["theta"][..., ::5] = 0
+    y, h, _ = _run(w, inp, chunk=32)
+    torch.cuda.synchronize()
+    ref_y, ref_h, _ = _oracle(w, channel_sample(inp, range(w.dim)))
+    err_y, err_h = _errs(w, y, h, ref_y, ref_h)
+    print(f"degenerate {disc} cplx={cplx} {dtype} err_y={err_y:.3e} err_h={err_h:.3e}", flush=True)
+    assert err_y <= TOL[dtype] and err_h <= TOL[dtype], (err_y, err_h)

@@ -92,3 +92,22 @@ def test_ssd_full_size_sampled():
     compared on a sample of channels (every batch row and step)."""
     idx = sorted(np.random.default_rng(3).choice(BASE.dim, 12, replace=False).tolist())
     _check(BASE, seed=None, d_index=idx, label="full size")
+
+
+def test_ssd_degenerate_values():
+    """A head with A = 0 (no decay: cum stays 0) and steps with delta = 0 (the
+    state is held, nothing enters), over several chunks with a ragged tail."""
+    w = BASE.scaled(batch=2, dim=192, seqlen=150)
+    inp = dict(make_ssd_inputs(w, seed=46, device="cuda"))
+    inp["A"] = inp["A"].clone()
+    inp["A"][1] = 0.0
+    inp["delta"] = inp["delta"].clone()
+    inp["delta"][:, 7::13] = 0
+    y, h = ssm_ssd_fwd(inp["u"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], inp["Dskip"], headdim=w.headdim)
+    torch.cuda.synchronize()
+    x = ssd_as_scan(inp, w)
+    ref_y, ref_h = oracle.scan(x["u"], x["delta"], x["A"], x["Bm"], x["Cm"], x["Dskip"], disc="euler",
+                               is_complex=False)
+    err_y, err_h = rel_err(_host(y), ref_y), rel_err(_host(h), ref_h)
+    print(f"degenerate err_y={err_y:.3e} err_h={err_h:.3e}", flush=True)
+    assert err_y <= TOL["bf16"] and err_h <= TOL["bf16"], (err_y, err_h)
