@@ -248,3 +248,12 @@ def test_mimo_degenerate_values(disc, cplx, dtype):
     err_y, err_h = _errs(w, y, h, ref_y, ref_h)
     print(f"degenerate {disc} cplx={cplx} {dtype} err_y={err_y:.3e} err_h={err_h:.3e}", flush=True)
     assert err_y <= TOL[dtype] and err_h <= TOL[dtype], (err_y, err_h)
+
+
+def test_mimo_largest_staging():
+    """R = 8 and N = 64, complex trapezoidal: the largest B and C rows (1024
+    fp32 values per step and array, 64 KB of double-buffered LDS in the scan),
+    over several chunks, and the decode step on the same sizes."""
+    w = _work("trap", True, "f32", batch=1, dim=3, seqlen=70, dstate=64, rank=8)
+    _check(w, seed=22, chunk=32, label="R=8 N=64")
+    _decode_check(w, seed=23, steps=2, label="decode R=8 N=64")
