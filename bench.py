@@ -231,6 +231,53 @@ def cpu_baseline_decode(inputs, w, h_start, target_s: float):
     }
 
 
+EVICT_BYTES = 1 << 30  # scratch written before every timed rep: evicts the L2s and the 256 MB MALL
+
+
+class Timing:
+    """Per-rep times (ms) of a timed loop; `ms` (the median) is what a step costs."""
+
+    def __init__(self, reps):
+        self.reps = sorted(reps)
+        n = len(self.reps)
+        self.median = self.reps[n // 2] if n % 2 else 0.5 * (self.reps[n // 2 - 1] + self.reps[n // 2])
+        self.min = self.reps[0]
+        self.mean = sum(self.reps) / n
+
+    @property
+    def ms(self):
+        return self.median
+
+    def record(self):
+        return {"median_ms": self.median, "min_ms": self.min, "mean_ms": self.mean, "reps": len(self.reps),
+                "method": "HIP events around each step on the launch stream; before every step a "
+                          f"{EVICT_BYTES >> 20} MiB scratch buffer is written outside the events (L2/MALL eviction)"}
+
+
+def _timed(torch, stream, step, steps: int, warmup: int, label: str = "steps") -> Timing:
+    """Warm up, then time each of `steps` calls of step() with its own event
+    pair on `stream`, writing a 1 GiB scratch buffer before each call (outside
+    the events) so that no input is served from the L2s or the MALL."""
+    for i in range(warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{warmup} done")
+    scratch = torch.empty(EVICT_BYTES // 4, dtype=torch.float32, device=torch.cuda.current_device())
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i, (a, b) in enumerate(events):
+            scratch.fill_(float(i))
+            a.record(stream)
+            step()
+            b.record(stream)
+    torch.cuda.synchronize()
+    t = Timing([a.elapsed_time(b) for a, b in events])
+    del scratch
+    log(f"timed {steps} {label}: median {t.median:.4f} ms, min {t.min:.4f} ms, mean {t.mean:.4f} ms")
+    return t
+
+
 def bench_decode(args, w, torch, dev):
     from selective_state_space_42_amd.inputs import make_inputs
     from selective_state_space_42_amd.scan import ssm_scan_step
@@ -254,22 +301,13 @@ def bench_decode(args, w, torch, dev):
                       cur["lam"], h=h, u_prev=prev["u"] if trap else None, B_prev=prev["Bm"] if trap else None,
                       disc=w.disc, y=y, stream=stream.cuda_stream)
 
-    for i in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    log(f"timed {args.steps} decode steps: {ms * 1e3:.2f} us/step")
+    timing = _timed(torch, stream, step, args.steps, args.warmup, "decode steps")
+    ms = timing.ms
     alg_bytes = decode_algorithmic_bytes(w)
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": w.batch * w.dim / (ms * 1e-3), "unit": UNIT, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": ms, "timing": timing.record(), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": 1, "dstate": w.dstate,
                    "disc": w.disc, "complex": w.is_complex, "io_dtype": w.io_dtype, "algo": "step"},
@@ -325,19 +363,13 @@ def bench_backward(args, w, torch, dev):
         if st != 0:
             raise RuntimeError(f"ssm_scan_bwd status {st}")
 
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        call()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    log(f"timed {args.steps} backward passes: {ms:.3f} ms each")
+    timing = _timed(torch, stream, call, args.steps, 0, "backward passes")
+    ms = timing.ms
     alg = backward_algorithmic_bytes(w)
     achieved = alg / (ms * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": w.batch * w.seqlen * w.dim / (ms * 1e-3), "unit": UNIT, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "timing": timing.record(), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen, "dstate": w.dstate,
                    "disc": w.disc, "complex": w.is_complex, "io_dtype": w.io_dtype, "algo": "backward"},
@@ -390,22 +422,13 @@ def bench_ssd(args, w, torch, dev):
         ssm_ssd_fwd(inputs["u"], inputs["delta"], inputs["A"], inputs["Bm"], inputs["Cm"], inputs["Dskip"],
                     headdim=w.headdim, y=y, h_last=h_last, workspace=ws, stream=stream.cuda_stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    log(f"timed {args.steps} SSD passes: {ms:.3f} ms each")
+    timing = _timed(torch, stream, step, args.steps, args.warmup, "SSD passes")
+    ms = timing.ms
     alg = ssd_algorithmic_bytes(w)
     achieved = alg / (ms * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": w.batch * w.seqlen * w.dim / (ms * 1e-3), "unit": UNIT, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "timing": timing.record(), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen, "dstate": w.dstate,
                    "headdim": w.headdim, "disc": "euler", "complex": False, "io_dtype": w.io_dtype, "algo": "ssd"},
@@ -444,18 +467,7 @@ def bench_ssd(args, w, torch, dev):
     print(json.dumps(out), flush=True)
 
 
-def _timed(torch, stream, step, steps: int, warmup: int) -> float:
-    """ms per call of step() over `steps` calls after `warmup`, by events on `stream`."""
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+
 
 
 def bench_mimo(args, w, torch, dev):
@@ -479,13 +491,14 @@ def bench_mimo(args, w, torch, dev):
                      inputs["theta"], inputs["lam"], disc=w.disc, y=y, h_last=h_last, workspace=ws,
                      stream=stream.cuda_stream)
 
-    ms = _timed(torch, stream, step, args.steps, args.warmup)
+    timing = _timed(torch, stream, step, args.steps, args.warmup)
+    ms = timing.ms
     log(f"timed {args.steps} MIMO scans: {ms:.3f} ms each")
     alg = mimo_algorithmic_bytes(w)
     achieved = alg / (ms * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": w.batch * w.seqlen * w.dim / (ms * 1e-3), "unit": UNIT, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "timing": timing.record(), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen, "dstate": w.dstate,
                    "rank": w.rank, "disc": w.disc, "complex": w.is_complex, "io_dtype": w.io_dtype,
@@ -548,13 +561,14 @@ def bench_mimo_decode(args, w, torch, dev):
                       cur["lam"], h=h, u_prev=prev["u"] if trap else None, B_prev=prev["Bm"] if trap else None,
                       disc=w.disc, y=y, stream=stream.cuda_stream)
 
-    ms = _timed(torch, stream, step, args.steps, args.warmup)
+    timing = _timed(torch, stream, step, args.steps, args.warmup)
+    ms = timing.ms
     log(f"timed {args.steps} MIMO decode steps: {ms * 1e3:.2f} us/step")
     alg = mimo_decode_algorithmic_bytes(w)
     achieved = alg / (ms * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": w.batch * w.dim / (ms * 1e-3), "unit": UNIT, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": ms, "timing": timing.record(), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": 1, "dstate": w.dstate,
                    "rank": w.rank, "disc": w.disc, "complex": w.is_complex, "io_dtype": w.io_dtype,
@@ -614,6 +628,36 @@ def copy_calibration(torch, dev, nbytes: int, steps: int, warmup: int):
                       "ms_per_copy": ms, "GBps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def stream_calibration(torch, dev, steps: int, warmup: int):
+    """The practical HBM ceiling for the scan's traffic shape, measured by the
+    library's own read-dominant stream kernel (ssm_calibrate_stream): 19 bytes
+    read per byte written (95 % reads, like the scan), 45.9 GB read and
+    2.4 GB written per launch, far beyond the L2s and the 256 MB MALL.  Both
+    the default and the non-temporal cache policy are timed; the kernel also
+    reports the sustained shader clock (s_memtime against the 100 MHz
+    s_memrealtime counter)."""
+    from selective_state_space_42_amd.scan import ssm_calibrate_stream
+
+    ratio, dst_bytes = 19, 9 << 28
+    src = torch.empty(ratio * dst_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty(dst_bytes // 4, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    moved = (ratio + 1) * dst_bytes
+    out = {"calibration": "hbm_read_stream", "read_bytes": ratio * dst_bytes, "write_bytes": dst_bytes,
+           "reads_per_write": ratio, "peak_GBps": PEAK_HBM_GBS}
+    for name, nt in (("default", False), ("nontemporal", True)):
+        t = _timed(torch, stream, lambda: ssm_calibrate_stream(src, dst, nontemporal=nt, clocks=clocks,
+                                                               stream=stream.cuda_stream),
+                   steps, warmup, f"{name} stream launches")
+        ticks = clocks.cpu().tolist()
+        out[name] = {"GBps_median": moved / (t.median * 1e-3) / 1e9, "GBps_best": moved / (t.min * 1e-3) / 1e9,
+                     "frac_of_peak_median": moved / (t.median * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "timing": t.record(),
+                     "sustained_clock_MHz": ticks[0] / ticks[1] * 100.0 if ticks[1] > 0 else None}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -624,6 +668,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (ssm_scan_bwd) instead")
+    ap.add_argument("--stream-calibration", action="store_true",
+                    help="instead of the scan, time the library's read-dominant HBM stream kernel (95 %% reads, "
+                         "48 GB per launch): the practical bandwidth ceiling the scan is compared with")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the scan, time a plain device-to-device copy of BYTES bytes "
                          "(the known-size kernel that HBM byte counters are scaled against)")
@@ -645,6 +692,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_calibration:
         copy_calibration(torch, dev, args.copy_calibration, args.steps, args.warmup)
+        return
+    if args.stream_calibration:
+        stream_calibration(torch, dev, args.steps, args.warmup)
         return
     if args.workload in DECODE_WORKLOADS:
         bench_decode(args, DECODE_WORKLOADS[args.workload], torch, dev)
@@ -678,19 +728,8 @@ def main():
                      inputs["theta"], inputs["lam"], disc=w.disc, y=y, h_last=h_last,
                      workspace=ws if ws_bytes else None, algo=args.algo, stream=stream.cuda_stream)
 
-    for i in range(args.warmup):
-        step()
-        torch.cuda.synchronize()
-        log(f"warmup {i + 1}/{args.warmup} done")
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+    timing = _timed(torch, stream, step, args.steps, args.warmup)
+    ms = timing.ms
 
     tc = w.batch * w.seqlen * w.dim
     alg_bytes = algorithmic_bytes(w)
@@ -702,7 +741,7 @@ def main():
 
     out = {
         "metric": METRIC, "value": tc / (ms * 1e-3), "unit": UNIT, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": ms, "timing": timing.record(), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen, "dstate": w.dstate,
                    "disc": w.disc, "complex": w.is_complex, "io_dtype": w.io_dtype, "algo": algo_used},

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 3
+#define SSM_SCAN_ABI_VERSION 4
 
 /* Element type of u, delta, B, C, theta, lambda and y.  A, D and h_last are
  * always fp32; all arithmetic is fp32 (bf16 inputs are widened exactly, y is

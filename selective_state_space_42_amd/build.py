@@ -18,8 +18,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libssmscan.so")
-SOURCES = [os.path.join(CSRC, "ssm_scan.hip"), os.path.join(CSRC, "mimo.hip")]
-HEADERS = [os.path.join(ROOT, "include", "ssm_scan.h")] + [
+SOURCES = [os.path.join(CSRC, "ssm_scan.hip"), os.path.join(CSRC, "mimo.hip"), os.path.join(CSRC, "calibrate.hip")]
+HEADERS = [os.path.join(ROOT, "include", "ssm_scan.h"), os.path.join(ROOT, "include", "ssm_calibrate.h")] + [
     os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".h")]
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 

@@ -14,14 +14,17 @@ from selective_state_space_42_amd import scan
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "ssm_calibrate.h")]
 
 OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
 P = 0x10000  # an aligned fake device address (never dereferenced)
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(ssm_(?:scan|ssd|mimo)_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        names |= set(re.findall(r"\b(ssm_(?:scan|ssd|mimo|calibrate)_\w+)\s*\(", open(h).read()))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -30,14 +33,14 @@ def test_library_exports_every_declared_symbol():
     assert {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_step", "ssm_scan_bwd", "ssm_scan_workspace_bytes",
             "ssm_scan_bwd_workspace_bytes", "ssm_ssd_fwd", "ssm_ssd_workspace_bytes", "ssm_mimo_fwd",
             "ssm_mimo_step", "ssm_mimo_workspace_bytes", "ssm_scan_status_string", "ssm_scan_abi_version",
-            "ssm_scan_last_hip_error"} <= set(names)
+            "ssm_scan_last_hip_error", "ssm_calibrate_stream"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_version_and_status_strings():
     header_version = int(re.search(r"#define SSM_SCAN_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert scan.ssm_scan_abi_version() == header_version == scan.ABI_VERSION == 3
+    assert scan.ssm_scan_abi_version() == header_version == scan.ABI_VERSION == 4
     for code, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported configuration"),
                        (3, "workspace too small"), (4, "HIP runtime error"), (99, "unknown status")]:
         assert scan.ssm_scan_status_string(code) == text
@@ -295,3 +298,16 @@ def test_mimo_step_rules():
     assert call_mimo_step(mimo_desc(L=1, disc="euler"), lam=0, u_prev=P, B_prev=P) == INVALID
     assert call_mimo_step(mimo_desc(L=1), u_prev=P + 4, B_prev=P) == INVALID
     assert call_mimo_step(mimo_desc(L=1, R=3)) == UNSUPPORTED
+
+
+def test_calibrate_stream_argument_checks():
+    lib = scan._lib()
+    v = ctypes.c_void_p
+    assert lib.ssm_calibrate_stream(None, 1 << 20, v(P), 1 << 16, 0, None, None) == INVALID
+    assert lib.ssm_calibrate_stream(v(P), 1 << 20, None, 1 << 16, 0, None, None) == INVALID
+    assert lib.ssm_calibrate_stream(v(P), 1000, v(P + (1 << 24)), 16, 0, None, None) == INVALID      # not a multiple
+    assert lib.ssm_calibrate_stream(v(P), 65 * 16, v(P + (1 << 24)), 16, 0, None, None) == INVALID   # ratio above 64
+    assert lib.ssm_calibrate_stream(v(P + 8), 320, v(P + (1 << 24)), 16, 0, None, None) == INVALID   # misaligned
+    assert lib.ssm_calibrate_stream(v(P), 320, v(P + 16), 16, 0, None, None) == INVALID              # overlapping
+    assert lib.ssm_calibrate_stream(v(P), 320, v(P + (1 << 24)), 16, 2, None, None) == INVALID       # bad flag
+    assert lib.ssm_calibrate_stream(v(P), 320, v(P + (1 << 24)), 16, 0, v(P + 4), None) == INVALID   # clocks
