@@ -81,7 +81,9 @@ typedef enum {
                                        per-tile windows exceed 32-bit offsets:
                                        24*D*N*esize, 98*D*esize or 4*D*N above 2^30 */
     SSM_ERR_WORKSPACE_TOO_SMALL = 3,
-    SSM_ERR_HIP = 4                 /* a HIP call failed; see ssm_scan_last_hip_error() */
+    SSM_ERR_HIP = 4,                /* a HIP call failed; see ssm_scan_last_hip_error() */
+    SSM_ERR_SCRATCH_LIMIT = 5       /* ssm_scan_fwd_noalloc: the problem needs more scratch
+                                       than SSM_SCAN_NOALLOC_SCRATCH_BYTES */
 } ssm_status_t;
 
 typedef struct {
@@ -169,6 +171,34 @@ int ssm_scan_fwd_ex(const ssm_scan_desc_t *desc, const void *u, const void *delt
                     const void *B, const void *C, const float *D, const void *theta,
                     const void *lambda, const float *h0, const float *q0, void *y, float *h_last,
                     float *q_last, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Size of the fixed per-GPU scratch buffer of ssm_scan_fwd_noalloc. */
+#define SSM_SCAN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * ssm_scan_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Arguments, results and errors are those of ssm_scan_fwd, except that there
+ * is no workspace argument: the kernels use a fixed scratch buffer of
+ * SSM_SCAN_NOALLOC_SCRATCH_BYTES inside the library instead, one per GPU,
+ * which exists from the loading of the library's code on that GPU until the
+ * process ends.  The call allocates nothing (no hipMalloc, hipFree or other
+ * allocating routine).
+ *
+ *  - Limit: when ssm_scan_workspace_bytes(desc) exceeds
+ *    SSM_SCAN_NOALLOC_SCRATCH_BYTES the call returns SSM_ERR_SCRATCH_LIMIT
+ *    before any HIP call; such problems need ssm_scan_fwd with a workspace.
+ *  - Device: the buffer of the current HIP device is used, so `stream` must
+ *    belong to it.  The first call on a device looks up that device's buffer
+ *    address; if that lookup fails the call returns SSM_ERR_HIP.
+ *  - Sharing: every call on one GPU uses that GPU's buffer, and the buffer
+ *    keeps the last call's contents.  Each call re-initialises on its stream,
+ *    with a kernel (no memset), everything the kernels need to start at zero.
+ *    Calls on one GPU must not overlap in time: they would race on the buffer.
+ */
+int ssm_scan_fwd_noalloc(const ssm_scan_desc_t *desc, const void *u, const void *delta, const float *A,
+                         const void *B, const void *C, const float *D, const void *theta,
+                         const void *lambda, void *y, float *h_last, void *stream);
 
 /*
  * One step of the recurrence with the state kept in device memory and

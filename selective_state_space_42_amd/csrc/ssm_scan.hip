@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "ssm_scan.h"
 #include "device_common.h"
 #include "kernel_sequential.h"
@@ -18,9 +20,47 @@
 #include "kernel_ssd.h"
 #include "mimo_launch.h"
 
+// The fixed scratch buffer of ssm_scan_fwd_noalloc: one copy per GPU, held
+// from the loading of this code object on that GPU until the process ends.
+// In host code `scratch` only names the symbol; its device address (a
+// different one on each GPU) comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[SSM_SCAN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// Device address of `scratch` on each GPU, looked up once per device with
+// that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, or nullptr after storing the
+// failing HIP error (or when the device index is out of range).
+void* scratch_for_current_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = static_cast<int>(e);
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        g_last_hip_error = static_cast<int>(hipErrorInvalidDevice);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            g_last_hip_error = static_cast<int>(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
 
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return SSM_OK;
@@ -347,6 +387,7 @@ const char* ssm_scan_status_string(int status) {
         case SSM_ERR_UNSUPPORTED: return "unsupported configuration";
         case SSM_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case SSM_ERR_HIP: return "HIP runtime error";
+        case SSM_ERR_SCRATCH_LIMIT: return "problem needs more scratch than the allocation-free entry point holds";
         default: return "unknown status";
     }
 }
@@ -416,6 +457,30 @@ int ssm_scan_fwd_ex(const ssm_scan_desc_t* desc, const void* u, const void* delt
     p.lpc = next_pow2(desc->dstate);
     return desc->io_dtype == SSM_DTYPE_F32 ? launch_sequential<float>(desc, p, s)
                                            : launch_sequential<uint16_t>(desc, p, s);
+}
+
+int ssm_scan_fwd_noalloc(const ssm_scan_desc_t* desc, const void* u, const void* delta, const float* A,
+                         const void* B, const void* C, const float* D, const void* theta, const void* lambda,
+                         void* y, float* h_last, void* stream) {
+    // every check that needs no device first, so that invalid calls and
+    // over-limit problems return before any HIP call
+    int st = check_desc(desc);
+    if (st != SSM_OK) return st;
+    st = check_inputs(desc, u, delta, A, B, C, D, theta, lambda, y);
+    if (st != SSM_OK) return st;
+    if (h_last && !aligned(h_last, desc->is_complex ? 8 : 4)) return SSM_ERR_INVALID_ARGUMENT;
+    const int algo = choose_algo(desc);
+    if (algo == SSM_ALGO_CHUNKED && desc->dstate > ssm::kChunkLanes) return SSM_ERR_UNSUPPORTED;
+    const size_t need =
+        algo == SSM_ALGO_CHUNKED ? ssm::chunked_workspace_bytes(desc->batch, desc->seqlen, desc->dim) : 0;
+    if (need > SSM_SCAN_NOALLOC_SCRATCH_BYTES) return SSM_ERR_SCRATCH_LIMIT;
+    void* ws = nullptr;
+    if (need > 0) {
+        ws = scratch_for_current_device();
+        if (!ws) return SSM_ERR_HIP;
+    }
+    return ssm_scan_fwd_ex(desc, u, delta, A, B, C, D, theta, lambda, nullptr, nullptr, y, h_last, nullptr, ws,
+                           need > 0 ? SSM_SCAN_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int ssm_scan_step(const ssm_scan_desc_t* desc, const void* u, const void* delta, const float* A, const void* B,

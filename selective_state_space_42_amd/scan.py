@@ -70,6 +70,8 @@ def _lib():
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_scan_fwd_ex.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 14 + [ctypes.c_size_t, vp]
     lib.ssm_scan_fwd_ex.restype = ctypes.c_int
+    lib.ssm_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 11
+    lib.ssm_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ssm_calibrate_stream.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, ctypes.c_int32, vp, vp]
     lib.ssm_calibrate_stream.restype = ctypes.c_int
     lib.ssm_scan_step.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 13
@@ -260,6 +262,31 @@ def ssm_scan_fwd_ex(u, delta, A, B, C, D=None, theta=None, lam=None, h0=None, q0
     if st != 0:
         raise ScanError(st, "ssm_scan_fwd_ex")
     return y, h_last, q_last
+
+
+def ssm_scan_fwd_noalloc(u, delta, A, B, C, D=None, theta=None, lam=None, *, disc: str, y=None, h_last=None,
+                         want_h_last: bool = True, algo: str = "auto", stream=None):
+    """ssm_scan_fwd with the library's fixed per-GPU scratch instead of a
+    workspace (the call allocates nothing; y and h_last are allocated here
+    only when not given).  Returns (y, h_last)."""
+    Bsz, L, Dm = _dims("ssm_scan_fwd_noalloc", u, 3, "u")
+    N = _dims("ssm_scan_fwd_noalloc", A, 2, "A")[1]
+    is_complex = B.dim() == 4
+    specs = _scan_specs("ssm_scan_fwd_noalloc", u, delta, A, B, C, D, theta, lam, y, disc, is_complex)
+    shape = (Bsz, Dm, N, 2) if is_complex else (Bsz, Dm, N)
+    _check("ssm_scan_fwd_noalloc", u.dtype, specs + [("h_last", h_last, shape, torch.float32)])
+    desc = make_desc(Bsz, L, Dm, N, u.dtype, disc, is_complex, algo)
+    if y is None:
+        y = torch.empty_like(u)
+    if h_last is None and want_h_last:
+        h_last = torch.empty(shape, dtype=torch.float32, device=u.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+    st = _lib().ssm_scan_fwd_noalloc(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                     _ptr(theta), _ptr(lam), _ptr(y), _ptr(h_last), ctypes.c_void_p(stream))
+    if st != 0:
+        raise ScanError(st, "ssm_scan_fwd_noalloc")
+    return y, h_last
 
 
 def ssm_calibrate_stream(src, dst, nontemporal: bool = False, clocks=None, stream=None) -> None:

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_step", "ssm_scan_bwd", "ssm_scan_workspace_bytes",
             "ssm_scan_bwd_workspace_bytes", "ssm_ssd_fwd", "ssm_ssd_workspace_bytes", "ssm_mimo_fwd",
             "ssm_mimo_step", "ssm_mimo_workspace_bytes", "ssm_scan_status_string", "ssm_scan_abi_version",
-            "ssm_scan_last_hip_error", "ssm_calibrate_stream"} <= set(names)
+            "ssm_scan_last_hip_error", "ssm_scan_fwd_noalloc", "ssm_calibrate_stream"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -298,6 +298,44 @@ def test_mimo_step_rules():
     assert call_mimo_step(mimo_desc(L=1, disc="euler"), lam=0, u_prev=P, B_prev=P) == INVALID
     assert call_mimo_step(mimo_desc(L=1), u_prev=P + 4, B_prev=P) == INVALID
     assert call_mimo_step(mimo_desc(L=1, R=3)) == UNSUPPORTED
+
+
+SCRATCH_LIMIT = 5
+NOALLOC_BYTES = 64 << 20
+
+
+def call_noalloc(desc, u=P, delta=P, A=P, B=P, C=P, D=0, theta=0, lam=0, y=P, h=0):
+    lib = scan._lib()
+    dp = None if desc is None else ctypes.byref(desc)
+    args = [u, delta, A, B, C, D, theta, lam, y, h]
+    return lib.ssm_scan_fwd_noalloc(dp, *[ctypes.c_void_p(a) if a else None for a in args], None)
+
+
+def test_noalloc_limit_in_header():
+    text = open(HEADER).read()
+    assert "#define SSM_SCAN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert "SSM_ERR_SCRATCH_LIMIT = 5" in text
+    assert "scratch" in scan.ssm_scan_status_string(SCRATCH_LIMIT)
+
+
+def test_noalloc_validates_before_any_hip_call():
+    assert call_noalloc(None) == INVALID
+    assert call_noalloc(desc(L=0)) == INVALID
+    for k in ["u", "delta", "A", "B", "C", "y"]:
+        assert call_noalloc(desc(), **{k: 0}) == INVALID, k
+    assert call_noalloc(desc(disc="trap")) == INVALID             # no lambda
+    assert call_noalloc(desc(N=65)) == UNSUPPORTED
+    assert call_noalloc(desc(cplx=True), h=P + 4) == INVALID      # misaligned complex h_last
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    big = desc(B=1, L=1 << 20, D=1024, N=16, dtype="bf16", disc="trap", cplx=True, algo="chunked")
+    assert scan.ssm_scan_workspace_bytes(big) > NOALLOC_BYTES
+    assert call_noalloc(big, lam=P, theta=P) == SCRATCH_LIMIT
+    # the largest chunked problem that fits is accepted by the size check
+    # (it would go on to look up the GPU's scratch, so it is not called here)
+    small = desc(B=1, L=4096, D=64, N=16, dtype="bf16", disc="trap", cplx=True, algo="chunked")
+    assert 0 < scan.ssm_scan_workspace_bytes(small) <= NOALLOC_BYTES
 
 
 def test_calibrate_stream_argument_checks():
