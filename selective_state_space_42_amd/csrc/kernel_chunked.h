@@ -64,6 +64,7 @@ constexpr int kWaves = 4;          // waves per workgroup, consecutive in time
 constexpr int kTW = 24;            // steps per wave (a multiple of 8)
 constexpr int kTT = kWaves * kTW;  // steps per tile
 constexpr int kThreads = kWaves * 64;
+constexpr int kCpolSc1 = 16;       // buffer-access cache policy: coherent across the device (as agent-scope atomics)
 constexpr int kSlots = 8;          // ticket counters (one per XCD)
 constexpr int kDmaWaves = kWaves - 1;  // waves 1.. issue the tile's LDS copies; wave 0 looks back
 constexpr int kPayloadF2 = 3 * 64 * kNPL;  // float2 per tile: aggregate P, aggregate h, inclusive h
@@ -149,6 +150,18 @@ inline bool chunked_preferred(int64_t, int64_t, int64_t) { return true; }
 __device__ __forceinline__ void wait_stores() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
+// (lgkmcnt(0)) but not for its global loads, stores or copies into LDS, which
+// a __syncthreads() may wait for whenever any are in flight.  Used where
+// those are deliberately left outstanding across the barrier; every reader of
+// their results waits for them itself.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+    __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
 
@@ -326,7 +339,6 @@ struct RawRows {
 // D of its staging channel and theta of its states over its steps (theta as
 // stored, decoded in pass 1).  Buffer resources cover exactly the valid data,
 // so lanes and steps outside read 0 and no load needs a branch or a mask.
-// At least kOwnLoadsMin vector-memory instructions are issued.
 template <typename T, bool CPLX>
 __device__ __forceinline__ void issue_own(TileRegs<T>& r, const ChunkParams& p, const Tile& t, int tid, int c,
                                           int pr, int s0) {
@@ -381,10 +393,10 @@ __device__ __forceinline__ void issue_own(TileRegs<T>& r, const ChunkParams& p, 
     }
 }
 
-// Lower bound on the vector-memory instructions issue_own() issues (theta
-// rows for a complex state, else the D load).
-template <bool CPLX>
-constexpr int kOwnLoadsMin = CPLX ? chunk::kTW : 1;
+// Pass-2 step after whose outputs a wave issues the next tile's register
+// loads (after an output block: one per 8 steps).
+constexpr int kOwnIssueStep = 7;
+static_assert(kOwnIssueStep % 8 == 7 && kOwnIssueStep < chunk::kTW, "issue after an output block");
 
 // Issue one DMA wave's share (dw in [0, kDmaWaves)) of tile `t`'s
 // buffer-to-LDS copies: the B/C rows and, with p.rows_dma, the raw per-step
@@ -695,8 +707,8 @@ __device__ __forceinline__ void pass1(const TileRegs<T>& r, const float2 (*s_dw)
 // Persistent workgroups: each takes tickets from its slot's counter until the
 // slot's tiles are exhausted.  The pipeline per workgroup is
 //   [tile k: commit staged values to LDS | pass 1]
-//   [issue the global loads of tile k+1 into registers | look-back of k |
-//    pass 2 of k]
+//   [look-back of k | copies of tile k+1's rows into LDS]
+//   [pass 2 of k, with tile k+1's register loads issued after its first outputs]
 // so tile k+1's memory latency overlaps tile k's look-back and pass 2.  A
 // tile only waits on tiles with smaller tickets of the same slot; each such
 // tile is held by a running workgroup that is processing it or will process it
@@ -730,7 +742,8 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
     float2* s_aggH = reinterpret_cast<float2*>(s_x) + kAggF2;  // [wave][lane][j]
     float* s_red = s_x;                                         // [wave][step % 8][lane (padded)]
     __shared__ float2 s_carry[kWaves][64][kNPL];  // incoming state of each wave's steps
-    __shared__ uint32_t s_ticket;
+    __shared__ uint32_t s_ticket[2];  // the ticket after the current tile, by tile parity (buf)
+    __shared__ uint32_t s_pred_inc;  // wave 0 holds the predecessor's inclusive state (see pred_flag)
 
     const T* u = static_cast<const T*>(p.u);
     const T* delta = static_cast<const T*>(p.delta);
@@ -757,26 +770,42 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
 
     TileRegs<T> r;  // one tile's register-carried loads
 
-    // ---- prologue: first ticket, its loads, the ticket after it
-    if (tid == 0) s_ticket = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // ---- prologue: first ticket, its loads, the ticket after it.  Later
+    // tickets are requested in the carry step of the tile before the one that
+    // reads them.
+    uint32_t ticket = 0;  // thread 0: the ticket after the current tile (see the loop)
+    if (tid == 0) {
+        s_ticket[1] = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ticket = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
-    uint32_t cur = __builtin_amdgcn_readfirstlane(s_ticket);
+    uint32_t cur = __builtin_amdgcn_readfirstlane(s_ticket[1]);
     if (cur >= slot_tiles) return;
-    // The ticket after the current one is requested by lane 0 of wave 1 (wave 0
-    // is busy with the look-back then) and published through LDS a tile later.
-    uint32_t next_ticket = 0;  // thread kTicketThread only
-    constexpr int kTicketThread = 64;
-    if (tid == kTicketThread)
-        next_ticket = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     Tile tc = decode_tile(cur, per_tt, slot, lay, D);
     int buf = 0;
     issue_own<T, CPLX>(r, p, tc, tid, c, pr, s0);
     if (wave != 0) issue_dma<T, DISC>(p, lay, tc, lane, wave - 1, &s_bcb[0][0][0], s_raw, s_k);
+    // Wave 0: the flag of the current tile's predecessor as read in the carry
+    // step of the previous tile (empty before the first tile).  A flag only rises, so
+    // when it already showed the inclusive state the payload is loaded at the
+    // start of the tile and has arrived by the time the look-back needs it.
+    uint32_t pred_flag = kFlagEmpty;
 
     for (;;) {
         // ---- 1. stage the current tile
         wait_stores();  // this wave's loads and DMA (B/C rows, raw rows) have landed (vmcnt(0))
         __syncthreads();
+        const bool pred_inc = tc.tt > 0 && __builtin_amdgcn_readfirstlane(pred_flag) == kFlagInclusive;  // wave 0 only
+        float2 pred_state[kNPL];
+        if (wave == 0 && pred_inc) {
+            const float2* pk = payload + (tc.g * lay.n_tt + tc.tt - 1) * kPayloadF2;
+#pragma unroll
+            for (int j = 0; j < kNPL; ++j) pred_state[j] = ld_agent(pk, pay_off(2, lane, j));
+        }
+        if (tid == 0) {
+            s_pred_inc = pred_inc ? 1u : 0u;
+            s_ticket[buf] = ticket;  // read in this tile's carry step
+        }
         commit_tile<T, DISC>(r, p, lay, tc, tid, s_raw, s_k, s_dw, s_e);
         __syncthreads();
         float4 (*s_bc)[kChunkLanes] = s_bcb[buf];
@@ -840,15 +869,13 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
             s_aggP[(wave * 64 + lane) * kNPL + j] = to_f2(P);
             s_aggH[(wave * 64 + lane) * kNPL + j] = to_f2(gl[j]);
         }
-        if (tid == kTicketThread) s_ticket = next_ticket;
         __syncthreads();
 
-        // ---- 3. cross-tile carry.  Wave 0: look back, form the inclusive state
-        // and every wave's incoming state.  Wave 1: publish the tile aggregate.
-        // Waves 1..: the ticket after next and the next tile's LDS copies.
-        // (vmcnt retires in order, so wave 0 issues no loads before its
-        // look-back traffic has returned.)
-        const uint32_t nx = __builtin_amdgcn_readfirstlane(s_ticket);
+        // ---- 3. cross-tile carry.  Wave 0: look back, form the inclusive
+        // state and every wave's incoming state.  Wave 1: publish the tile
+        // aggregate.  Waves 1..: the next tile's LDS copies.  Then the ticket
+        // after next and the next tile's predecessor flag.
+        const uint32_t nx = __builtin_amdgcn_readfirstlane(s_ticket[buf]);
         const bool has_next = nx < slot_tiles;
         const Tile tn = has_next ? decode_tile(nx, per_tt, slot, lay, D) : tc;
         float2* pay_base = payload + (tc.g * lay.n_tt) * kPayloadF2;
@@ -856,7 +883,12 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
         const int64_t tt = tc.tt;
         float2* mine = pay_base + tt * kPayloadF2;
         if (wave != 0) {
-            if (wave == 1 && tt > 0) {
+            // The aggregate lets a successor that finds this tile before its
+            // inclusive state fold past it.  When wave 0 already holds the
+            // predecessor's inclusive state, that state follows within the
+            // carry step, so the aggregate is skipped (a successor that finds
+            // the flag empty waits for the inclusive state).
+            if (wave == 1 && tt > 0 && s_pred_inc == 0u) {
                 Cx Pt[kNPL], Ht[kNPL];
                 tile_aggregate(s_aggP, s_aggH, lane, Pt, Ht);
 #pragma unroll
@@ -867,18 +899,22 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
                 wait_stores();
                 if (lane == 0) __hip_atomic_store(&flag[tt], kFlagAggregate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            if (tid == kTicketThread)
-                next_ticket = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (has_next) issue_dma<T, DISC>(p, lay, tn, lane, wave - 1, &s_bcb[buf ^ 1][0][0], s_raw, s_k);
         } else {
             Cx Pt[kNPL], Ht[kNPL], carry[kNPL];
+#pragma unroll
+            for (int j = 0; j < kNPL; ++j) carry[j] = {0.f, 0.f};
+            if (pred_inc) {  // the predecessor's state, loaded at the start of the tile
+#pragma unroll
+                for (int j = 0; j < kNPL; ++j) carry[j] = to_cx(pred_state[j]);
+            }
             tile_aggregate(s_aggP, s_aggH, lane, Pt, Ht);
             // re-read the wave aggregates from LDS after the look-back rather
             // than holding them in registers across it
             asm volatile("" ::: "memory");
-#pragma unroll
-            for (int j = 0; j < kNPL; ++j) carry[j] = {0.f, 0.f};
-            if (tt > 0) {
+            if (pred_inc) {
+                // carry already formed
+            } else if (tt > 0) {
                 look_back(flag, pay_base, tt, lane, carry);
             } else if (p.h0 || (kTR && p.q0)) {
                 // the state before step 0; the trapezoid carries the shifted
@@ -904,10 +940,9 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
                     carry[j] = g0;
                 }
             }
+            // every wave's incoming state first (LDS only), then the stores
 #pragma unroll
             for (int j = 0; j < kNPL; ++j) {
-                const Cx inc = cfma(Pt[j], carry[j], Ht[j]);
-                st_agent(mine, pay_off(2, lane, j), to_f2(inc));
                 Cx hin = carry[j];  // incoming state of each wave's steps
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w) {
@@ -915,6 +950,11 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
                     hin = cfma(to_cx(s_aggP[(w * 64 + lane) * kNPL + j]), hin,
                                to_cx(s_aggH[(w * 64 + lane) * kNPL + j]));
                 }
+            }
+#pragma unroll
+            for (int j = 0; j < kNPL; ++j) {
+                const Cx inc = cfma(Pt[j], carry[j], Ht[j]);
+                st_agent(mine, pay_off(2, lane, j), to_f2(inc));
                 if (tt == lay.n_tt - 1 && p.h_last && nok[j]) {
                     const int64_t hs = (tc.b * D + d) * N + pr * kNPL + j;
                     if constexpr (CPLX) {
@@ -926,20 +966,26 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
                 }
             }
         }
-        __syncthreads();
-        // Every wave's register loads of the next tile come from this one site
-        // (one set of destination registers, so pass 2 never waits on them).
-        // On wave 0 they go out behind the inclusive stores; once at most that
-        // many instructions are outstanding the stores are complete and the
-        // flag may be raised.
-        if (has_next) issue_own<T, CPLX>(r, p, tn, tid, c, pr, s0);
-        if (wave == 0) {
-            if (has_next)
-                wait_vm_below<kOwnLoadsMin<CPLX>>();
-            else
-                wait_stores();
-            if (lane == 0) __hip_atomic_store(&flag[tt], kFlagInclusive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // Every wave, with no branch around it: the ticket after next and
+        // the next tile's predecessor flag (see pred_flag), taken by lane 0 of
+        // wave 0 only; every other lane's offset falls outside the window, so
+        // its atomic or load does nothing (the flag then reads as empty, as it
+        // does without a predecessor).  Results that are neither uniform nor
+        // defined in a branch are not waited for before they are used: the
+        // ticket goes to LDS at the start of the next tile, the flag is read
+        // there.
+        {
+            const bool w0l0 = wave == 0 && lane == 0;
+            ticket = static_cast<uint32_t>(__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(
+                1, make_rsrc(&ctrl[slot], 4), w0l0 ? 0u : kOutOfRange, 0, 0));
+            pred_flag = __builtin_amdgcn_raw_buffer_load_b32(
+                make_rsrc(flags + tn.g * lay.n_tt, static_cast<uint32_t>(tn.tt) * 4u),
+                w0l0 && tn.tt > 0 ? static_cast<uint32_t>(tn.tt - 1) * 4u : kOutOfRange, 0, kCpolSc1);
         }
+        // The next tile's copies (waves 1..) and the inclusive stores (wave 0)
+        // stay in flight into pass 2; the inclusive flag and the next tile's
+        // register loads follow once its first outputs are out (see pass 2).
+        lds_barrier();
 
         // ---- 4. incoming state of this wave's steps (formed by wave 0)
         Cx h[kNPL];
@@ -999,6 +1045,18 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
                     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                     __builtin_amdgcn_wave_barrier();
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                }
+                if (s == kOwnIssueStep) {
+                    // Everything this wave issued before the output store just
+                    // above has completed (the wait is normally already
+                    // satisfied: the partial reads above wait for the copies
+                    // into LDS).  Wave 0 raises the inclusive flag; every wave
+                    // issues its register loads of the next tile, which land
+                    // during the rest of the pass.
+                    wait_vm_below<1>();
+                    if (wave == 0 && lane == 0)
+                        __hip_atomic_store(&flag[tt], kFlagInclusive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (has_next) issue_own<T, CPLX>(r, p, tn, tid, c, pr, s0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
