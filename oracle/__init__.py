@@ -59,9 +59,14 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(f) for f in _SOURCES):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    # SSM_ORACLE_LIB names another build of the same sources (the sanitizer
+    # tests load an AddressSanitizer/UBSan build through it)
+    path = os.environ.get("SSM_ORACLE_LIB")
+    if not path:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(f) for f in _SOURCES):
+            build()
+    lib = ctypes.CDLL(path)
     dp = ctypes.c_void_p
     i64 = ctypes.c_int64
     lib.oracle_scan_f64.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int] + [dp] * 13 + [ctypes.c_int]

@@ -13,7 +13,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libssmscan.so")
+# SSM_SCAN_LIB names another build of the library (the sanitizer tests load a
+# host-only AddressSanitizer/UBSan build of the argument checking through it)
+LIB_PATH = os.environ.get("SSM_SCAN_LIB") or os.path.join(_PKG, "libssmscan.so")
 
 SSM_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 SSM_DISC = {"zoh": 0, "euler": 1, "trap": 2}
