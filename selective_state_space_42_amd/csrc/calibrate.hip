@@ -8,6 +8,7 @@
 
 #include <stdint.h>
 
+#include "device_math.h"
 #include "ssm_calibrate.h"
 
 namespace {
@@ -56,7 +57,63 @@ __global__ void __launch_bounds__(256) stream_kernel(const f4v* __restrict__ src
     }
 }
 
+// out[i] = f(x[i], y[i]) by the scan's own policies (see the header)
+__global__ void __launch_bounds__(256) math_eval_kernel(int fn, const float* __restrict__ x,
+                                                        const float* __restrict__ y, float* __restrict__ out,
+                                                        int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const float a = x[i];
+    const float b = (fn == 0 || fn >= 7) ? y[i] : 0.f;
+    float s = 0.f, c = 0.f, r = 0.f;
+    switch (fn) {
+        case 0:
+            r = ssm::exp_dA(a, ssm::prep_A(b));
+            break;
+        case 1:
+        case 2:
+            ssm::sin_cos_rev(__builtin_amdgcn_fractf(__builtin_fmaf(a, ssm::kInv2Pi, 0.f)), &s, &c);
+            r = fn == 1 ? s : c;
+            break;
+        case 3:
+        case 4:
+            ssm::sin_cos_poly(a, &s, &c);
+            r = fn == 3 ? s : c;
+            break;
+        case 5:
+        case 6:
+            ssm::sin_cos_wide(static_cast<double>(a), &s, &c);
+            r = fn == 5 ? s : c;
+            break;
+        default: {
+            float ez, em1;
+            ssm::exp_expm1(a * b, a * ssm::prep_A(b), &ez, &em1);
+            r = fn == 7 ? em1 : ez;
+        }
+    }
+    out[i] = r;
+}
+
 }  // namespace
+
+extern "C" int ssm_calibrate_device_math(int32_t fn, const float* x, const float* y, float* out, int64_t n,
+                                    void* stream) {
+    if (fn < 0 || fn > 8 || n < 0 || n >= (int64_t(1) << 31)) return 1;
+    if (n == 0) return 0;
+    const bool needs_y = fn == 0 || fn >= 7;
+    if (!x || !out || (needs_y && !y)) return 1;
+    const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), o1 = o0 + static_cast<uintptr_t>(n) * 4;
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), x1 = x0 + static_cast<uintptr_t>(n) * 4;
+    if (o0 < x1 && x0 < o1) return 1;
+    if (needs_y) {
+        const uintptr_t y0 = reinterpret_cast<uintptr_t>(y), y1 = y0 + static_cast<uintptr_t>(n) * 4;
+        if (o0 < y1 && y0 < o1) return 1;
+    }
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(math_eval_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), fn, x, y, out, n);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
 
 extern "C" int ssm_calibrate_stream(const void* src, size_t src_bytes, void* dst, size_t dst_bytes,
                                     int32_t nontemporal, uint64_t* clocks, void* stream) {

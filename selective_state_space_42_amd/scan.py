@@ -76,6 +76,8 @@ def _lib():
     lib.ssm_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ssm_calibrate_stream.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, ctypes.c_int32, vp, vp]
     lib.ssm_calibrate_stream.restype = ctypes.c_int
+    lib.ssm_calibrate_device_math.argtypes = [ctypes.c_int32, vp, vp, vp, ctypes.c_int64, vp]
+    lib.ssm_calibrate_device_math.restype = ctypes.c_int
     lib.ssm_scan_step.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 13
     lib.ssm_scan_step.restype = ctypes.c_int
     lib.ssm_scan_bwd.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 21 + [ctypes.c_size_t, vp]
@@ -306,6 +308,34 @@ def ssm_calibrate_stream(src, dst, nontemporal: bool = False, clocks=None, strea
                                      ctypes.c_void_p(stream))
     if st != 0:
         raise ScanError(st, "ssm_calibrate_stream")
+
+
+DEVICE_MATH = {"exp_dA": 0, "sin_hw": 1, "cos_hw": 2, "sin_poly": 3, "cos_poly": 4, "sin_wide": 5, "cos_wide": 6,
+               "expm1_zoh": 7, "exp_zoh": 8}
+
+
+def ssm_calibrate_device_math(fn: str, x, y=None, out=None, stream=None):
+    """The scan kernel's transcendental policy `fn` (a key of DEVICE_MATH)
+    applied element-wise on the GPU: out[i] = f(x[i], y[i]) (fp32 GPU tensors
+    of one shape; y for exp_dA, expm1_zoh and exp_zoh only)."""
+    code = DEVICE_MATH[fn]
+    needs_y = code == 0 or code >= 7
+    ts = [("x", x)] + ([("y", y)] if needs_y else [])
+    for name, t in ts:
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_contiguous() \
+                or t.device.type != "cuda":
+            raise ValueError(f"ssm_calibrate_device_math: {name} must be a contiguous fp32 GPU tensor")
+    if needs_y and y.shape != x.shape:
+        raise ValueError("ssm_calibrate_device_math: y must have x's shape")
+    if out is None:
+        out = torch.empty_like(x)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = _lib().ssm_calibrate_device_math(code, _ptr(x), _ptr(y) if needs_y else None, _ptr(out), x.numel(),
+                                          ctypes.c_void_p(stream))
+    if st != 0:
+        raise ScanError(st, "ssm_calibrate_device_math")
+    return out
 
 
 def ssm_scan_step(u, delta, A, B, C, D=None, theta=None, lam=None, *, h, u_prev=None, B_prev=None, disc: str,

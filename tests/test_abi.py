@@ -33,7 +33,8 @@ def test_library_exports_every_declared_symbol():
     assert {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_step", "ssm_scan_bwd", "ssm_scan_workspace_bytes",
             "ssm_scan_bwd_workspace_bytes", "ssm_ssd_fwd", "ssm_ssd_workspace_bytes", "ssm_mimo_fwd",
             "ssm_mimo_step", "ssm_mimo_workspace_bytes", "ssm_scan_status_string", "ssm_scan_abi_version",
-            "ssm_scan_last_hip_error", "ssm_scan_fwd_noalloc", "ssm_calibrate_stream"} <= set(names)
+            "ssm_scan_last_hip_error", "ssm_scan_fwd_noalloc", "ssm_calibrate_stream",
+            "ssm_calibrate_device_math"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -349,3 +350,20 @@ def test_calibrate_stream_argument_checks():
     assert lib.ssm_calibrate_stream(v(P), 320, v(P + 16), 16, 0, None, None) == INVALID              # overlapping
     assert lib.ssm_calibrate_stream(v(P), 320, v(P + (1 << 24)), 16, 2, None, None) == INVALID       # bad flag
     assert lib.ssm_calibrate_stream(v(P), 320, v(P + (1 << 24)), 16, 0, v(P + 4), None) == INVALID   # clocks
+
+
+def test_device_math_argument_checks():
+    lib = scan._lib()
+    v = ctypes.c_void_p
+    X, Y, O = P, P + (1 << 20), P + (2 << 20)
+    assert lib.ssm_calibrate_device_math(9, v(X), v(Y), v(O), 16, None) == INVALID    # unknown function
+    assert lib.ssm_calibrate_device_math(-1, v(X), v(Y), v(O), 16, None) == INVALID
+    assert lib.ssm_calibrate_device_math(0, v(X), None, v(O), 16, None) == INVALID    # exp needs y
+    assert lib.ssm_calibrate_device_math(7, v(X), None, v(O), 16, None) == INVALID    # so does expm1
+    assert lib.ssm_calibrate_device_math(1, None, None, v(O), 16, None) == INVALID
+    assert lib.ssm_calibrate_device_math(1, v(X), None, None, 16, None) == INVALID
+    assert lib.ssm_calibrate_device_math(1, v(X), None, v(X + 32), 16, None) == INVALID   # out overlaps x
+    assert lib.ssm_calibrate_device_math(0, v(X), v(Y), v(Y + 32), 16, None) == INVALID   # out overlaps y
+    assert lib.ssm_calibrate_device_math(1, v(X), None, v(O), -1, None) == INVALID
+    assert lib.ssm_calibrate_device_math(1, v(X), None, v(O), 1 << 31, None) == INVALID
+    assert lib.ssm_calibrate_device_math(1, v(X), None, v(O), 0, None) == 0               # nothing to do
