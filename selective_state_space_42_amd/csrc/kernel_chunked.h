@@ -153,6 +153,26 @@ __device__ __forceinline__ void wait_stores() {
     asm volatile("" ::: "memory");
 }
 
+// Test builds only (SSM_LOOKBACK_TEST_DELAY > 0, see the build script): a
+// bounded pause before a tile raises a flag, of 0 .. SSM_LOOKBACK_TEST_DELAY
+// sleeps of 64 x 64 clocks chosen by a hash of the chain, the tile and the
+// flag, so successors meet their predecessors' flags in scrambled orders
+// (empty, aggregate or inclusive at any distance) while every wave still ends
+// normally.  Compiles to nothing in the library.
+#ifndef SSM_LOOKBACK_TEST_DELAY
+#define SSM_LOOKBACK_TEST_DELAY 0
+#endif
+__device__ __forceinline__ void test_publish_delay(uint32_t chain, int64_t tile, uint32_t salt) {
+    if constexpr (SSM_LOOKBACK_TEST_DELAY > 0) {
+        uint32_t h = static_cast<uint32_t>(tile) * 2654435761u ^ (chain * 40503u + salt * 97u);
+        h ^= h >> 15;
+        h *= 0x2c1b3c6du;
+        h ^= h >> 12;
+        const int n = static_cast<int>(h % (SSM_LOOKBACK_TEST_DELAY + 1));
+        for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(64);
+    }
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
 // (lgkmcnt(0)) but not for its global loads, stores or copies into LDS, which
 // a __syncthreads() may wait for whenever any are in flight.  Used where
@@ -897,6 +917,7 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
                     st_agent(mine, pay_off(1, lane, j), to_f2(Ht[j]));
                 }
                 wait_stores();
+                test_publish_delay(tc.g, tt, 1u);
                 if (lane == 0) __hip_atomic_store(&flag[tt], kFlagAggregate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             if (has_next) issue_dma<T, DISC>(p, lay, tn, lane, wave - 1, &s_bcb[buf ^ 1][0][0], s_raw, s_k);
@@ -1054,8 +1075,11 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
                     // issues its register loads of the next tile, which land
                     // during the rest of the pass.
                     wait_vm_below<1>();
-                    if (wave == 0 && lane == 0)
-                        __hip_atomic_store(&flag[tt], kFlagInclusive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (wave == 0) {
+                        test_publish_delay(tc.g, tt, 2u);
+                        if (lane == 0)
+                            __hip_atomic_store(&flag[tt], kFlagInclusive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
                     if (has_next) issue_own<T, CPLX>(r, p, tn, tid, c, pr, s0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
