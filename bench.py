@@ -107,6 +107,31 @@ def mimo_algorithmic_bytes(w) -> int:
             + 4 * D * N + 4 * D + 4 * B * D * N * (1 + cplx))
 
 
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # published fp32 vector peak (packed FMA: 2 lanes x 2 flops per lane-slot)
+
+
+def ssd_algorithmic_flops(w, q: int = 64) -> int:
+    """The SSD form's four dense products per (batch row, head, chunk of q
+    steps), N states, P channels per head: C B^T (2 q^2 N), the causal
+    intra-chunk product (q (q + 1) P: row t sums t + 1 terms), C H_in (2 q N P)
+    and the chunk state B^T X (2 q N P)."""
+    B, L, N, P, H = w.batch, w.seqlen, w.dstate, w.headdim, w.heads
+    chunks = (L + q - 1) // q
+    return B * H * chunks * (2 * q * q * N + q * (q + 1) * P + 4 * q * N * P)
+
+
+def mimo_algorithmic_flops(w) -> int:
+    """fp32 vector flops per (b, t, d, n) of the complex MIMO recurrence of
+    rank R: the rotation-decay product alpha g (6) and the weighted input
+    added (4), the input q = sum_r B_r u_r (4 R: a complex-by-real multiply and
+    add per r) and the R outputs' Re(C_r g) (4 R).  Transcendentals are not
+    counted."""
+    B, L, D, N, R = w.batch, w.seqlen, w.dim, w.dstate, w.rank
+    per = (10 + 8 * R) if w.is_complex else (2 + 4 * R)
+    return B * L * D * N * per
+
+
 def mimo_decode_algorithmic_bytes(w) -> int:
     """One MIMO decode step: the step's inputs and the previous step's u and B
     read once, the state read and written once, the R outputs written once."""
@@ -435,6 +460,11 @@ def bench_ssd(args, w, torch, dev):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profile(w.name, "ssd"),
                      "algorithmic_bytes_per_launch": alg},
+        # the products' side: algorithmic matrix flops over the step time against the bf16 MFMA peak
+        "roofline_mfma": {"bound": "mfma", "achieved": ssd_algorithmic_flops(w) / (ms * 1e-3) / 1e12,
+                          "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                          "frac": ssd_algorithmic_flops(w) / (ms * 1e-3) / 1e12 / PEAK_BF16_MFMA_TFLOPS,
+                          "algorithmic_flops_per_launch": ssd_algorithmic_flops(w)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -503,9 +533,15 @@ def bench_mimo(args, w, torch, dev):
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen, "dstate": w.dstate,
                    "rank": w.rank, "disc": w.disc, "complex": w.is_complex, "io_dtype": w.io_dtype,
                    "algo": "mimo", "workspace_bytes": ws_bytes},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profile(w.name, "mimo"),
-                     "algorithmic_bytes_per_launch": alg},
+        # the prefill's vector arithmetic bounds it (fp32 recurrences of rank R
+        # per state); the HBM side is kept beside it
+        "roofline": {"bound": "alu", "achieved": mimo_algorithmic_flops(w) / (ms * 1e-3) / 1e12,
+                     "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                     "frac": mimo_algorithmic_flops(w) / (ms * 1e-3) / 1e12 / PEAK_FP32_VECTOR_TFLOPS,
+                     "traffic": None, "algorithmic_flops_per_launch": mimo_algorithmic_flops(w)},
+        "roofline_hbm": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profile(w.name, "mimo"),
+                         "algorithmic_bytes_per_launch": alg},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

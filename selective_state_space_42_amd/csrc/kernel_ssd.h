@@ -16,7 +16,7 @@
 //             + exp(cum_t) sum_n C_t[n] H_in[n, p]                            (state entering the chunk)
 //   H_out     = exp(cum_{Q-1}) H_in + sum_s exp(cum_{Q-1} - cum_s) delta_s B_s X[s, :]
 // Every term is a dense contraction and runs on the bf16 MFMA units
-// (v_mfma_f32_32x32x8_bf16, fp32 accumulation): C B^T (Q x N . N x Q), the
+// (gfx950's v_mfma_f32_32x32x16_bf16, fp32 accumulation): C B^T (Q x N . N x Q), the
 // intra-chunk product (Q x Q . Q x P), C H_in (Q x N . N x P) and the chunk
 // state (N x Q . Q x P).  The operands are rounded to bf16 (u, B and C are
 // bf16 already; the decay-weighted matrix, the weighted B and H_in are
@@ -74,6 +74,7 @@ __device__ __forceinline__ void ssd_cumsum_wave(float* s, int lane) {
 }
 
 typedef short ssd_bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 ssd_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float ssd_f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ uint16_t ssd_bf16(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
@@ -81,14 +82,25 @@ __device__ __forceinline__ float ssd_widen(uint16_t v) { return __uint_as_float(
 
 // One 32 x 32 block of A . B with K = 8 * ksteps on the bf16 MFMA units, both
 // operands in LDS with k contiguous: a_rows[i][k] (rows i0 ..) and b_cols[j][k]
-// (columns j0 ..).  Lane l supplies A[i0 + l % 32][k0 + 4 (l / 32) + 0..3] and
-// B[k0 + 4 (l / 32) + 0..3][j0 + l % 32]; the 32 x 32 result is spread as
+// (columns j0 ..).  Pairs of 8-wide k steps go to one 32x32x16 instruction,
+// for which lane l supplies A[i0 + l % 32][k0 + 8 (l / 32) + 0..7] and
+// B[k0 + 8 (l / 32) + 0..7][j0 + l % 32] (one 16-byte LDS read each); an odd
+// last step uses the 32x32x8 form, lane l supplying 4 values at
+// k0 + 4 (l / 32).  Both leave the 32 x 32 result spread as
 // acc[r] = C[i0 + 8 (r / 4) + 4 (l / 32) + r % 4][j0 + l % 32].
 template <int kStride>
 __device__ __forceinline__ void ssd_mfma_block(const uint16_t (*a_rows)[kStride], const uint16_t (*b_cols)[kStride],
                                                int i0, int j0, int ksteps, int lane, ssd_f32x16& acc) {
+    static_assert(kStride % 8 == 0, "16-byte operand rows");
     const int kh = lane >> 5;
-    for (int ks = 0; ks < ksteps; ++ks) {
+    int ks = 0;
+    for (; ks + 2 <= ksteps; ks += 2) {
+        const int k0 = ks * 8 + 8 * kh;
+        const ssd_bf16x8 av = *reinterpret_cast<const ssd_bf16x8*>(&a_rows[i0 + (lane & 31)][k0]);
+        const ssd_bf16x8 bv = *reinterpret_cast<const ssd_bf16x8*>(&b_cols[j0 + (lane & 31)][k0]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+    }
+    if (ks < ksteps) {
         const int k0 = ks * 8 + 4 * kh;
         const ssd_bf16x4 av = *reinterpret_cast<const ssd_bf16x4*>(&a_rows[i0 + (lane & 31)][k0]);
         const ssd_bf16x4 bv = *reinterpret_cast<const ssd_bf16x4*>(&b_cols[j0 + (lane & 31)][k0]);
