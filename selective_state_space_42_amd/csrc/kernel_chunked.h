@@ -735,8 +735,20 @@ __device__ __forceinline__ void pass1(const TileRegs<T>& r, const float2 (*s_dw)
 // right after its current (even smaller) ticket, so the smallest unfinished
 // ticket always makes progress.
 template <typename T, int DISC, bool CPLX>
-__global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkParams p, ChunkLayout lay) {
+__global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkParams p_in, ChunkLayout lay_in) {
     using namespace chunk;
+    // Parameters are read from the kernel-argument segment, through a pointer
+    // the compiler must treat as changed at the top of every tile.  Otherwise
+    // it keeps every loop-invariant pointer and size in scalar registers for
+    // the whole persistent loop, and the excess is spilled to vector lanes and
+    // read back (v_readlane) in every tile's control code.  The arguments are
+    // laid out in order at their natural alignment.
+    using KArgs = const __attribute__((address_space(4))) char*;
+    KArgs kargs = (KArgs)(__builtin_amdgcn_kernarg_segment_ptr());
+    constexpr size_t kLayOff = (sizeof(ChunkParams) + alignof(ChunkLayout) - 1) / alignof(ChunkLayout) *
+                               alignof(ChunkLayout);
+    const ChunkParams& p = p_in;
+    const ChunkLayout& lay = lay_in;
     using BE = Buf<T>;
     constexpr uint32_t es = BE::kSize;
     constexpr bool kFast = std::is_same_v<T, uint16_t>;
@@ -765,25 +777,12 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
     __shared__ uint32_t s_ticket[2];  // the ticket after the current tile, by tile parity (buf)
     __shared__ uint32_t s_pred_inc;  // wave 0 holds the predecessor's inclusive state (see pred_flag)
 
-    const T* u = static_cast<const T*>(p.u);
-    const T* delta = static_cast<const T*>(p.delta);
-    const T* theta = static_cast<const T*>(p.theta);
-    const T* lambda = static_cast<const T*>(p.lambda);
-    T* y = static_cast<T*>(p.y);
-    char* ws = static_cast<char*>(p.workspace);
-    uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws);
-    uint32_t* flags = reinterpret_cast<uint32_t*>(ws + lay.off_flags);
-    float2* payload = reinterpret_cast<float2*>(ws + lay.off_payload);
-    const float4* bc = reinterpret_cast<const float4*>(ws + lay.off_bc);
-    const float* kt = reinterpret_cast<const float*>(ws + lay.off_k);
-
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int lane = tid & 63;
     const int c = lane / kLPC;
     const int pr = lane % kLPC;
     const int s0 = wave * kTW;  // this wave's first step within a tile
-    const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
     const int slot = blockIdx.x % kSlots;
     const uint32_t per_tt = static_cast<uint32_t>(lay.slot_groups[slot]);
     const uint32_t slot_tiles = per_tt * static_cast<uint32_t>(lay.n_tt);
@@ -795,13 +794,14 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
     // reads them.
     uint32_t ticket = 0;  // thread 0: the ticket after the current tile (see the loop)
     if (tid == 0) {
+        uint32_t* ctrl = static_cast<uint32_t*>(p.workspace);
         s_ticket[1] = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ticket = __hip_atomic_fetch_add(&ctrl[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     uint32_t cur = __builtin_amdgcn_readfirstlane(s_ticket[1]);
     if (cur >= slot_tiles) return;
-    Tile tc = decode_tile(cur, per_tt, slot, lay, D);
+    Tile tc = decode_tile(cur, per_tt, slot, lay, p.dim);
     int buf = 0;
     issue_own<T, CPLX>(r, p, tc, tid, c, pr, s0);
     if (wave != 0) issue_dma<T, DISC>(p, lay, tc, lane, wave - 1, &s_bcb[0][0][0], s_raw, s_k);
@@ -812,6 +812,17 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
     uint32_t pred_flag = kFlagEmpty;
 
     for (;;) {
+        asm volatile("" : "+s"(kargs));
+        const ChunkParams& p = *reinterpret_cast<const ChunkParams*>((const char*)kargs);
+        const ChunkLayout& lay = *reinterpret_cast<const ChunkLayout*>((const char*)(kargs + kLayOff));
+        const T* delta = static_cast<const T*>(p.delta);
+        const T* lambda = static_cast<const T*>(p.lambda);
+        T* y = static_cast<T*>(p.y);
+        char* ws = static_cast<char*>(p.workspace);
+        uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws);
+        uint32_t* flags = reinterpret_cast<uint32_t*>(ws + lay.off_flags);
+        float2* payload = reinterpret_cast<float2*>(ws + lay.off_payload);
+        const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
         // ---- 1. stage the current tile
         wait_stores();  // this wave's loads and DMA (B/C rows, raw rows) have landed (vmcnt(0))
         __syncthreads();
