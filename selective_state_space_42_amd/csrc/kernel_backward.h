@@ -22,8 +22,8 @@
 // Work decomposition: one lane per (channel, state), LPC = 16 (N <= 16) or 64
 // lanes per channel, 64 / LPC channels of one batch row per wave (a batch
 // row's last wave may be partly idle).  Every operand of step t of a lane is
-// a wave-uniform base (scalar registers, advanced per step) plus a small
-// fixed per-lane offset, so no access needs vector address arithmetic.
+// a wave-uniform pointer (scalar registers, advanced per step) plus a small
+// fixed per-lane byte offset; no lane holds a 64-bit pointer of its own.
 //   1. bwd_ckpt_kernel sweeps forward once and stores the state before every
 //      segment of kSeg steps (the only state-sized data in memory: L/kSeg
 //      snapshots).
@@ -65,6 +65,8 @@ namespace ssm {
 namespace bwd {
 constexpr int kSeg = 8;   // steps per recompute segment (states kept in LDS)
 constexpr int kGroup = 4;  // steps whose loads are issued together
+// the snapshot sweep advances by whole groups through each segment
+static_assert(kSeg % kGroup == 0, "segments are whole load groups");
 }
 
 struct BwdParams {
@@ -151,13 +153,33 @@ __device__ __forceinline__ BwdGeo<LPC> bwd_geo(const BwdParams& p, bool chunked)
     return g;
 }
 
-// the stored bits of element i (decoded by bwd_f)
+// The stored bits (decoded by bwd_f) of element i of a wave-uniform pointer,
+// plus a lane's fixed byte offset: the address is a scalar base and a 32-bit
+// vector offset, with no per-lane 64-bit arithmetic.
 template <typename T>
-__device__ __forceinline__ uint32_t bwd_bits(const T* p, int64_t i) {
+__device__ __forceinline__ uint32_t bwd_in(const T* wave, int64_t i, uint32_t lane_bytes) {
+    const T* e = reinterpret_cast<const T*>(reinterpret_cast<const char*>(wave + i) + lane_bytes);
     if constexpr (std::is_same_v<T, float>)
-        return __float_as_uint(p[i]);
+        return __float_as_uint(*e);
     else
-        return p[i];
+        return *e;
+}
+// gradient slot: element i of a wave-uniform pointer plus a lane's byte offset
+__device__ __forceinline__ float& bwd_out(float* wave, int64_t i, uint32_t lane_bytes) {
+    return *reinterpret_cast<float*>(reinterpret_cast<char*>(wave + i) + lane_bytes);
+}
+// Step accesses within a segment: the wave's pointer, the step's byte offset
+// (uniform) and the lane's (fixed).
+template <typename T>
+__device__ __forceinline__ uint32_t bwd_ld(const T* wave, uint32_t lane_bytes, uint32_t step_bytes) {
+    const T* e = reinterpret_cast<const T*>(reinterpret_cast<const char*>(wave) + step_bytes + lane_bytes);
+    if constexpr (std::is_same_v<T, float>)
+        return __float_as_uint(*e);
+    else
+        return *e;
+}
+__device__ __forceinline__ void bwd_st(float* wave, uint32_t lane_bytes, uint32_t step_bytes, float v) {
+    *reinterpret_cast<float*>(reinterpret_cast<char*>(wave) + step_bytes + lane_bytes) = v;
 }
 
 template <typename T>
@@ -168,12 +190,15 @@ __device__ __forceinline__ float bwd_f(uint32_t raw) {
         return __uint_as_float(raw << 16);
 }
 
-// Per-lane pointers to step t's operands and gradient slots, and the
-// (uniform) number of elements each moves per step.
+// Step t's operands and gradient slots: wave-uniform pointers (the wave's
+// first channel, state 0) and each lane's byte offsets from them, for the
+// per-token arrays (tc), theta (th) and B, C (bn), inputs (l*) and fp32
+// gradients (g*); the offsets do not depend on t.
 template <typename T>
 struct BwdPtr {
     const T *u, *dt, *lam, *dy, *th, *B, *C;
     float *du, *ddt, *dlam, *dth, *dB, *dC;
+    uint32_t ltc, lth, lbn, gtc, gth, gbn;
 };
 struct BwdStride {
     int64_t tc, th, bn;  // per-token arrays, theta, B and C
@@ -181,9 +206,13 @@ struct BwdStride {
 
 template <typename T, bool CPLX, int LPC>
 __device__ __forceinline__ BwdPtr<T> bwd_ptr(const BwdParams& p, const BwdGeo<LPC>& g, int64_t t) {
-    const int64_t tc = (g.b * p.seqlen + t) * p.dim + g.d;
-    const int64_t th = tc * p.dstate + g.nc;
-    const int64_t bn = ((g.b * p.seqlen + t) * p.dstate + g.nc) * (CPLX ? 2 : 1);
+    constexpr uint32_t es = sizeof(T);
+    const int64_t tc = (g.b * p.seqlen + t) * p.dim + g.d0;  // uniform
+    const int64_t th = tc * p.dstate;
+    const int64_t bn = (g.b * p.seqlen + t) * p.dstate * (CPLX ? 2 : 1);
+    const uint32_t otc = static_cast<uint32_t>(g.d - g.d0);  // the lane's element offsets
+    const uint32_t oth = otc * static_cast<uint32_t>(p.dstate) + static_cast<uint32_t>(g.nc);
+    const uint32_t obn = static_cast<uint32_t>(g.nc) * (CPLX ? 2u : 1u);
     BwdPtr<T> q;
     q.u = static_cast<const T*>(p.u) + tc;
     q.dt = static_cast<const T*>(p.delta) + tc;
@@ -195,9 +224,15 @@ __device__ __forceinline__ BwdPtr<T> bwd_ptr(const BwdParams& p, const BwdGeo<LP
     q.du = p.du + tc;
     q.ddt = p.ddelta + tc;
     q.dlam = p.dlambda ? p.dlambda + tc : p.ddelta + tc;
-    q.dth = p.dtheta ? p.dtheta + th : p.ddelta + tc;
+    q.dth = p.dtheta ? p.dtheta + th : p.ddelta + tc;  // written only with p.dtheta
     q.dB = p.dB + bn;
     q.dC = p.dC + bn;
+    q.ltc = otc * es;
+    q.lth = (p.theta ? oth : otc) * es;
+    q.lbn = obn * es;
+    q.gtc = otc * 4u;
+    q.gth = (p.dtheta ? oth : otc) * 4u;
+    q.gbn = obn * 4u;
     return q;
 }
 
@@ -216,18 +251,19 @@ struct BwdRaw {
 // needs; else what the reverse step needs)
 template <typename T, int DISC, bool CPLX, bool FWD>
 __device__ __forceinline__ void bwd_load(const BwdPtr<T>& q, const BwdStride& st, int k, BwdRaw<CPLX>& r) {
-    const int64_t tc = k * st.tc, bn = k * st.bn;
-    r.x = bwd_bits(q.u, tc);
-    r.dt = bwd_bits(q.dt, tc);
-    if constexpr (DISC == kTrap) r.lam = bwd_bits(q.lam, tc);
-    r.br = bwd_bits(q.B, bn);
-    if constexpr (CPLX) r.bi = bwd_bits(q.B, bn + 1);
+    constexpr uint32_t es = sizeof(T);
+    const uint32_t tc = static_cast<uint32_t>(k * st.tc) * es, bn = static_cast<uint32_t>(k * st.bn) * es;
+    r.x = bwd_ld(q.u, q.ltc, tc);
+    r.dt = bwd_ld(q.dt, q.ltc, tc);
+    if constexpr (DISC == kTrap) r.lam = bwd_ld(q.lam, q.ltc, tc);
+    r.br = bwd_ld(q.B, q.lbn, bn);
+    if constexpr (CPLX) r.bi = bwd_ld(q.B, q.lbn, bn + es);
     if constexpr (FWD) {
-        if constexpr (CPLX) r.th = bwd_bits(q.th, k * st.th);
+        if constexpr (CPLX) r.th = bwd_ld(q.th, q.lth, static_cast<uint32_t>(k * st.th) * es);
     } else {
-        r.dy = bwd_bits(q.dy, tc);
-        r.cr = bwd_bits(q.C, bn);
-        if constexpr (CPLX) r.ci = bwd_bits(q.C, bn + 1);
+        r.dy = bwd_ld(q.dy, q.ltc, tc);
+        r.cr = bwd_ld(q.C, q.lbn, bn);
+        if constexpr (CPLX) r.ci = bwd_ld(q.C, q.lbn, bn + es);
     }
 }
 
@@ -391,12 +427,12 @@ __global__ void __launch_bounds__(256) bwd_adj_kernel(BwdParams p) {
         for (int j = 0; j < kG; ++j) {
             const int k = grp * kG + j;
             const int64_t kk = (k < nsteps ? k : nsteps - 1) - grp * kG;  // stay inside the chunk
-            rw[j].dt = bwd_bits(q.dt, kk * st.tc);
-            rw[j].dy = bwd_bits(q.dy, kk * st.tc);
-            rw[j].cr = bwd_bits(q.C, kk * st.bn);
+            rw[j].dt = bwd_in(q.dt, kk * st.tc, q.ltc);
+            rw[j].dy = bwd_in(q.dy, kk * st.tc, q.ltc);
+            rw[j].cr = bwd_in(q.C, kk * st.bn, q.lbn);
             if constexpr (CPLX) {
-                rw[j].ci = bwd_bits(q.C, kk * st.bn + 1);
-                rw[j].th = bwd_bits(q.th, kk * st.th);
+                rw[j].ci = bwd_in(q.C, kk * st.bn + 1, q.lbn);
+                rw[j].th = bwd_in(q.th, kk * st.th, q.lth);
             }
         }
 #pragma unroll
@@ -464,8 +500,15 @@ __global__ void __launch_bounds__(256) bwd_adj_carry_kernel(BwdParams p) {
 // occupancy (measured 15.4 against 16.2 ms on a 4 x 2560 x 8192 x 16 complex
 // problem, which 12-step segments at three workgroups per CU took).
 template <typename T, int DISC, bool CPLX, int LPC>
-__global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p) {
+__global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p_in) {
     constexpr int kSeg = bwd::kSeg, kG = bwd::kGroup, kCPW = BwdGeo<LPC>::kCPW;
+    // The parameters are re-read from the kernel-argument segment in every
+    // segment, through a pointer the compiler must treat as changed there, so
+    // that they are not all held in scalar registers across the loop (whose
+    // excess the compiler spills to vector lanes).
+    using KArgs = const __attribute__((address_space(4))) char*;
+    KArgs kargs = (KArgs)(__builtin_amdgcn_kernarg_segment_ptr());
+    const BwdParams& p = p_in;
     constexpr int kCw = CPLX ? 2 : 1;
     constexpr bool kWgSum = LPC == 16;  // the LDS sums of dB and dC exist for one state per lane up to 16
     __shared__ float2 s_h[4][kSeg][64];  // h_t of the segment
@@ -509,13 +552,15 @@ __global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p) {
     const bool has_th = CPLX && p.theta;
     if (DISC == kTrap && t_hi < L) {  // step t_hi's term on q_{t_hi - 1}: (1 - lambda) delta X_c
         const BwdPtr<T> q1 = bwd_ptr<T, CPLX>(p, g, t_hi);
-        const float e1 = (1.f - bwd_f<T>(bwd_bits(q1.lam, 0))) * bwd_f<T>(bwd_bits(q1.dt, 0));
+        const float e1 = (1.f - bwd_f<T>(bwd_in(q1.lam, 0, q1.ltc))) * bwd_f<T>(bwd_in(q1.dt, 0, q1.ltc));
         dqr = e1 * Gr;
         dqi = e1 * Gi;
     }
 
 #pragma unroll 1
     for (int64_t sg = sg_hi - 1; sg >= sg_lo; --sg) {
+        asm volatile("" : "+s"(kargs));
+        const BwdParams& p = *reinterpret_cast<const BwdParams*>((const char*)kargs);
         const int64_t t0 = sg * kSeg;
         const int len = static_cast<int>(L - t0 < kSeg ? L - t0 : kSeg);
         // state before the segment, and q_{t0-1} for the trapezoid
@@ -532,9 +577,9 @@ __global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p) {
         const BwdPtr<T> qs = bwd_ptr<T, CPLX>(p, g, t0);  // the segment's first step
         float q0r = 0.f, q0i = 0.f;
         if (DISC == kTrap && t0 > 0) {
-            const float x = bwd_f<T>(bwd_bits(qs.u, -st.tc));
-            q0r = bwd_f<T>(bwd_bits(qs.B, -st.bn)) * x;
-            if constexpr (CPLX) q0i = bwd_f<T>(bwd_bits(qs.B, -st.bn + 1)) * x;
+            const float x = bwd_f<T>(bwd_in(qs.u, -st.tc, qs.ltc));
+            q0r = bwd_f<T>(bwd_in(qs.B, -st.bn, qs.lbn)) * x;
+            if constexpr (CPLX) q0i = bwd_f<T>(bwd_in(qs.B, -st.bn + 1, qs.lbn)) * x;
         }
 
         // forward over the segment: h_t and alpha_t into LDS (steps past the
@@ -578,9 +623,9 @@ __global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p) {
             // q_{t-1} of the group's first step: the step before the group
             float qbr = q0r, qbi = q0i;
             if (DISC == kTrap && g0 > 0) {
-                const float x = bwd_f<T>(bwd_bits(qs.u, (g0 - 1) * st.tc));
-                qbr = bwd_f<T>(bwd_bits(qs.B, (g0 - 1) * st.bn)) * x;
-                if constexpr (CPLX) qbi = bwd_f<T>(bwd_bits(qs.B, (g0 - 1) * st.bn + 1)) * x;
+                const float x = bwd_f<T>(bwd_in(qs.u, (g0 - 1) * st.tc, qs.ltc));
+                qbr = bwd_f<T>(bwd_in(qs.B, (g0 - 1) * st.bn, qs.lbn)) * x;
+                if constexpr (CPLX) qbi = bwd_f<T>(bwd_in(qs.B, (g0 - 1) * st.bn + 1, qs.lbn)) * x;
             }
 #pragma unroll
             for (int j = kG - 1; j >= 0; --j) {
@@ -664,11 +709,12 @@ __global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p) {
                 gdt = bwd_chan_sum<LPC>(gdt);
                 if constexpr (DISC == kTrap) glam = bwd_chan_sum<LPC>(glam);
                 const int64_t otc = k * st.tc, obn = k * st.bn;
-                if (CPLX && p.dtheta && g.ok) qs.dth[k * st.th] = -Pi;
+                if (CPLX && p.dtheta && g.ok) bwd_st(qs.dth, qs.gth, static_cast<uint32_t>(k * st.th) * 4u, -Pi);
                 if (lead) {
-                    qs.du[otc] = gu + dy * skip;
-                    qs.ddt[otc] = gdt;
-                    if constexpr (DISC == kTrap) qs.dlam[otc] = glam;
+                    const uint32_t ob = static_cast<uint32_t>(otc) * 4u;
+                    bwd_st(qs.du, qs.gtc, ob, gu + dy * skip);
+                    bwd_st(qs.ddt, qs.gtc, ob, gdt);
+                    if constexpr (DISC == kTrap) bwd_st(qs.dlam, qs.gtc, ob, glam);
                     accD += dy * x;
                 }
                 // per (b, t, n): sums over the wave's channels (LPC = 16: its four
@@ -695,11 +741,11 @@ __global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p) {
                     }
                 } else {
                     if (lane < LPC && g.n < N) {
-                        atomicAdd(qs.dB + obn, gBr);
-                        atomicAdd(qs.dC + obn, gCr);
+                        atomicAdd(&bwd_out(qs.dB, obn, qs.gbn), gBr);
+                        atomicAdd(&bwd_out(qs.dC, obn, qs.gbn), gCr);
                         if constexpr (CPLX) {
-                            atomicAdd(qs.dB + obn + 1, gBi);
-                            atomicAdd(qs.dC + obn + 1, gCi);
+                            atomicAdd(&bwd_out(qs.dB, obn + 1, qs.gbn), gBi);
+                            atomicAdd(&bwd_out(qs.dC, obn + 1, qs.gbn), gCi);
                         }
                     }
                 }
