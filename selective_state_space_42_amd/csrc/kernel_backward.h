@@ -508,6 +508,8 @@ __global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p_in) {
     // excess the compiler spills to vector lanes).
     using KArgs = const __attribute__((address_space(4))) char*;
     KArgs kargs = (KArgs)(__builtin_amdgcn_kernarg_segment_ptr());
+    static_assert(std::is_trivially_copyable_v<BwdParams> && std::is_standard_layout_v<BwdParams>,
+                  "the argument segment holds a bitwise copy of the parameter struct");
     const BwdParams& p = p_in;
     constexpr int kCw = CPLX ? 2 : 1;
     constexpr bool kWgSum = LPC == 16;  // the LDS sums of dB and dC exist for one state per lane up to 16

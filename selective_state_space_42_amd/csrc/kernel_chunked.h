@@ -747,6 +747,9 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
     KArgs kargs = (KArgs)(__builtin_amdgcn_kernarg_segment_ptr());
     constexpr size_t kLayOff = (sizeof(ChunkParams) + alignof(ChunkLayout) - 1) / alignof(ChunkLayout) *
                                alignof(ChunkLayout);
+    static_assert(std::is_trivially_copyable_v<ChunkParams> && std::is_standard_layout_v<ChunkParams> &&
+                      std::is_trivially_copyable_v<ChunkLayout> && std::is_standard_layout_v<ChunkLayout>,
+                  "the argument segment holds bitwise copies of the parameter structs");
     const ChunkParams& p = p_in;
     const ChunkLayout& lay = lay_in;
     using BE = Buf<T>;
