@@ -37,11 +37,12 @@
 //   flag 0 = nothing, 1 = aggregate (P, h_loc) published, 2 = inclusive state
 //   published.  Tiles take tickets from one of 8 counters (one per XCD slot,
 //   blockIdx % 8) so that a tile only ever waits on tiles that started earlier
-//   (forward progress).  Flags and payloads move only through relaxed
-//   agent-scope atomics, which bypass the per-XCD L2 (coherent across XCDs);
-//   the publisher waits for its payload stores to complete (s_waitcnt
-//   vmcnt(0)) before storing the flag, and readers load the payload only after
-//   seeing the flag.  This avoids whole-L2 write-back/invalidate fences.
+//   (forward progress).  Flags move through relaxed agent-scope atomics and
+//   payloads through loads and stores with the same coherent (sc1) cache
+//   policy, which bypass the per-XCD L2 (coherent across XCDs); the
+//   publisher waits for its payload stores to complete (s_waitcnt vmcnt(0))
+//   before storing the flag, and readers load the payload only after seeing
+//   the flag.  This avoids whole-L2 write-back/invalidate fences.
 // A prep kernel zeroes flags and counters, converts B and C to fp32 rows of
 // (B re, B im, C re, C im) per (b, t, n) (zero padded to whole tiles and to
 // 16 states) and, for the trapezoid, computes K_t.
@@ -185,20 +186,32 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Agent-scope relaxed 8-byte accesses at a wave-uniform base plus a 32-bit
-// per-lane byte offset (so the address is one scalar base and one VGPR).
-__device__ __forceinline__ void st_agent(float2* base, uint32_t off, float2 v) {
-    __hip_atomic_store(reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(base) + off), __builtin_bit_cast(uint64_t, v),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 ld_agent(const float2* base, uint32_t off) {
-    return __builtin_bit_cast(
-        float2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(reinterpret_cast<const char*>(base) + off),
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
 // byte offset of (section, lane, state j) in a tile's payload
 __device__ __forceinline__ uint32_t pay_off(int section, int lane, int j) {
     return static_cast<uint32_t>(((section * 64 + lane) * chunk::kNPL + j) * 8);
+}
+
+// A lane's two states of one payload section move as one 16-byte access at a
+// wave-uniform tile base, so that one instruction covers a whole 1 KB
+// section (8-byte accesses per state left every line half written per
+// instruction, and the coherent stores went out as partial lines, twice).
+// The sc1 cache policy makes them coherent across the XCDs' L2s, as the
+// flags' agent-scope atomics are.  No reader needs them to be atomic: a
+// payload is read only after its flag, which is raised once the payload
+// stores have completed.
+typedef uint32_t pay_u32x4 __attribute__((ext_vector_type(4)));
+static_assert(chunk::kNPL == 2, "two states of a lane are one 16-byte payload entry");
+__device__ __forceinline__ void st_pay(float2* tile, int section, int lane, float2 s0, float2 s1) {
+    const pay_u32x4 v = {__float_as_uint(s0.x), __float_as_uint(s0.y), __float_as_uint(s1.x), __float_as_uint(s1.y)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, make_rsrc(tile, chunk::kPayloadF2 * 8), pay_off(section, lane, 0), 0,
+                                           chunk::kCpolSc1);
+}
+__device__ __forceinline__ void ld_pay(const float2* tile, int section, int lane, float2* s0, float2* s1) {
+    const pay_u32x4 v =
+        __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(tile, chunk::kPayloadF2 * 8), pay_off(section, lane, 0), 0,
+                                              chunk::kCpolSc1);
+    *s0 = make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
+    *s1 = make_float2(__uint_as_float(v.z), __uint_as_float(v.w));
 }
 
 struct Cx {
@@ -617,17 +630,13 @@ __device__ __forceinline__ void look_back(const uint32_t* flag, const float2* pa
             for (int q = 0; q < kLookBatch; ++q) {
                 if (q < nb) {
                     const float2* pk = pay_base + (k0 - h0 - q) * kPayloadF2;
-#pragma unroll
-                    for (int j = 0; j < kNPL; ++j) {
-                        Pv[q][j] = ld_agent(pk, pay_off(0, lane, j));
-                        Hv[q][j] = ld_agent(pk, pay_off(1, lane, j));
-                    }
+                    ld_pay(pk, 0, lane, &Pv[q][0], &Pv[q][1]);
+                    ld_pay(pk, 1, lane, &Hv[q][0], &Hv[q][1]);
                 }
             }
             if (last && found) {
                 const float2* pk = pay_base + (k0 - ni) * kPayloadF2;
-#pragma unroll
-                for (int j = 0; j < kNPL; ++j) Iv[j] = ld_agent(pk, pay_off(2, lane, j));
+                ld_pay(pk, 2, lane, &Iv[0], &Iv[1]);
             }
 #pragma unroll
             for (int q = 0; q < kLookBatch; ++q) {
@@ -833,8 +842,8 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
         float2 pred_state[kNPL];
         if (wave == 0 && pred_inc) {
             const float2* pk = payload + (tc.g * lay.n_tt + tc.tt - 1) * kPayloadF2;
-#pragma unroll
-            for (int j = 0; j < kNPL; ++j) pred_state[j] = ld_agent(pk, pay_off(2, lane, j));
+            asm volatile("" ::: "memory");  // not above the flag test
+            ld_pay(pk, 2, lane, &pred_state[0], &pred_state[1]);
         }
         if (tid == 0) {
             s_pred_inc = pred_inc ? 1u : 0u;
@@ -925,11 +934,8 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
             if (wave == 1 && tt > 0 && s_pred_inc == 0u) {
                 Cx Pt[kNPL], Ht[kNPL];
                 tile_aggregate(s_aggP, s_aggH, lane, Pt, Ht);
-#pragma unroll
-                for (int j = 0; j < kNPL; ++j) {
-                    st_agent(mine, pay_off(0, lane, j), to_f2(Pt[j]));
-                    st_agent(mine, pay_off(1, lane, j), to_f2(Ht[j]));
-                }
+                st_pay(mine, 0, lane, to_f2(Pt[0]), to_f2(Pt[1]));
+                st_pay(mine, 1, lane, to_f2(Ht[0]), to_f2(Ht[1]));
                 wait_stores();
                 test_publish_delay(tc.g, tt, 1u);
                 if (lane == 0) __hip_atomic_store(&flag[tt], kFlagAggregate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -986,17 +992,19 @@ __global__ void __launch_bounds__(chunk::kThreads, 2) chunk_scan_kernel(ChunkPar
                                to_cx(s_aggH[(w * 64 + lane) * kNPL + j]));
                 }
             }
+            Cx inc[kNPL];
+#pragma unroll
+            for (int j = 0; j < kNPL; ++j) inc[j] = cfma(Pt[j], carry[j], Ht[j]);
+            st_pay(mine, 2, lane, to_f2(inc[0]), to_f2(inc[1]));
 #pragma unroll
             for (int j = 0; j < kNPL; ++j) {
-                const Cx inc = cfma(Pt[j], carry[j], Ht[j]);
-                st_agent(mine, pay_off(2, lane, j), to_f2(inc));
                 if (tt == lay.n_tt - 1 && p.h_last && nok[j]) {
                     const int64_t hs = (tc.b * D + d) * N + pr * kNPL + j;
                     if constexpr (CPLX) {
-                        p.h_last[2 * hs] = inc.re;
-                        p.h_last[2 * hs + 1] = inc.im;
+                        p.h_last[2 * hs] = inc[j].re;
+                        p.h_last[2 * hs + 1] = inc[j].im;
                     } else {
-                        p.h_last[hs] = inc.re;
+                        p.h_last[hs] = inc[j].re;
                     }
                 }
             }
