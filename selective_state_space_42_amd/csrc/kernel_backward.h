@@ -64,9 +64,14 @@ namespace ssm {
 
 namespace bwd {
 constexpr int kSeg = 8;   // steps per recompute segment (states kept in LDS)
-constexpr int kGroup = 4;  // steps whose loads are issued together
+constexpr int kGroup = 4;  // steps whose loads are issued together (snapshot and reverse sweeps)
 // the snapshot sweep advances by whole groups through each segment
 static_assert(kSeg % kGroup == 0, "segments are whole load groups");
+// Steps whose loads the chunk-adjoint sweep issues together: it keeps no
+// per-step state, so a long group costs only the registers of its loads and
+// takes one memory latency per 16 steps (the snapshot sweep, bound by its
+// step-to-step dependence, measured slower with long groups).
+constexpr int kSweepGroup = 16;
 }
 
 struct BwdParams {
@@ -408,7 +413,7 @@ __global__ void __launch_bounds__(256) bwd_ckpt_kernel(BwdParams p) {
 // the product of conj(alpha) over it.
 template <typename T, int DISC, bool CPLX, int LPC>
 __global__ void __launch_bounds__(256) bwd_adj_kernel(BwdParams p) {
-    constexpr int kG = bwd::kGroup;
+    constexpr int kG = bwd::kSweepGroup;
     const BwdGeo<LPC> g = bwd_geo<LPC, CPLX>(p, true);
     if (g.c == 0 || g.c >= p.nchunks) return;  // whole waves
     const int64_t L = p.seqlen, N = p.dstate;
