@@ -37,10 +37,11 @@
 //      down (the combine of the fengwang.github.io essay, in reverse).
 //   3. bwd_main_kernel runs every chunk in parallel from its X_c, walking its
 //      segments from the last to the first: it recomputes a segment's states
-//      from its snapshot into wave-private LDS, then runs the reverse sweep
+//      from its snapshot into registers, then runs the reverse sweep
 //      over them.  The trapezoid's term that step t1 sends back to q_{t1-1}
-//      is (1 - lambda_{t1}) delta_{t1} X_c.  The sweeps issue their loads
-//      kGroup steps at a time.
+//      is (1 - lambda_{t1}) delta_{t1} X_c.  The snapshot and reverse sweeps
+//      issue their loads kGroup steps at a time, the chunk-adjoint sweep
+//      kSweepGroup steps.
 // Sums: du, ddelta, dlambda per (b, t, d) over the channel's lanes by DPP
 // butterflies; dB, dC per (b, t, n) over channels: across the wave's
 // channels by lane permutes, then, when a workgroup's four waves share the
@@ -63,7 +64,7 @@
 namespace ssm {
 
 namespace bwd {
-constexpr int kSeg = 8;   // steps per recompute segment (states kept in LDS)
+constexpr int kSeg = 8;   // steps per recompute segment (states kept in registers)
 constexpr int kGroup = 4;  // steps whose loads are issued together (snapshot and reverse sweeps)
 // the snapshot sweep advances by whole groups through each segment
 static_assert(kSeg % kGroup == 0, "segments are whole load groups");
@@ -499,13 +500,12 @@ __global__ void __launch_bounds__(256) bwd_adj_carry_kernel(BwdParams p) {
 
 // The reverse sweep of one chunk (every chunk in parallel), segment by
 // segment from the last: recompute the segment's states and decays from its
-// snapshot into wave-private LDS, then sweep it backwards.
-// At most 128 VGPRs so that four workgroups fit a CU (with 8-step segments
-// the LDS takes 34 KB); the few values that spill cost less than the lost
-// occupancy (measured 15.4 against 16.2 ms on a 4 x 2560 x 8192 x 16 complex
-// problem, which 12-step segments at three workgroups per CU took).
+// snapshot into registers (both segment loops are unrolled, so every index
+// into them is a constant), then sweep it backwards.  Four workgroups per CU
+// (at most 128 VGPRs) for a complex state, five (102) for a real one, whose
+// few spilled values cost less than the occupancy they buy.
 template <typename T, int DISC, bool CPLX, int LPC>
-__global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p_in) {
+__global__ void __launch_bounds__(256, CPLX ? 4 : 5) bwd_main_kernel(BwdParams p_in) {
     constexpr int kSeg = bwd::kSeg, kG = bwd::kGroup, kCPW = BwdGeo<LPC>::kCPW;
     // The parameters are re-read from the kernel-argument segment in every
     // segment, through a pointer the compiler must treat as changed there, so
@@ -518,8 +518,6 @@ __global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p_in) {
     const BwdParams& p = p_in;
     constexpr int kCw = CPLX ? 2 : 1;
     constexpr bool kWgSum = LPC == 16;  // the LDS sums of dB and dC exist for one state per lane up to 16
-    __shared__ float2 s_h[4][kSeg][64];  // h_t of the segment
-    __shared__ float2 s_a[4][kSeg][64];  // alpha_t (ZOH: (rho, e^z - 1))
     // the workgroup's sums of (dB, dC) per step of the segment and state
     __shared__ float s_bc[kWgSum ? kSeg : 1][kWgSum ? LPC : 1][2 * kCw];
     bwd_assume_disjoint(p);
@@ -589,12 +587,14 @@ __global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p_in) {
             if constexpr (CPLX) q0i = bwd_f<T>(bwd_in(qs.B, -st.bn + 1, qs.lbn)) * x;
         }
 
-        // forward over the segment: h_t and alpha_t into LDS (steps past the
+        // forward over the segment: h_t and alpha_t into registers (steps past the
         // end are not computed: the last segment of the sequence may be short)
+        float2 s_h[kSeg], s_a[kSeg];  // h_t and alpha_t of the segment (ZOH: (rho, e^z - 1)), in registers
         {
             float hr = hpr, hi = hpi, qpr = q0r, qpi = q0i;
-#pragma unroll 1
-            for (int g0 = 0; g0 < len; g0 += kG) {
+#pragma unroll
+            for (int g0 = 0; g0 < kSeg; g0 += kG) {
+                if (g0 >= len) break;  // uniform
                 BwdRaw<CPLX> rw[kG];
 #pragma unroll
                 for (int j = 0; j < kG; ++j)
@@ -614,16 +614,17 @@ __global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p_in) {
                     const float nr = ar * hr - ai * hi + br;
                     hi = ar * hi + ai * hr + bi;
                     hr = nr;
-                    s_h[w][g0 + j][lane] = make_float2(hr, hi);
-                    s_a[w][g0 + j][lane] = al;
+                    s_h[g0 + j] = make_float2(hr, hi);
+                    s_a[g0 + j] = al;
                 }
             }
         }
 
         // reverse over the segment, one load group at a time
         const int glast = (len - 1) / kG * kG;
-#pragma unroll 1
-        for (int g0 = glast; g0 >= 0; g0 -= kG) {
+#pragma unroll
+        for (int g0 = kSeg - kG; g0 >= 0; g0 -= kG) {
+            if (g0 > glast) continue;  // uniform
             BwdRaw<CPLX> rw[kG];
 #pragma unroll
             for (int j = 0; j < kG; ++j) bwd_load<T, DISC, CPLX, false>(qs, st, g0 + j < len ? g0 + j : len - 1, rw[j]);
@@ -643,10 +644,10 @@ __global__ void __launch_bounds__(256, 4) bwd_main_kernel(BwdParams p_in) {
                 const float dy = g.ch_ok ? bwd_f<T>(rw[j].dy) : 0.f;
                 const float br = bwd_f<T>(rw[j].br), bi = CPLX ? bwd_f<T>(rw[j].bi) : 0.f;
                 const float cr = bwd_f<T>(rw[j].cr), ci = CPLX ? bwd_f<T>(rw[j].ci) : 0.f;
-                const float2 al = s_a[w][k][lane];
+                const float2 al = s_a[k];
                 const float ar = al.x, ai = DISC == kZOH ? 0.f : al.y;
-                const float2 ht = s_h[w][k][lane];
-                const float2 hp = k > 0 ? s_h[w][k - 1][lane] : make_float2(hpr, hpi);
+                const float2 ht = s_h[k];
+                const float2 hp = k > 0 ? s_h[k - 1] : make_float2(hpr, hpi);
                 // y_t = Re(C h_t) + D u_t
                 Gr += dy * cr;
                 Gi -= dy * ci;
