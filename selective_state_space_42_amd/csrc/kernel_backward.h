@@ -641,7 +641,9 @@ __global__ void __launch_bounds__(256, CPLX ? 4 : 5) bwd_main_kernel(BwdParams p
                 if (k >= len) continue;  // uniform
                 const float dt = bwd_f<T>(rw[j].dt), x = bwd_f<T>(rw[j].x);
                 const float lam = DISC == kTrap ? bwd_f<T>(rw[j].lam) : 0.f;
-                const float dy = g.ch_ok ? bwd_f<T>(rw[j].dy) : 0.f;
+                // zero for a lane outside the problem: its adjoint then stays
+                // zero (it starts so) and every gradient it forms is zero
+                const float dy = g.ok ? bwd_f<T>(rw[j].dy) : 0.f;
                 const float br = bwd_f<T>(rw[j].br), bi = CPLX ? bwd_f<T>(rw[j].bi) : 0.f;
                 const float cr = bwd_f<T>(rw[j].cr), ci = CPLX ? bwd_f<T>(rw[j].ci) : 0.f;
                 const float2 al = s_a[k];
@@ -711,7 +713,6 @@ __global__ void __launch_bounds__(256, CPLX ? 4 : 5) bwd_main_kernel(BwdParams p
                     Gi = ar * Gi - ai * Gr;
                     Gr = nr;
                 }
-                if (!g.ok) gu = gdt = glam = gBr = gBi = gCr = gCi = 0.f;
                 // per (b, t, d): sums over the channel's states
                 gu = bwd_chan_sum<LPC>(gu);
                 gdt = bwd_chan_sum<LPC>(gdt);
