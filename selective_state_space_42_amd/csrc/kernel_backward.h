@@ -344,15 +344,39 @@ __device__ __forceinline__ float bwd_chan_sum(float v) {
     return v;
 }
 
-// Sum over the wave's four rows of 16 lanes (the four channels of LPC = 16),
-// every lane receiving its column's sum: the upper and lower 32 lanes are
-// swapped and added, then the odd and even rows (gfx950 permlane swaps, no
-// LDS traffic).
-__device__ __forceinline__ float bwd_rows_sum(float v) {
-    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    const float s = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+// The four sums over the wave's four rows of 16 lanes (the four channels of
+// LPC = 16) at once: a 32-lane swap exchanges the upper half of one value
+// with the lower half of another, so one add finishes a level for two
+// values, and the 16-lane swap does the same for the rows of each half.
+// Row 0 ends with the column sums of b_re, row 1 of c_re, row 2 of b_im and
+// row 3 of c_im (a real state: rows 0 and 2, b and c).
+template <bool CPLX>
+__device__ __forceinline__ float bwd_rows_sum4(float b_re, float b_im, float c_re, float c_im) {
+    auto swap32 = [](float lo, float hi) {
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+        return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    };
+    auto swap16 = [](float a, float b) {
+        const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    };
+    if constexpr (CPLX)
+        return swap16(swap32(b_re, b_im), swap32(c_re, c_im));
+    else
+        return swap16(swap32(b_re, c_re), 0.f);
+}
+// which rows hold a sum, and the (b re, b im, c re, c im) component it is
+template <bool CPLX>
+__device__ __forceinline__ bool bwd_row_live(int lane) {
+    return CPLX || (lane & 16) == 0;
+}
+template <bool CPLX>
+__device__ __forceinline__ int bwd_row_comp(int lane) {
+    const int row = lane >> 4;
+    if constexpr (CPLX)
+        return (row & 1) * 2 + (row >> 1);  // rows 0..3: b re, c re, b im, c im
+    else
+        return row >> 1;                     // rows 0, 2: b, c
 }
 
 // Forward sweep storing the state before every segment of kSeg steps (the
@@ -731,25 +755,20 @@ __global__ void __launch_bounds__(256, CPLX ? 4 : 5) bwd_main_kernel(BwdParams p
                 // channels by LDS atomics flushed once per segment (wg_sum), or
                 // one global atomic per wave
                 if constexpr (LPC == 16) {
-                    gBr = bwd_rows_sum(gBr);
-                    gCr = bwd_rows_sum(gCr);
-                    if constexpr (CPLX) {
-                        gBi = bwd_rows_sum(gBi);
-                        gCi = bwd_rows_sum(gCi);
-                    }
-                }
-                if (kWgSum && wg_sum) {
-                    if (lane < LPC) {
-                        float* acc = &s_bc[kWgSum ? k : 0][kWgSum ? g.n : 0][0];
-                        atomicAdd(acc, gBr);
-                        atomicAdd(acc + kCw, gCr);
-                        if constexpr (CPLX) {
-                            atomicAdd(acc + 1, gBi);
-                            atomicAdd(acc + kCw + 1, gCi);
+                    // every live row of the wave ends with the column sums of
+                    // one of the four values: one add per lane
+                    const float v = bwd_rows_sum4<CPLX>(gBr, gBi, gCr, gCi);
+                    if (bwd_row_live<CPLX>(lane)) {
+                        const int comp = bwd_row_comp<CPLX>(lane);  // 0 B re, 1 B im (complex), kCw + . for C
+                        if (kWgSum && wg_sum) {
+                            atomicAdd(&s_bc[kWgSum ? k : 0][kWgSum ? g.n : 0][comp], v);
+                        } else if (g.n < N) {
+                            float* dst = comp < kCw ? qs.dB : qs.dC;
+                            atomicAdd(&bwd_out(dst, obn + comp % kCw, qs.gbn), v);
                         }
                     }
                 } else {
-                    if (lane < LPC && g.n < N) {
+                    if (g.n < N) {
                         atomicAdd(&bwd_out(qs.dB, obn, qs.gbn), gBr);
                         atomicAdd(&bwd_out(qs.dC, obn, qs.gbn), gCr);
                         if constexpr (CPLX) {
