@@ -151,6 +151,7 @@ def mimo_decode_algorithmic_bytes(w) -> int:
 KERNEL_SOURCES = {
     "chunked": ["kernel_chunked.h"],
     "sequential": ["kernel_sequential.h"],
+    "sweep": ["kernel_sweep.h"],
     "step": ["kernel_step.h"],
     "backward": ["kernel_backward.h"],
     "ssd": ["kernel_ssd.h"],
@@ -700,7 +701,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--algo", default="auto", choices=["auto", "sequential", "chunked"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "sequential", "chunked", "sweep"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (ssm_scan_bwd) instead")
@@ -722,7 +723,7 @@ def main():
 
     from selective_state_space_42_amd.inputs import (DECODE_WORKLOADS, MIMO_DECODE_WORKLOADS, MIMO_WORKLOADS,
                                                      SSD_WORKLOADS, WORKLOADS, make_inputs)
-    from selective_state_space_42_amd.scan import make_desc, ssm_scan_fwd, ssm_scan_workspace_bytes
+    from selective_state_space_42_amd.scan import make_desc, ssm_scan_algo, ssm_scan_fwd, ssm_scan_workspace_bytes
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -770,9 +771,7 @@ def main():
     tc = w.batch * w.seqlen * w.dim
     alg_bytes = algorithmic_bytes(w)
     achieved = alg_bytes / (ms * 1e-3) / 1e9
-    algo_used = args.algo
-    if algo_used == "auto":
-        algo_used = "chunked" if ws_bytes > 0 else "sequential"
+    algo_used = ssm_scan_algo(desc)
     traffic = traffic_from_profile(w.name, algo_used)
 
     out = {

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 4
+#define SSM_SCAN_ABI_VERSION 5
 
 /* Element type of u, delta, B, C, theta, lambda and y.  A, D and h_last are
  * always fp32; all arithmetic is fp32 (bf16 inputs are widened exactly, y is
@@ -67,16 +67,27 @@ typedef enum {
  * channel's states across lanes; needs many channels to fill the GPU; any
  * N <= 64).  CHUNKED splits the sequence into tiles of 96 steps x 8 channels,
  * keeps each tile's state in registers and carries it between tiles with a
- * decoupled look-back (fills the GPU at any shape; N <= 16).  AUTO uses
- * CHUNKED when N <= 16, else SEQUENTIAL.  Both give the same result up to
- * rounding. */
-typedef enum { SSM_ALGO_AUTO = 0, SSM_ALGO_SEQUENTIAL = 1, SSM_ALGO_CHUNKED = 2 } ssm_algo_t;
+ * decoupled look-back (fills the GPU at any shape; N <= 16).  SWEEP gives
+ * each lane one (channel, state) and sweeps the whole sequence in one pass,
+ * 16 steps at a time staged through LDS (N <= 16; needs no workspace; fills
+ * the GPU once B * ceil(D/4) reaches a few waves per SIMD; UNSUPPORTED when
+ * 34*D*N*esize reaches 2^31).  AUTO uses SWEEP when N <= 16 and
+ * B * ceil(D/4) >= 2048 for a real state or >= 3072 for a complex exp-Euler
+ * one (two and three waves per SIMD of a 256-CU GPU, where it measured
+ * faster; never for the complex trapezoid), else CHUNKED when N <= 16, else
+ * SEQUENTIAL.  All give the same result up to rounding. */
+typedef enum {
+    SSM_ALGO_AUTO = 0,
+    SSM_ALGO_SEQUENTIAL = 1,
+    SSM_ALGO_CHUNKED = 2,
+    SSM_ALGO_SWEEP = 3
+} ssm_algo_t;
 
 typedef enum {
     SSM_OK = 0,
     SSM_ERR_INVALID_ARGUMENT = 1,   /* null required pointer, bad size, overflow,
                                        misalignment, forbidden NULL/non-NULL combination */
-    SSM_ERR_UNSUPPORTED = 2,        /* complex ZOH, dstate > 64 (> 16 for CHUNKED),
+    SSM_ERR_UNSUPPORTED = 2,        /* complex ZOH, dstate > 64 (> 16 for CHUNKED and SWEEP),
                                        unknown enum value, or (CHUNKED) a shape whose
                                        per-tile windows exceed 32-bit offsets:
                                        24*D*N*esize, 98*D*esize or 4*D*N above 2^30 */
@@ -103,6 +114,11 @@ typedef struct {
  * channels: the look-back payloads) plus 260 bytes per (batch, step) for the
  * fp32 B/C rows; e.g. 4.6 GB for B=1, L=2^20, D=1024. */
 size_t ssm_scan_workspace_bytes(const ssm_scan_desc_t *desc);
+
+/* The kernel family ssm_scan_fwd runs for `desc` (an ssm_algo_t other than
+ * SSM_ALGO_AUTO: desc->algo itself when it is not AUTO, else the family AUTO
+ * picks for the shape), or -1 for an invalid descriptor.  Touches no device. */
+int ssm_scan_algo(const ssm_scan_desc_t *desc);
 
 /*
  * Forward selective scan.

@@ -1,0 +1,457 @@
+// kernel_sweep.h -- the lane sweep: one lane per (channel, state), one pass
+// over the whole sequence.
+//
+// When batch rows x channels x states give every SIMD of the GPU a few waves
+// of work, the sequence needs no splitting: each lane carries its own state
+// h_t[n] from t = 0 to L - 1 in registers, discretising and contracting as it
+// goes.  Against the chunked kernel every element's work is done once (no
+// second pass over a stored alpha_t, no aggregate sums, no look-back), and
+// the kernel needs no workspace, no flags and no workgroup barriers.
+//
+// Work decomposition
+//   lane  = (channel c, state n): 16 lanes per channel, c = lane / 16; lanes
+//           with n >= N carry a zero state.
+//   wave  = 4 consecutive channels of one batch row, every step.  Waves are
+//           independent; a workgroup only packs four of them, each with its
+//           own LDS region.
+//   block = 16 steps.  The wave stages the block's per-step terms in LDS,
+//           sweeps the 16 steps, then sums the 16 lanes' partial outputs
+//           through an LDS transpose so that lane (c, n) finishes y at step n
+//           of the block for channel c.
+// Staging of a block (every load issued one block ahead, through buffer
+// resources that return 0 outside the data, so ragged blocks need no branch):
+//   - lane (c, n) loads u, delta (the trapezoid also lambda and the next
+//     step's delta and lambda) at step n of the block for channel c, forms
+//     that (step, channel)'s terms (delta, w) once for the whole wave, and
+//     keeps the output's skip term for the step it finishes;
+//   - lane (c, n) loads B_t[n] and C_t[n] for steps c, c+4, c+8, c+12 (the
+//     wave's four channels share them) and, for the trapezoid, the row sums
+//     K_t = Re(sum_n C_t[n] B_t[n]) are formed from those with 16-lane sums;
+//   - lane (c, n) loads its own theta_t[n] for the 16 steps (coalesced: a
+//     wave reads 64 consecutive elements per step).
+//
+// The recurrence per discretisation (the discretisation table of the
+// ai.tomabc.com Mamba-3 story; ZOH also section 2.1 of the blog.lonae.com
+// essay), carried in fp32:
+//   ZOH     h_t = e^{delta A} h_{t-1} + (e^{delta A} - 1)/A B_t u_t   (delta B_t u_t at A = 0)
+//   Euler   h_t = alpha_t h_{t-1} + delta_t B_t u_t
+//   trap.   carried as g_t = h_t + beta'_{t+1} B_t u_t with beta'_t = (1 - lambda_t) delta_t:
+//           g_t = alpha_t g_{t-1} + (lambda_t delta_t + beta'_{t+1}) u_t B_t and
+//           y_t = Re(sum_n C_t g_t) + (D - beta'_{t+1} K_t) u_t, beta'_L = 0
+//           (the two-band form of the exponential-trapezoidal rule; the
+//           same substitution as the chunked kernel's).
+// with alpha_t = e^{delta_t A} e^{i theta_t} for a complex state (the
+// complex-state section of the same story) and y_t = Re(sum_n C_t h_t) + D u_t
+// from the post-update state (the mamba2_ssd loop, section 3.2 of the
+// blog.lonae.com essay).
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "device_math.h"
+
+namespace ssm {
+
+namespace sweep {
+constexpr int kLPC = 16;              // lanes per channel: states n = 0 .. 15
+constexpr int kCPW = 64 / kLPC;       // channels per wave
+constexpr int kS = kLPC;              // steps per block (lane n finishes step n)
+constexpr int kWaves = 4;             // waves per workgroup (independent)
+constexpr int kRedStride = kS + 1;    // padded row of the output transpose
+constexpr int kBcSteps = kS / kCPW;   // B/C steps loaded per lane and block
+// Waves of work from which the sweep beats the chunked kernel, measured on
+// MI355X (1024 SIMDs): two waves per SIMD for a real state, three for a
+// complex exp-Euler one (its per-step theta reads are small pieces whose
+// latency the extra waves hide).  The complex trapezoid measured slower than
+// the chunked kernel at 2.5 and 5 waves per SIMD and is left to it.
+constexpr int64_t kMinWavesReal = 2048;
+constexpr int64_t kMinWavesComplex = 3072;
+}  // namespace sweep
+
+struct SweepParams {
+    const void* u;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* Dskip;
+    const void* theta;
+    const void* lambda;
+    void* y;
+    float* h_last;
+    const float* h0;  // state before step 0, layout of h_last (NULL: zero)
+    const float* q0;  // trapezoid: q_{-1} = B_{-1} u_{-1}, layout of h_last (NULL: zero)
+    float* q_last;    // trapezoid: q_{L-1} = B_{L-1} u_{L-1} (written when not NULL)
+    int64_t batch, seqlen, dim, dstate;
+};
+
+// Waves of a launch (one per 4 channels of a batch row).
+inline int64_t sweep_waves(int64_t B, int64_t D) { return B * ((D + sweep::kCPW - 1) / sweep::kCPW); }
+
+// Whether the automatic choice takes the sweep for this shape and mode.
+inline bool sweep_preferred(int64_t B, int64_t D, bool is_complex, bool trap) {
+    if (!is_complex) return sweep_waves(B, D) >= sweep::kMinWavesReal;
+    return !trap && sweep_waves(B, D) >= sweep::kMinWavesComplex;
+}
+
+// The per-block byte offsets a lane forms are 32-bit: 17 rows of D elements
+// and 16 steps of D x N theta elements must fit.
+inline bool sweep_offsets_fit(int64_t D, int64_t N, int64_t es) {
+    return (sweep::kS + 1) * D * N * es * 2 < (int64_t(1) << 31);
+}
+
+// LDS of one wave.
+struct SweepLds {
+    float4 bc[sweep::kS][sweep::kLPC];  // (B re, B im, C re, C im) per (step, state); real: (B, 0, C, 0)
+    float2 dw[sweep::kS][sweep::kCPW];  // (delta, w) per (step, channel)
+    float k[sweep::kS];                 // K_t (trapezoid)
+    float red[64 * sweep::kRedStride];  // the lanes' partial outputs, one padded row per lane
+};
+
+// One block's loads, as they arrive: per-(step, channel) rows for the lane's
+// step, B/C entries for its kBcSteps steps.
+template <typename T>
+struct SweepRows {
+    uint32_t x, dt, lam, dtn, lamn;  // stored bits
+    float bc[sweep::kBcSteps][4];    // (B re, B im, C re, C im)
+};
+
+template <typename T>
+struct SweepTheta;
+template <>
+struct SweepTheta<uint16_t> {
+    uint32_t v[sweep::kS];
+    __device__ __forceinline__ float get(int s) const { return bf16_lo(v[s]); }
+    __device__ __forceinline__ float absmax() const { return 0.f; }
+};
+template <>
+struct SweepTheta<float> {
+    float v[sweep::kS];
+    __device__ __forceinline__ float get(int s) const { return v[s]; }
+    __device__ __forceinline__ float absmax() const {
+        float m = 0.f;
+#pragma unroll
+        for (int s = 0; s < sweep::kS; ++s) m = fmaxf(m, fabsf(v[s]));
+        return m;
+    }
+};
+
+// Per-lane geometry of a wave (uniform parts in scalar registers).
+struct SweepLane {
+    int64_t b, d0;
+    int nch, c, n;
+    bool cok, sok;
+};
+
+// Issue the per-(step, channel) and B/C loads of the block starting at step
+// t0 (any t0: past the end every load returns 0).  PAIRS: B and C are aligned
+// to whole complex entries, so an entry is one load.
+template <typename T, int DISC, bool CPLX, bool PAIRS>
+__device__ __forceinline__ void sweep_issue(const SweepParams& p, const SweepLane& g, int64_t t0, SweepRows<T>& r) {
+    using namespace sweep;
+    using BE = Buf<T>;
+    constexpr uint32_t es = BE::kSize;
+    constexpr int kCE = CPLX ? 2 : 1;
+    const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
+    const int64_t left = L - t0 > 0 ? L - t0 : 0;
+    // rows t0 .. t0 + 16 of the wave's channels (the trapezoid reads one past the block)
+    {
+        const int64_t rows = left > kS + 1 ? kS + 1 : left;
+        const uint32_t bytes = rows ? static_cast<uint32_t>((rows - 1) * D + g.nch) * es : 0u;
+        const int64_t base = rows ? (g.b * L + t0) * D + g.d0 : 0;
+        const uint32_t off = g.cok ? static_cast<uint32_t>(g.n * D + g.c) * es : kOutOfRange;
+        const uint32_t offn = g.cok ? static_cast<uint32_t>((g.n + 1) * D + g.c) * es : kOutOfRange;
+        const rsrc_t ru = make_rsrc(static_cast<const T*>(p.u) + base, bytes);
+        const rsrc_t rd = make_rsrc(static_cast<const T*>(p.delta) + base, bytes);
+        r.x = BE::load_raw(ru, off);
+        r.dt = BE::load_raw(rd, off);
+        if constexpr (DISC == kTrap) {
+            const rsrc_t rl = make_rsrc(static_cast<const T*>(p.lambda) + base, bytes);
+            r.lam = BE::load_raw(rl, off);
+            r.dtn = BE::load_raw(rd, offn);
+            r.lamn = BE::load_raw(rl, offn);
+        }
+    }
+    // B/C entries of steps c + 4j, state n
+    const int64_t steps = left > kS ? kS : left;
+    const uint32_t bytes = static_cast<uint32_t>(steps * N * kCE) * es;
+    const int64_t base = steps ? (g.b * L + t0) * N * kCE : 0;
+    const rsrc_t rB = make_rsrc(static_cast<const T*>(p.B) + base, bytes);
+    const rsrc_t rC = make_rsrc(static_cast<const T*>(p.C) + base, bytes);
+    const bool nok = g.n < N;
+#pragma unroll
+    for (int j = 0; j < kBcSteps; ++j) {
+        const int s = g.c + kCPW * j;
+        const uint32_t off = nok ? static_cast<uint32_t>((s * N + g.n) * kCE) * es : kOutOfRange;
+        if constexpr (!CPLX) {
+            r.bc[j][0] = BE::load(rB, off);
+            r.bc[j][1] = 0.f;
+            r.bc[j][2] = BE::load(rC, off);
+            r.bc[j][3] = 0.f;
+        } else if constexpr (PAIRS) {
+            BE::load_pair(rB, off, &r.bc[j][0], &r.bc[j][1]);
+            BE::load_pair(rC, off, &r.bc[j][2], &r.bc[j][3]);
+        } else {
+            const uint32_t off1 = nok ? off + es : kOutOfRange;
+            r.bc[j][0] = BE::load(rB, off);
+            r.bc[j][1] = BE::load(rB, off1);
+            r.bc[j][2] = BE::load(rC, off);
+            r.bc[j][3] = BE::load(rC, off1);
+        }
+    }
+}
+
+// Where a lane's theta of the block starting at t0 lies: the resource (empty
+// past the end or without theta), the lane's offset at the block's first
+// step and the stride between steps.
+struct SweepThetaSrc {
+    rsrc_t r;
+    uint32_t off, step;
+};
+template <typename T>
+__device__ __forceinline__ SweepThetaSrc sweep_theta_src(const SweepParams& p, const SweepLane& g, int64_t t0) {
+    using namespace sweep;
+    constexpr uint32_t es = Buf<T>::kSize;
+    const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
+    const int64_t left = L - t0 > 0 ? L - t0 : 0;
+    const int64_t steps = left > kS ? kS : left;
+    const T* theta = static_cast<const T*>(p.theta);
+    const uint32_t bytes = theta && steps ? static_cast<uint32_t>(((steps - 1) * D + g.nch) * N) * es : 0u;
+    const int64_t base = theta && steps ? ((g.b * L + t0) * D + g.d0) * N : 0;
+    SweepThetaSrc q;
+    q.r = make_rsrc(theta ? theta + base : static_cast<const T*>(p.u), bytes);
+    q.off = g.sok ? static_cast<uint32_t>(g.c * N + g.n) * es : kOutOfRange;
+    q.step = static_cast<uint32_t>(D * N) * es;
+    return q;
+}
+template <typename T>
+__device__ __forceinline__ void sweep_theta_load(const SweepThetaSrc& q, int st, SweepTheta<T>& th) {
+    if constexpr (std::is_same_v<T, uint16_t>)
+        th.v[st] = __builtin_amdgcn_raw_buffer_load_b16(q.r, q.off + st * q.step, 0, 0);
+    else
+        th.v[st] = Buf<float>::load(q.r, q.off + st * q.step);
+}
+
+// Sum of v over the 16 lanes of each row (one channel's lanes), in every
+// lane of the row: DPP moves within the row (swap neighbours, swap pairs,
+// mirror within each half-row, mirror the row), so no LDS round trip.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp_f<0x141>(v);  // row_half_mirror
+    v += dpp_f<0x140>(v);  // row_mirror
+    return v;
+}
+
+// Turn a block's loads into the wave's LDS terms; returns the skip term of
+// the (step, channel) this lane finishes.
+template <typename T, int DISC, bool CPLX>
+__device__ __forceinline__ float sweep_commit(SweepLds& s, const SweepLane& g, const SweepRows<T>& r, float dsk) {
+    using namespace sweep;
+    using BE = Buf<T>;
+    const float x = BE::widen(r.x), dt = BE::widen(r.dt);
+#pragma unroll
+    for (int j = 0; j < kBcSteps; ++j)
+        s.bc[g.c + kCPW * j][g.n] = make_float4(r.bc[j][0], r.bc[j][1], r.bc[j][2], r.bc[j][3]);
+    float w, ey;
+    if constexpr (DISC == kZOH) {
+        w = x;
+        ey = dsk * x;
+    } else if constexpr (DISC == kEuler) {
+        w = dt * x;
+        ey = dsk * x;
+    } else {
+        const float lam = BE::widen(r.lam), dtn = BE::widen(r.dtn), lamn = BE::widen(r.lamn);
+        const float bnext = (1.f - lamn) * dtn;  // beta'_{t+1} (zero past the end)
+        w = (lam * dt + bnext) * x;
+        float kt[kBcSteps];
+#pragma unroll
+        for (int j = 0; j < kBcSteps; ++j) kt[j] = row16_sum(r.bc[j][2] * r.bc[j][0] - r.bc[j][3] * r.bc[j][1]);
+        if (g.n == 0) {
+#pragma unroll
+            for (int j = 0; j < kBcSteps; ++j) s.k[g.c + kCPW * j] = kt[j];  // K_t = Re(sum_n C_t B_t)
+        }
+        ey = (dsk - bnext * s.k[g.n]) * x;
+    }
+    s.dw[g.n][g.c] = make_float2(dt, w);
+    return ey;
+}
+
+// Sweep the 16 steps of a block from the lane's state (gr, gi), writing each
+// step's partial output Re(C_t[n] g_t[n]) to the lane's row of s.red.  Once a
+// step's theta is used, the same register is loaded with that step's theta
+// of the next block (from `nq`).
+template <typename T, int DISC, bool CPLX, int SC>
+__device__ __forceinline__ void sweep_steps(SweepLds& s, const SweepLane& g, SweepTheta<T>& th,
+                                            const SweepThetaSrc& nq, float a, float a2, float inv_a, float& gr,
+                                            float& gi) {
+    using namespace sweep;
+    float* red = s.red + (g.c * kLPC + g.n) * kRedStride;
+    float2 nx_dw = s.dw[0][g.c];
+    float4 nx_bc = s.bc[0][g.n];
+#pragma unroll
+    for (int st = 0; st < kS; ++st) {
+        const float2 dw = nx_dw;  // (delta, w)
+        const float4 bc = nx_bc;
+        if (st + 1 < kS) {
+            nx_dw = s.dw[st + 1][g.c];
+            nx_bc = s.bc[st + 1][g.n];
+        }
+        float py;
+        if constexpr (CPLX) {
+            const float rho = exp_dA(dw.x, a2);
+            float sn, cs;
+            sin_cos<SC>(th.get(st), &sn, &cs);
+            sweep_theta_load<T>(nq, st, th);
+            const float ar = rho * cs, ai = rho * sn;
+            const float ur = dw.y * bc.x, ui = dw.y * bc.y;
+            const float nr = ar * gr - ai * gi + ur;
+            const float ni = ar * gi + ai * gr + ui;
+            gr = nr;
+            gi = ni;
+            py = bc.z * gr - bc.w * gi;
+        } else {
+            float rho, bt;
+            if constexpr (DISC == kZOH) {
+                float em1;
+                exp_expm1(dw.x * a, dw.x * a2, &rho, &em1);
+                bt = (a != 0.f ? em1 * inv_a : dw.x) * (dw.y * bc.x);
+            } else {
+                rho = exp_dA(dw.x, a2);
+                bt = dw.y * bc.x;
+            }
+            gr = rho * gr + bt;
+            py = bc.z * gr;
+        }
+        red[st] = py;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// One block: commit the staged loads, issue the next block's, sweep, and
+// finish the outputs of the block's 16 steps.
+template <typename T, int DISC, bool CPLX, bool PAIRS>
+__device__ __forceinline__ void sweep_block(const SweepParams& p, SweepLds& s, const SweepLane& g, int64_t t0,
+                                            SweepRows<T>& r, SweepTheta<T>& th, float a, float a2, float inv_a,
+                                            float dsk, float& gr, float& gi) {
+    using namespace sweep;
+    using BE = Buf<T>;
+    constexpr uint32_t es = BE::kSize;
+    if constexpr (CPLX) {
+        // Keep the workgroup's waves in step, block by block, so that their
+        // theta reads of one step (adjacent 128- or 256-byte pieces of one
+        // row) reach memory together.  Nothing is exchanged: no memory wait.
+        __builtin_amdgcn_s_barrier();
+    }
+    const float ey = sweep_commit<T, DISC, CPLX>(s, g, r, dsk);
+    sweep_issue<T, DISC, CPLX, PAIRS>(p, g, t0 + kS, r);
+    const SweepThetaSrc nq = sweep_theta_src<T>(p, g, t0 + kS);
+
+    if constexpr (CPLX && std::is_same_v<T, float>) {
+        // fp32 sin/cos: the polynomials when every angle of the wave's block
+        // is within pi/4, else the fp64-reduced evaluation
+        if (__all(th.absmax() <= kPiOver4))
+            sweep_steps<T, DISC, CPLX, kSinCosPoly>(s, g, th, nq, a, a2, inv_a, gr, gi);
+        else
+            sweep_steps<T, DISC, CPLX, kSinCosWide>(s, g, th, nq, a, a2, inv_a, gr, gi);
+    } else {
+        sweep_steps<T, DISC, CPLX, kSinCosHw>(s, g, th, nq, a, a2, inv_a, gr, gi);
+    }
+
+    // sum over the channel's 16 lanes: lane (c, n) takes step n
+    float acc = ey;
+#pragma unroll
+    for (int m = 0; m < kLPC; ++m) acc += s.red[(g.c * kLPC + m) * kRedStride + g.n];
+
+    const int64_t L = p.seqlen, D = p.dim;
+    const int64_t left = L - t0;
+    const int64_t steps = left > kS ? kS : left;
+    const uint32_t bytes = static_cast<uint32_t>((steps - 1) * D + g.nch) * es;
+    const rsrc_t ry = make_rsrc(static_cast<T*>(p.y) + (g.b * L + t0) * D + g.d0, bytes);
+    BE::store(ry, g.cok ? static_cast<uint32_t>(g.n * D + g.c) * es : kOutOfRange, acc);
+}
+
+template <typename T, int DISC, bool CPLX, bool PAIRS>
+__global__ void __launch_bounds__(sweep::kWaves * 64, 4) sweep_scan_kernel(SweepParams p) {
+    using namespace sweep;
+    using E = Elem<T>;
+    constexpr int kCE = CPLX ? 2 : 1;
+    __shared__ SweepLds s_all[kWaves];
+    // the wave index is uniform; saying so keeps every block address and
+    // buffer resource in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
+    const int64_t n_dblk = (D + kCPW - 1) / kCPW;
+    // Waves past the last channel group run the same blocks with no channel
+    // (every load out of range, every store dropped), so that each wave of a
+    // workgroup meets the same barriers.
+    const int64_t waves = p.batch * n_dblk;
+    const int64_t wv = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+    const bool live = wv < waves;
+    SweepLds& s = s_all[wave];
+
+    SweepLane g;
+    g.b = live ? wv / n_dblk : 0;
+    g.d0 = live ? (wv % n_dblk) * kCPW : 0;
+    g.nch = live ? static_cast<int>(D - g.d0 < kCPW ? D - g.d0 : kCPW) : 0;
+    g.c = lane / kLPC;
+    g.n = lane % kLPC;
+    g.cok = g.c < g.nch;
+    g.sok = g.cok && g.n < N;
+    const int64_t d = g.d0 + g.c;
+
+    const float a = g.sok ? p.A[d * N + g.n] : 0.f;
+    const float a2 = prep_A(a);
+    const float inv_a = a != 0.f ? 1.f / a : 0.f;
+    const float dsk = g.cok && p.Dskip ? p.Dskip[d] : 0.f;
+
+    // initial state (the trapezoid carries g_{-1} = h_{-1} + beta'_0 q_{-1})
+    const int64_t sidx = (g.b * D + d) * N + g.n;  // (b, d, n) in the layout of h_last
+    float gr = 0.f, gi = 0.f;
+    if (g.sok && p.h0) {
+        gr = p.h0[kCE * sidx];
+        if constexpr (CPLX) gi = p.h0[2 * sidx + 1];
+    }
+    if constexpr (DISC == kTrap) {
+        if (g.sok && p.q0) {
+            const int64_t tc = g.b * L * D + d;
+            const float bp0 = (1.f - E::load(static_cast<const T*>(p.lambda), tc)) *
+                              E::load(static_cast<const T*>(p.delta), tc);
+            gr += bp0 * p.q0[kCE * sidx];
+            if constexpr (CPLX) gi += bp0 * p.q0[2 * sidx + 1];
+        }
+    }
+
+    SweepRows<T> r;
+    SweepTheta<T> th;
+    sweep_issue<T, DISC, CPLX, PAIRS>(p, g, 0, r);
+    if constexpr (CPLX) {
+        const SweepThetaSrc q = sweep_theta_src<T>(p, g, 0);
+#pragma unroll
+        for (int st = 0; st < kS; ++st) sweep_theta_load<T>(q, st, th);
+    }
+    for (int64_t t0 = 0; t0 < L; t0 += kS)
+        sweep_block<T, DISC, CPLX, PAIRS>(p, s, g, t0, r, th, a, a2, inv_a, dsk, gr, gi);
+
+    // the trapezoid's g_{L-1} is h_{L-1} (beta'_L = 0)
+    if (g.sok && p.h_last) {
+        p.h_last[kCE * sidx] = gr;
+        if constexpr (CPLX) p.h_last[2 * sidx + 1] = gi;
+    }
+    if constexpr (DISC == kTrap) {
+        if (g.sok && p.q_last) {  // q_{L-1} = B_{L-1} u_{L-1}
+            const float x = E::load(static_cast<const T*>(p.u), (g.b * L + L - 1) * D + d);
+            const int64_t k = (g.b * L + L - 1) * N + g.n;
+            p.q_last[kCE * sidx] = E::load(static_cast<const T*>(p.B), kCE * k) * x;
+            if constexpr (CPLX) p.q_last[2 * sidx + 1] = E::load(static_cast<const T*>(p.B), 2 * k + 1) * x;
+        }
+    }
+}
+
+}  // namespace ssm

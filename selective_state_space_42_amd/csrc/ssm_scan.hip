@@ -14,6 +14,7 @@
 #include "ssm_scan.h"
 #include "device_common.h"
 #include "kernel_sequential.h"
+#include "kernel_sweep.h"
 #include "kernel_chunked.h"
 #include "kernel_step.h"
 #include "kernel_backward.h"
@@ -83,7 +84,7 @@ int check_desc(const ssm_scan_desc_t* d) {
     if (d->io_dtype != SSM_DTYPE_F32 && d->io_dtype != SSM_DTYPE_BF16) return SSM_ERR_UNSUPPORTED;
     if (d->disc < SSM_DISC_ZOH || d->disc > SSM_DISC_EXP_TRAPEZOIDAL) return SSM_ERR_UNSUPPORTED;
     if (d->is_complex != 0 && d->is_complex != 1) return SSM_ERR_UNSUPPORTED;
-    if (d->algo < SSM_ALGO_AUTO || d->algo > SSM_ALGO_CHUNKED) return SSM_ERR_UNSUPPORTED;
+    if (d->algo < SSM_ALGO_AUTO || d->algo > SSM_ALGO_SWEEP) return SSM_ERR_UNSUPPORTED;
     if (d->is_complex && d->disc == SSM_DISC_ZOH) return SSM_ERR_UNSUPPORTED;
     if (d->dstate > 64) return SSM_ERR_UNSUPPORTED;
     // B*L*D*N*2 complex words of 4 bytes must fit an int64 byte offset.
@@ -99,7 +100,51 @@ int check_desc(const ssm_scan_desc_t* d) {
 int choose_algo(const ssm_scan_desc_t* d) {
     if (d->algo != SSM_ALGO_AUTO) return d->algo;
     if (d->dstate > ssm::kChunkLanes) return SSM_ALGO_SEQUENTIAL;
+    if (ssm::sweep_preferred(d->batch, d->dim, d->is_complex != 0, d->disc == SSM_DISC_EXP_TRAPEZOIDAL) &&
+        ssm::sweep_offsets_fit(d->dim, d->dstate, d->io_dtype == SSM_DTYPE_F32 ? 4 : 2))
+        return SSM_ALGO_SWEEP;
     return ssm::chunked_preferred(d->batch, d->seqlen, d->dim) ? SSM_ALGO_CHUNKED : SSM_ALGO_SEQUENTIAL;
+}
+
+// Shapes the lane sweep cannot take (explicit SSM_ALGO_SWEEP).
+bool sweep_unsupported(const ssm_scan_desc_t* d) {
+    return d->dstate > ssm::sweep::kLPC ||
+           !ssm::sweep_offsets_fit(d->dim, d->dstate, d->io_dtype == SSM_DTYPE_F32 ? 4 : 2) ||
+           (ssm::sweep_waves(d->batch, d->dim) + ssm::sweep::kWaves - 1) / ssm::sweep::kWaves > INT32_MAX;
+}
+
+template <typename T, int DISC, bool CPLX>
+void launch_sweep_k(const ssm::SweepParams& p, bool pairs, dim3 grid, hipStream_t s) {
+    if (pairs)
+        hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, DISC, CPLX, true>), grid, dim3(ssm::sweep::kWaves * 64), 0, s,
+                           p);
+    else
+        hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, DISC, CPLX, false>), grid, dim3(ssm::sweep::kWaves * 64), 0, s,
+                           p);
+}
+
+// pairs: complex B and C aligned to whole (re, im) entries
+template <typename T>
+int launch_sweep(const ssm_scan_desc_t* d, const ssm::SweepParams& p, bool pairs, hipStream_t s) {
+    const int64_t blocks = (ssm::sweep_waves(d->batch, d->dim) + ssm::sweep::kWaves - 1) / ssm::sweep::kWaves;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (d->is_complex) {
+        if (d->disc == SSM_DISC_EXP_EULER)
+            launch_sweep_k<T, ssm::kEuler, true>(p, pairs, grid, s);
+        else
+            launch_sweep_k<T, ssm::kTrap, true>(p, pairs, grid, s);
+    } else {
+        if (d->disc == SSM_DISC_ZOH)
+            hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, ssm::kZOH, false, false>), grid,
+                               dim3(ssm::sweep::kWaves * 64), 0, s, p);
+        else if (d->disc == SSM_DISC_EXP_EULER)
+            hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, ssm::kEuler, false, false>), grid,
+                               dim3(ssm::sweep::kWaves * 64), 0, s, p);
+        else
+            hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, ssm::kTrap, false, false>), grid,
+                               dim3(ssm::sweep::kWaves * 64), 0, s, p);
+    }
+    return hip_status(hipGetLastError());
 }
 
 template <typename T>
@@ -392,6 +437,11 @@ const char* ssm_scan_status_string(int status) {
     }
 }
 
+int ssm_scan_algo(const ssm_scan_desc_t* desc) {
+    if (check_desc(desc) != SSM_OK) return -1;
+    return choose_algo(desc);
+}
+
 size_t ssm_scan_workspace_bytes(const ssm_scan_desc_t* desc) {
     if (check_desc(desc) != SSM_OK) return 0;
     if (choose_algo(desc) != SSM_ALGO_CHUNKED) return 0;
@@ -424,6 +474,7 @@ int ssm_scan_fwd_ex(const ssm_scan_desc_t* desc, const void* u, const void* delt
 
     const int algo = choose_algo(desc);
     if (algo == SSM_ALGO_CHUNKED && desc->dstate > ssm::kChunkLanes) return SSM_ERR_UNSUPPORTED;
+    if (algo == SSM_ALGO_SWEEP && sweep_unsupported(desc)) return SSM_ERR_UNSUPPORTED;
     const size_t need = algo == SSM_ALGO_CHUNKED
                             ? ssm::chunked_workspace_bytes(desc->batch, desc->seqlen, desc->dim)
                             : 0;
@@ -449,6 +500,17 @@ int ssm_scan_fwd_ex(const ssm_scan_desc_t* desc, const void* u, const void* delt
         return st < 0 ? hip_status(static_cast<hipError_t>(-st)) : st;
     }
 
+    if (algo == SSM_ALGO_SWEEP) {
+        ssm::SweepParams p{};
+        p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.theta = theta;
+        p.lambda = lambda; p.y = y; p.h_last = h_last;
+        p.h0 = h0; p.q0 = q0; p.q_last = q_last;
+        p.batch = desc->batch; p.seqlen = desc->seqlen; p.dim = desc->dim; p.dstate = desc->dstate;
+        const bool pairs = desc->is_complex && aligned(B, 2 * es) && aligned(C, 2 * es);
+        return desc->io_dtype == SSM_DTYPE_F32 ? launch_sweep<float>(desc, p, pairs, s)
+                                               : launch_sweep<uint16_t>(desc, p, pairs, s);
+    }
+
     ssm::SeqParams p{};
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = D; p.theta = theta;
     p.lambda = lambda; p.y = y; p.h_last = h_last;
@@ -471,6 +533,7 @@ int ssm_scan_fwd_noalloc(const ssm_scan_desc_t* desc, const void* u, const void*
     if (h_last && !aligned(h_last, desc->is_complex ? 8 : 4)) return SSM_ERR_INVALID_ARGUMENT;
     const int algo = choose_algo(desc);
     if (algo == SSM_ALGO_CHUNKED && desc->dstate > ssm::kChunkLanes) return SSM_ERR_UNSUPPORTED;
+    if (algo == SSM_ALGO_SWEEP && sweep_unsupported(desc)) return SSM_ERR_UNSUPPORTED;
     const size_t need =
         algo == SSM_ALGO_CHUNKED ? ssm::chunked_workspace_bytes(desc->batch, desc->seqlen, desc->dim) : 0;
     if (need > SSM_SCAN_NOALLOC_SCRATCH_BYTES) return SSM_ERR_SCRATCH_LIMIT;

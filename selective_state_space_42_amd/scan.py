@@ -19,8 +19,8 @@ LIB_PATH = os.environ.get("SSM_SCAN_LIB") or os.path.join(_PKG, "libssmscan.so")
 
 SSM_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 SSM_DISC = {"zoh": 0, "euler": 1, "trap": 2}
-SSM_ALGO = {"auto": 0, "sequential": 1, "chunked": 2}
-ABI_VERSION = 4
+SSM_ALGO = {"auto": 0, "sequential": 1, "chunked": 2, "sweep": 3}
+ABI_VERSION = 5
 
 
 class ScanDesc(ctypes.Structure):
@@ -94,6 +94,8 @@ def _lib():
     lib.ssm_mimo_step.restype = ctypes.c_int
     lib.ssm_mimo_workspace_bytes.argtypes = [ctypes.POINTER(MimoDesc)]
     lib.ssm_mimo_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssm_scan_algo.argtypes = [ctypes.POINTER(ScanDesc)]
+    lib.ssm_scan_algo.restype = ctypes.c_int
     lib.ssm_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
     lib.ssm_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_scan_status_string.argtypes = [ctypes.c_int]
@@ -119,6 +121,14 @@ def ssm_scan_abi_version() -> int:
 
 def ssm_scan_status_string(status: int) -> str:
     return _lib().ssm_scan_status_string(int(status)).decode()
+
+
+def ssm_scan_algo(desc: ScanDesc) -> str:
+    """Name of the kernel family ssm_scan_fwd runs for `desc` (AUTO resolved)."""
+    v = int(_lib().ssm_scan_algo(ctypes.byref(desc)))
+    if v < 0:
+        raise ScanError(1, "ssm_scan_algo")
+    return {a: k for k, a in SSM_ALGO.items()}[v]
 
 
 def ssm_scan_workspace_bytes(desc: ScanDesc) -> int:

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     header_version = int(re.search(r"#define SSM_SCAN_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert scan.ssm_scan_abi_version() == header_version == scan.ABI_VERSION == 4
+    assert scan.ssm_scan_abi_version() == header_version == scan.ABI_VERSION == 5
     for code, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported configuration"),
                        (3, "workspace too small"), (4, "HIP runtime error"), (99, "unknown status")]:
         assert scan.ssm_scan_status_string(code) == text
@@ -85,6 +85,23 @@ def test_unsupported_modes():
     d = desc()
     d.is_complex = 2
     assert call(d) == UNSUPPORTED
+
+
+def test_sweep_rules():
+    # the lane sweep takes N <= 16, needs no workspace, and AUTO picks it only
+    # once there are at least 2048 waves of 4 channels (two per SIMD)
+    assert call(desc(N=17, algo="sweep")) == UNSUPPORTED
+    assert scan.ssm_scan_workspace_bytes(desc(algo="sweep")) == 0
+    wide = desc(B=8, L=2048, D=1536, N=16, dtype="f32", disc="zoh", algo="auto")
+    assert scan.ssm_scan_workspace_bytes(wide) == 0                       # 3072 waves: the sweep
+    assert scan.ssm_scan_algo(wide) == "sweep"
+    assert scan.ssm_scan_algo(desc(N=17)) == "sequential"
+    assert scan.ssm_scan_algo(desc(algo="chunked")) == "chunked"
+    narrow = desc(B=1, L=2048, D=1536, N=16, dtype="f32", disc="zoh", algo="auto")
+    assert scan.ssm_scan_workspace_bytes(narrow) > 0                      # 384 waves: the chunked kernel
+    assert scan.ssm_scan_algo(narrow) == "chunked"
+    # 32-bit per-block offsets: 34 * D * N * esize must stay below 2^31
+    assert call(desc(B=1, L=4, D=1 << 20, N=16, dtype="f32", algo="sweep")) == UNSUPPORTED
 
 
 def test_required_pointers():

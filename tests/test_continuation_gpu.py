@@ -77,7 +77,7 @@ def _oracle(w, x, **kw):
                        disc=w.disc, is_complex=w.is_complex, return_q=True, **kw)
 
 
-@pytest.mark.parametrize("algo", ["sequential", "chunked"])
+@pytest.mark.parametrize("algo", ["sequential", "chunked", "sweep"])
 @pytest.mark.parametrize("mode", list(MODES))
 def test_two_calls_equal_one_shot(mode, algo):
     """L = 333 split at step 200 (inside a tile): y of both calls and the final h, q."""
@@ -99,7 +99,7 @@ def test_two_calls_equal_one_shot(mode, algo):
     assert err_y <= tol and err_h <= tol and err_q <= tol, (err_y, err_h, err_q, tol)
 
 
-@pytest.mark.parametrize("algo", ["sequential", "chunked"])
+@pytest.mark.parametrize("algo", ["sequential", "chunked", "sweep"])
 @pytest.mark.parametrize("mode", list(MODES))
 def test_nonzero_initial_state(mode, algo):
     """Random h0 (and q0) against the oracle continued from the same values."""

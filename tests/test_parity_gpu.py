@@ -35,15 +35,15 @@ MODES = {
     "complex_trap_bf16": CPLX_BF16,
     "complex_trap_f32": CPLX_BF16.scaled(io_dtype="f32"),
 }
-ALGOS = ["sequential", "chunked"]
+ALGOS = ["sequential", "chunked", "sweep"]
 
 
 def _run(w, algo, **kw):
     try:
         err_y, err_h, tol = check_workload(w, seed=123, algo=algo, **kw)
     except ScanError as e:
-        if e.status == 2 and algo == "chunked":
-            pytest.skip(f"chunked kernel does not support this case: {e}")
+        if e.status == 2 and algo in ("chunked", "sweep"):
+            pytest.skip(f"{algo} kernel does not support this case: {e}")
         raise
     print(f"{w.name} algo={algo} err_y={err_y:.3e} err_h={err_h:.3e} tol={tol:g}", flush=True)
     assert err_y <= tol and err_h <= tol, (err_y, err_h, tol)
@@ -142,7 +142,7 @@ def test_golden_fixtures(path, algo):
     try:
         y, h = run_gpu(inputs, disc, algo)
     except ScanError as e:
-        if e.status == 2 and algo == "chunked":
+        if e.status == 2 and algo in ("chunked", "sweep"):
             pytest.skip(str(e))
         raise
     ey = rel_err(y.float().cpu().double().numpy(), z["y"])
@@ -170,3 +170,19 @@ def test_full_size_workloads(name, k):
         _run(w, "auto", d_index=_sample(w.dim, k))
     finally:
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", ["complex_euler_f32", "complex_trap_bf16"])
+def test_sweep_unaligned_bc(mode):
+    """Complex B and C that start one element past a whole (re, im) entry: the
+    lane sweep then loads each part separately."""
+    w = MODES[mode].scaled(name=f"{mode}_unaligned", batch=2, dim=13, seqlen=200)
+    inp = make_inputs(w, 17, device="cuda")
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % (2 * t.element_size()) != 0
+        return v
+    _run(w, "sweep", inputs=dict(inp, Bm=shifted(inp["Bm"]), Cm=shifted(inp["Cm"])))
