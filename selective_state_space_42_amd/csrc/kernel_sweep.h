@@ -103,11 +103,31 @@ inline bool sweep_offsets_fit(int64_t D, int64_t N, int64_t es) {
 
 // LDS of one wave.
 struct SweepLds {
-    float4 bc[sweep::kS][sweep::kLPC];  // (B re, B im, C re, C im) per (step, state); real: (B, 0, C, 0)
+    float4 bc[sweep::kS][sweep::kLPC];  // (B re, B im, C re, C im) per (step, state); real: (B, C) pairs
     float2 dw[sweep::kS][sweep::kCPW];  // (delta, w) per (step, channel)
     float k[sweep::kS];                 // K_t (trapezoid)
     float red[64 * sweep::kRedStride];  // the lanes' partial outputs, one padded row per lane
 };
+
+// B/C entry of (step, state) in the LDS: 16 bytes for a complex state, the
+// first half of the array as (B, C) pairs for a real one (an 8-byte read per
+// step instead of 16).
+template <bool CPLX>
+__device__ __forceinline__ void st_bc(SweepLds& s, int st, int n, const float (&v)[4]) {
+    if constexpr (CPLX)
+        s.bc[st][n] = make_float4(v[0], v[1], v[2], v[3]);
+    else
+        reinterpret_cast<float2*>(&s.bc[0][0])[st * sweep::kLPC + n] = make_float2(v[0], v[2]);
+}
+template <bool CPLX>
+__device__ __forceinline__ float4 ld_bc(const SweepLds& s, int st, int n) {
+    if constexpr (CPLX) {
+        return s.bc[st][n];
+    } else {
+        const float2 v = reinterpret_cast<const float2*>(&s.bc[0][0])[st * sweep::kLPC + n];
+        return make_float4(v.x, 0.f, v.y, 0.f);
+    }
+}
 
 // One block's loads, as they arrive: per-(step, channel) rows for the lane's
 // step, B/C entries for its kBcSteps steps.
@@ -257,7 +277,7 @@ __device__ __forceinline__ float sweep_commit(SweepLds& s, const SweepLane& g, c
     const float x = BE::widen(r.x), dt = BE::widen(r.dt);
 #pragma unroll
     for (int j = 0; j < kBcSteps; ++j)
-        s.bc[g.c + kCPW * j][g.n] = make_float4(r.bc[j][0], r.bc[j][1], r.bc[j][2], r.bc[j][3]);
+        st_bc<CPLX>(s, g.c + kCPW * j, g.n, r.bc[j]);
     float w, ey;
     if constexpr (DISC == kZOH) {
         w = x;
@@ -293,14 +313,14 @@ __device__ __forceinline__ void sweep_steps(SweepLds& s, const SweepLane& g, Swe
     using namespace sweep;
     float* red = s.red + (g.c * kLPC + g.n) * kRedStride;
     float2 nx_dw = s.dw[0][g.c];
-    float4 nx_bc = s.bc[0][g.n];
+    float4 nx_bc = ld_bc<CPLX>(s, 0, g.n);
 #pragma unroll
     for (int st = 0; st < kS; ++st) {
         const float2 dw = nx_dw;  // (delta, w)
         const float4 bc = nx_bc;
         if (st + 1 < kS) {
             nx_dw = s.dw[st + 1][g.c];
-            nx_bc = s.bc[st + 1][g.n];
+            nx_bc = ld_bc<CPLX>(s, st + 1, g.n);
         }
         float py;
         if constexpr (CPLX) {
@@ -329,7 +349,9 @@ __device__ __forceinline__ void sweep_steps(SweepLds& s, const SweepLane& g, Swe
             py = bc.z * gr;
         }
         red[st] = py;
-        __builtin_amdgcn_sched_barrier(0);
+        // complex: keep the steps in order (the loads one step ahead stay
+        // ahead); real: let the compiler interleave steps (measured faster)
+        if constexpr (CPLX) __builtin_amdgcn_sched_barrier(0);
     }
 }
 
