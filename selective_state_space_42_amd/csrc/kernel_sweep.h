@@ -398,6 +398,18 @@ __device__ __forceinline__ void sweep_block(const SweepParams& p, SweepLds& s, c
     BE::store(ry, g.cok ? static_cast<uint32_t>(g.n * D + g.c) * es : kOutOfRange, acc);
 }
 
+// Workgroup i of a launch runs on XCD i mod 8.  Numbering the channel groups
+// XCD by XCD (XCD x takes a contiguous run of them) puts neighbouring
+// channels, which share the cache lines of the per-step rows u, delta and y,
+// behind one L2.  A bijection of 0 .. nb-1 for any nb.
+__device__ __forceinline__ uint32_t sweep_xcd_block(uint32_t bid, uint32_t nb) {
+    constexpr uint32_t kXcds = 8;
+    const uint32_t per = (nb + kXcds - 1) / kXcds, rem = nb % kXcds;
+    const uint32_t x = bid % kXcds, y = bid / kXcds;
+    const uint32_t before = rem == 0 || x <= rem ? x * per : rem * per + (x - rem) * (per - 1);
+    return before + y;
+}
+
 template <typename T, int DISC, bool CPLX, bool PAIRS>
 __global__ void __launch_bounds__(sweep::kWaves * 64, 4) sweep_scan_kernel(SweepParams p) {
     using namespace sweep;
@@ -414,7 +426,7 @@ __global__ void __launch_bounds__(sweep::kWaves * 64, 4) sweep_scan_kernel(Sweep
     // (every load out of range, every store dropped), so that each wave of a
     // workgroup meets the same barriers.
     const int64_t waves = p.batch * n_dblk;
-    const int64_t wv = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+    const int64_t wv = static_cast<int64_t>(sweep_xcd_block(blockIdx.x, gridDim.x)) * kWaves + wave;
     const bool live = wv < waves;
     SweepLds& s = s_all[wave];
 
