@@ -186,6 +186,19 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// A buffer resource whose base and size the caller knows to be the same in
+// every lane, declared so: read from the first lane into scalar registers.
+// Without it a base picked from a small array by a (uniform) index stays in
+// vector registers, and every access through the resource becomes a loop
+// over the distinct values (v_readfirstlane, compare, masked access).
+__device__ __forceinline__ rsrc_t make_uniform_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    const void* ub = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+    return make_rsrc(ub, __builtin_amdgcn_readfirstlane(bytes));
+}
+
 // byte offset of (section, lane, state j) in a tile's payload
 __device__ __forceinline__ uint32_t pay_off(int section, int lane, int j) {
     return static_cast<uint32_t>(((section * 64 + lane) * chunk::kNPL + j) * 8);
@@ -476,7 +489,7 @@ __device__ __forceinline__ void issue_dma(const ChunkParams& p, const ChunkLayou
                 const int ar = g / RR::kInstr, iq = g % RR::kInstr;
                 const int f = iq * 64 + lane;  // chunk of the array
                 const int rw = f / kRowChunks, part = f % kRowChunks;
-                const rsrc_t rs = make_rsrc(arrs[ar] + base, bytes);
+                const rsrc_t rs = make_uniform_rsrc(arrs[ar] + base, bytes);
                 if (f < RR::kChunks)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
                         rs, (__attribute__((address_space(3))) void*)(s_raw + ar * RR::kArrayDw + iq * 256), 16,
