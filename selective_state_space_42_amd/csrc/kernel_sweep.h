@@ -67,6 +67,7 @@ constexpr int kBcSteps = kS / kCPW;   // B/C steps loaded per lane and block
 // the chunked kernel at 2.5 and 5 waves per SIMD and is left to it.
 constexpr int64_t kMinWavesReal = 2048;
 constexpr int64_t kMinWavesComplex = 3072;
+constexpr int64_t kMaxStepsShort = 96;  // any shape: the sweep up to this many steps
 }  // namespace sweep
 
 struct SweepParams {
@@ -89,8 +90,12 @@ struct SweepParams {
 // Waves of a launch (one per 4 channels of a batch row).
 inline int64_t sweep_waves(int64_t B, int64_t D) { return B * ((D + sweep::kCPW - 1) / sweep::kCPW); }
 
-// Whether the automatic choice takes the sweep for this shape and mode.
-inline bool sweep_preferred(int64_t B, int64_t D, bool is_complex, bool trap) {
+// Whether the automatic choice takes the sweep for this shape and mode.  A
+// sequence no longer than one chunked tile (96 steps) gains nothing from the
+// chunked kernel's split of time and pays its extra launch; from 256 steps on
+// a sweep of few waves is latency-bound (measured).
+inline bool sweep_preferred(int64_t B, int64_t L, int64_t D, bool is_complex, bool trap) {
+    if (L <= sweep::kMaxStepsShort) return true;
     if (!is_complex) return sweep_waves(B, D) >= sweep::kMinWavesReal;
     return !trap && sweep_waves(B, D) >= sweep::kMinWavesComplex;
 }

@@ -100,7 +100,7 @@ int check_desc(const ssm_scan_desc_t* d) {
 int choose_algo(const ssm_scan_desc_t* d) {
     if (d->algo != SSM_ALGO_AUTO) return d->algo;
     if (d->dstate > ssm::kChunkLanes) return SSM_ALGO_SEQUENTIAL;
-    if (ssm::sweep_preferred(d->batch, d->dim, d->is_complex != 0, d->disc == SSM_DISC_EXP_TRAPEZOIDAL) &&
+    if (ssm::sweep_preferred(d->batch, d->seqlen, d->dim, d->is_complex != 0, d->disc == SSM_DISC_EXP_TRAPEZOIDAL) &&
         ssm::sweep_offsets_fit(d->dim, d->dstate, d->io_dtype == SSM_DTYPE_F32 ? 4 : 2))
         return SSM_ALGO_SWEEP;
     return ssm::chunked_preferred(d->batch, d->seqlen, d->dim) ? SSM_ALGO_CHUNKED : SSM_ALGO_SEQUENTIAL;

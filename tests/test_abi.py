@@ -100,6 +100,9 @@ def test_sweep_rules():
     narrow = desc(B=1, L=2048, D=1536, N=16, dtype="f32", disc="zoh", algo="auto")
     assert scan.ssm_scan_workspace_bytes(narrow) > 0                      # 384 waves: the chunked kernel
     assert scan.ssm_scan_algo(narrow) == "chunked"
+    # a sequence of at most one chunked tile (96 steps) always takes the sweep
+    assert scan.ssm_scan_algo(desc(B=1, L=96, D=4, N=4, algo="auto")) == "sweep"
+    assert scan.ssm_scan_algo(desc(B=1, L=97, D=4, N=4, algo="auto")) == "chunked"
     # 32-bit per-block offsets: 34 * D * N * esize must stay below 2^31
     assert call(desc(B=1, L=4, D=1 << 20, N=16, dtype="f32", algo="sweep")) == UNSUPPORTED
 
