@@ -20,8 +20,9 @@
 //           of the block for channel c.
 // Staging of a block (every load issued one block ahead, through buffer
 // resources that return 0 outside the data, so ragged blocks need no branch):
-//   - lane (c, n) loads u, delta (the trapezoid also lambda and the next
-//     step's delta and lambda) at step n of the block for channel c, forms
+//   - lane (c, n) loads u, delta (the trapezoid also lambda) at step n of the
+//     block for channel c (the trapezoid's next-step delta and lambda come
+//     from the neighbouring lane, the block's last lane loads them), forms
 //     that (step, channel)'s terms (delta, w) once for the whole wave, and
 //     keeps the output's skip term for the step it finishes;
 //   - lane (c, n) loads B_t[n] and C_t[n] for steps c, c+4, c+8, c+12 (the
@@ -186,7 +187,9 @@ __device__ __forceinline__ void sweep_issue(const SweepParams& p, const SweepLan
         const uint32_t bytes = rows ? static_cast<uint32_t>((rows - 1) * D + g.nch) * es : 0u;
         const int64_t base = rows ? (g.b * L + t0) * D + g.d0 : 0;
         const uint32_t off = g.cok ? static_cast<uint32_t>(g.n * D + g.c) * es : kOutOfRange;
-        const uint32_t offn = g.cok ? static_cast<uint32_t>((g.n + 1) * D + g.c) * es : kOutOfRange;
+        // the step after the block, read by the channel's last lane only (the
+        // other lanes take the next step's values from their neighbour)
+        const uint32_t offn = g.cok && g.n == kLPC - 1 ? static_cast<uint32_t>(kS * D + g.c) * es : kOutOfRange;
         const rsrc_t ru = make_rsrc(static_cast<const T*>(p.u) + base, bytes);
         const rsrc_t rd = make_rsrc(static_cast<const T*>(p.delta) + base, bytes);
         r.x = BE::load_raw(ru, off);
@@ -291,7 +294,14 @@ __device__ __forceinline__ float sweep_commit(SweepLds& s, const SweepLane& g, c
         w = dt * x;
         ey = dsk * x;
     } else {
-        const float lam = BE::widen(r.lam), dtn = BE::widen(r.dtn), lamn = BE::widen(r.lamn);
+        // delta and lambda of the next step: the neighbouring lane's (step n+1
+        // of the block), or for the last lane the row after the block.  Each
+        // row a wave reads is a separate cache line, so these shuffles save
+        // two 16-row loads per block.
+        const float lam = BE::widen(r.lam);
+        const float dtn_nb = __shfl_down(dt, 1, kLPC), lamn_nb = __shfl_down(lam, 1, kLPC);
+        const bool last = g.n == kLPC - 1;
+        const float dtn = last ? BE::widen(r.dtn) : dtn_nb, lamn = last ? BE::widen(r.lamn) : lamn_nb;
         const float bnext = (1.f - lamn) * dtn;  // beta'_{t+1} (zero past the end)
         w = (lam * dt + bnext) * x;
         float kt[kBcSteps];
