@@ -72,9 +72,9 @@ typedef enum {
  * 16 steps at a time staged through LDS (N <= 16; needs no workspace; fills
  * the GPU once B * ceil(D/4) reaches a few waves per SIMD; UNSUPPORTED when
  * 34*D*N*esize reaches 2^31).  AUTO uses SWEEP when N <= 16 and either
- * L <= 96 or B * ceil(D/4) >= 2048 for a real state or >= 3072 for a complex
- * exp-Euler one (two and three waves per SIMD of a 256-CU GPU, where it
- * measured faster; not for a longer complex trapezoid), else CHUNKED when
+ * L <= 96 or B * ceil(D/4) reaches 1536 for a real state, 2048 for a complex
+ * exp-Euler one or 3072 for the complex trapezoid (1.5, 2 and 3 waves per
+ * SIMD of a 256-CU GPU, where it measured faster), else CHUNKED when
  * N <= 16, else SEQUENTIAL.  All give the same result up to rounding. */
 typedef enum {
     SSM_ALGO_AUTO = 0,

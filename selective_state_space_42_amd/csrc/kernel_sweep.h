@@ -16,15 +16,15 @@
 //           own LDS region.
 //   block = 16 steps.  The wave stages the block's per-step terms in LDS,
 //           sweeps the 16 steps, then sums the 16 lanes' partial outputs
-//           through an LDS transpose so that lane (c, n) finishes y at step n
-//           of the block for channel c.
+//           through an LDS transpose so that lane 4 rn + rc finishes y at
+//           step rn of the block for channel rc.
 // Staging of a block (every load issued one block ahead, through buffer
 // resources that return 0 outside the data, so ragged blocks need no branch):
-//   - lane (c, n) loads u, delta (the trapezoid also lambda) at step n of the
-//     block for channel c (the trapezoid's next-step delta and lambda come
-//     from the neighbouring lane, the block's last lane loads them), forms
-//     that (step, channel)'s terms (delta, w) once for the whole wave, and
-//     keeps the output's skip term for the step it finishes;
+//   - lane 4 rn + rc loads u, delta (the trapezoid also lambda) at step rn of
+//     the block for channel rc (the trapezoid's next-step delta and lambda
+//     come from the lane 4 further on; the block's last step loads them),
+//     forms that (step, channel)'s terms (delta, w) once for the whole wave,
+//     and keeps the output's skip term for the step it finishes;
 //   - lane (c, n) loads B_t[n] and C_t[n] for steps c, c+4, c+8, c+12 (the
 //     wave's four channels share them) and, for the trapezoid, the row sums
 //     K_t = Re(sum_n C_t[n] B_t[n]) are formed from those with 16-lane sums;
@@ -62,12 +62,14 @@ constexpr int kWaves = 4;             // waves per workgroup (independent)
 constexpr int kRedStride = kS + 1;    // padded row of the output transpose
 constexpr int kBcSteps = kS / kCPW;   // B/C steps loaded per lane and block
 // Waves of work from which the sweep beats the chunked kernel, measured on
-// MI355X (1024 SIMDs): two waves per SIMD for a real state, three for a
-// complex exp-Euler one (its per-step theta reads are small pieces whose
-// latency the extra waves hide).  The complex trapezoid measured slower than
-// the chunked kernel at 2.5 and 5 waves per SIMD and is left to it.
-constexpr int64_t kMinWavesReal = 2048;
-constexpr int64_t kMinWavesComplex = 3072;
+// MI355X (1024 SIMDs): 1.5 waves per SIMD for a real state (1536 waves: 0.22
+// against 0.25 ms; 768: 0.19 against 0.15), two for a complex exp-Euler one
+// (2048 waves: 0.74 against 0.89 ms), three for the complex trapezoid (its
+// 2560-wave case, 2.5 per SIMD, leaves half the CUs a third workgroup and
+// measured 1.60 against 1.50 ms; 3840 waves 2.02 against 2.20).
+constexpr int64_t kMinWavesReal = 1536;
+constexpr int64_t kMinWavesComplex = 2048;
+constexpr int64_t kMinWavesComplexTrap = 3072;
 constexpr int64_t kMaxStepsShort = 96;  // any shape: the sweep up to this many steps
 }  // namespace sweep
 
@@ -98,7 +100,7 @@ inline int64_t sweep_waves(int64_t B, int64_t D) { return B * ((D + sweep::kCPW 
 inline bool sweep_preferred(int64_t B, int64_t L, int64_t D, bool is_complex, bool trap) {
     if (L <= sweep::kMaxStepsShort) return true;
     if (!is_complex) return sweep_waves(B, D) >= sweep::kMinWavesReal;
-    return !trap && sweep_waves(B, D) >= sweep::kMinWavesComplex;
+    return sweep_waves(B, D) >= (trap ? sweep::kMinWavesComplexTrap : sweep::kMinWavesComplex);
 }
 
 // The per-block byte offsets a lane forms are 32-bit: 17 rows of D elements
@@ -163,11 +165,16 @@ struct SweepTheta<float> {
     }
 };
 
-// Per-lane geometry of a wave (uniform parts in scalar registers).
+// Per-lane geometry of a wave (uniform parts in scalar registers).  A lane
+// holds the state of (channel c, state n), and reads and writes the
+// per-(step, channel) rows (u, delta, lambda, y) for (step rn, channel rc):
+// channel-fastest, so that each quarter of the wave touches 4 channels of one
+// step, one cache line, instead of one channel of 16 steps (measured 4% faster
+// for a real state, 15% for the trapezoid).
 struct SweepLane {
     int64_t b, d0;
-    int nch, c, n;
-    bool cok, sok;
+    int nch, c, n, rn, rc;
+    bool cok, sok, rok;
 };
 
 // Issue the per-(step, channel) and B/C loads of the block starting at step
@@ -186,10 +193,10 @@ __device__ __forceinline__ void sweep_issue(const SweepParams& p, const SweepLan
         const int64_t rows = left > kS + 1 ? kS + 1 : left;
         const uint32_t bytes = rows ? static_cast<uint32_t>((rows - 1) * D + g.nch) * es : 0u;
         const int64_t base = rows ? (g.b * L + t0) * D + g.d0 : 0;
-        const uint32_t off = g.cok ? static_cast<uint32_t>(g.n * D + g.c) * es : kOutOfRange;
-        // the step after the block, read by the channel's last lane only (the
-        // other lanes take the next step's values from their neighbour)
-        const uint32_t offn = g.cok && g.n == kLPC - 1 ? static_cast<uint32_t>(kS * D + g.c) * es : kOutOfRange;
+        const uint32_t off = g.rok ? static_cast<uint32_t>(g.rn * D + g.rc) * es : kOutOfRange;
+        // the step after the block, read by the lanes of the block's last step
+        // only (the others take the next step's values from a neighbour)
+        const uint32_t offn = g.rok && g.rn == kS - 1 ? static_cast<uint32_t>(kS * D + g.rc) * es : kOutOfRange;
         const rsrc_t ru = make_rsrc(static_cast<const T*>(p.u) + base, bytes);
         const rsrc_t rd = make_rsrc(static_cast<const T*>(p.delta) + base, bytes);
         r.x = BE::load_raw(ru, off);
@@ -276,8 +283,9 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-// Turn a block's loads into the wave's LDS terms; returns the skip term of
-// the (step, channel) this lane finishes.
+// Turn a block's loads into the wave's LDS terms (delta, w) per (step,
+// channel); returns the skip term of y at the lane's (step rn, channel rc)
+// (dsk: the skip weight of channel rc).
 template <typename T, int DISC, bool CPLX>
 __device__ __forceinline__ float sweep_commit(SweepLds& s, const SweepLane& g, const SweepRows<T>& r, float dsk) {
     using namespace sweep;
@@ -294,13 +302,13 @@ __device__ __forceinline__ float sweep_commit(SweepLds& s, const SweepLane& g, c
         w = dt * x;
         ey = dsk * x;
     } else {
-        // delta and lambda of the next step: the neighbouring lane's (step n+1
-        // of the block), or for the last lane the row after the block.  Each
-        // row a wave reads is a separate cache line, so these shuffles save
-        // two 16-row loads per block.
+        // delta and lambda of the next step: those of the lane kCPW further on
+        // (step rn+1 of the block, same channel), or for the block's last
+        // step the row after the block, which saves two more row loads per
+        // block.
         const float lam = BE::widen(r.lam);
-        const float dtn_nb = __shfl_down(dt, 1, kLPC), lamn_nb = __shfl_down(lam, 1, kLPC);
-        const bool last = g.n == kLPC - 1;
+        const float dtn_nb = __shfl_down(dt, kCPW), lamn_nb = __shfl_down(lam, kCPW);
+        const bool last = g.rn == kS - 1;
         const float dtn = last ? BE::widen(r.dtn) : dtn_nb, lamn = last ? BE::widen(r.lamn) : lamn_nb;
         const float bnext = (1.f - lamn) * dtn;  // beta'_{t+1} (zero past the end)
         w = (lam * dt + bnext) * x;
@@ -311,9 +319,9 @@ __device__ __forceinline__ float sweep_commit(SweepLds& s, const SweepLane& g, c
 #pragma unroll
             for (int j = 0; j < kBcSteps; ++j) s.k[g.c + kCPW * j] = kt[j];  // K_t = Re(sum_n C_t B_t)
         }
-        ey = (dsk - bnext * s.k[g.n]) * x;
+        ey = (dsk - bnext * s.k[g.rn]) * x;
     }
-    s.dw[g.n][g.c] = make_float2(dt, w);
+    s.dw[g.rn][g.rc] = make_float2(dt, w);
     return ey;
 }
 
@@ -375,7 +383,7 @@ __device__ __forceinline__ void sweep_steps(SweepLds& s, const SweepLane& g, Swe
 template <typename T, int DISC, bool CPLX, bool PAIRS>
 __device__ __forceinline__ void sweep_block(const SweepParams& p, SweepLds& s, const SweepLane& g, int64_t t0,
                                             SweepRows<T>& r, SweepTheta<T>& th, float a, float a2, float inv_a,
-                                            float dsk, float& gr, float& gi) {
+                                            float dsr, float& gr, float& gi) {
     using namespace sweep;
     using BE = Buf<T>;
     constexpr uint32_t es = BE::kSize;
@@ -385,7 +393,7 @@ __device__ __forceinline__ void sweep_block(const SweepParams& p, SweepLds& s, c
         // row) reach memory together.  Nothing is exchanged: no memory wait.
         __builtin_amdgcn_s_barrier();
     }
-    const float ey = sweep_commit<T, DISC, CPLX>(s, g, r, dsk);
+    const float ey = sweep_commit<T, DISC, CPLX>(s, g, r, dsr);
     sweep_issue<T, DISC, CPLX, PAIRS>(p, g, t0 + kS, r);
     const SweepThetaSrc nq = sweep_theta_src<T>(p, g, t0 + kS);
 
@@ -400,17 +408,18 @@ __device__ __forceinline__ void sweep_block(const SweepParams& p, SweepLds& s, c
         sweep_steps<T, DISC, CPLX, kSinCosHw>(s, g, th, nq, a, a2, inv_a, gr, gi);
     }
 
-    // sum over the channel's 16 lanes: lane (c, n) takes step n
+    // sum over the channel's 16 state lanes: lane (rn, rc) takes step rn of
+    // channel rc
     float acc = ey;
 #pragma unroll
-    for (int m = 0; m < kLPC; ++m) acc += s.red[(g.c * kLPC + m) * kRedStride + g.n];
+    for (int m = 0; m < kLPC; ++m) acc += s.red[(g.rc * kLPC + m) * kRedStride + g.rn];
 
     const int64_t L = p.seqlen, D = p.dim;
     const int64_t left = L - t0;
     const int64_t steps = left > kS ? kS : left;
     const uint32_t bytes = static_cast<uint32_t>((steps - 1) * D + g.nch) * es;
     const rsrc_t ry = make_rsrc(static_cast<T*>(p.y) + (g.b * L + t0) * D + g.d0, bytes);
-    BE::store(ry, g.cok ? static_cast<uint32_t>(g.n * D + g.c) * es : kOutOfRange, acc);
+    BE::store(ry, g.rok ? static_cast<uint32_t>(g.rn * D + g.rc) * es : kOutOfRange, acc);
 }
 
 // Workgroup i of a launch runs on XCD i mod 8.  Numbering the channel groups
@@ -451,14 +460,17 @@ __global__ void __launch_bounds__(sweep::kWaves * 64, 4) sweep_scan_kernel(Sweep
     g.nch = live ? static_cast<int>(D - g.d0 < kCPW ? D - g.d0 : kCPW) : 0;
     g.c = lane / kLPC;
     g.n = lane % kLPC;
+    g.rn = lane / kCPW;
+    g.rc = lane % kCPW;
     g.cok = g.c < g.nch;
     g.sok = g.cok && g.n < N;
+    g.rok = g.rc < g.nch;
     const int64_t d = g.d0 + g.c;
 
     const float a = g.sok ? p.A[d * N + g.n] : 0.f;
     const float a2 = prep_A(a);
     const float inv_a = a != 0.f ? 1.f / a : 0.f;
-    const float dsk = g.cok && p.Dskip ? p.Dskip[d] : 0.f;
+    const float dsr = g.rok && p.Dskip ? p.Dskip[g.d0 + g.rc] : 0.f;
 
     // initial state (the trapezoid carries g_{-1} = h_{-1} + beta'_0 q_{-1})
     const int64_t sidx = (g.b * D + d) * N + g.n;  // (b, d, n) in the layout of h_last
@@ -486,7 +498,7 @@ __global__ void __launch_bounds__(sweep::kWaves * 64, 4) sweep_scan_kernel(Sweep
         for (int st = 0; st < kS; ++st) sweep_theta_load<T>(q, st, th);
     }
     for (int64_t t0 = 0; t0 < L; t0 += kS)
-        sweep_block<T, DISC, CPLX, PAIRS>(p, s, g, t0, r, th, a, a2, inv_a, dsk, gr, gi);
+        sweep_block<T, DISC, CPLX, PAIRS>(p, s, g, t0, r, th, a, a2, inv_a, dsr, gr, gi);
 
     // the trapezoid's g_{L-1} is h_{L-1} (beta'_L = 0)
     if (g.sok && p.h_last) {

@@ -89,7 +89,8 @@ def test_unsupported_modes():
 
 def test_sweep_rules():
     # the lane sweep takes N <= 16, needs no workspace, and AUTO picks it only
-    # once there are at least 2048 waves of 4 channels (two per SIMD)
+    # once there are enough waves of 4 channels: 1536 for a real state, 2048
+    # for complex exp-Euler, 3072 for the complex trapezoid
     assert call(desc(N=17, algo="sweep")) == UNSUPPORTED
     assert scan.ssm_scan_workspace_bytes(desc(algo="sweep")) == 0
     wide = desc(B=8, L=2048, D=1536, N=16, dtype="f32", disc="zoh", algo="auto")
@@ -100,6 +101,13 @@ def test_sweep_rules():
     narrow = desc(B=1, L=2048, D=1536, N=16, dtype="f32", disc="zoh", algo="auto")
     assert scan.ssm_scan_workspace_bytes(narrow) > 0                      # 384 waves: the chunked kernel
     assert scan.ssm_scan_algo(narrow) == "chunked"
+    assert scan.ssm_scan_algo(desc(B=1, L=2048, D=6144, N=16, dtype="f32", disc="zoh", algo="auto")) == "sweep"
+    assert scan.ssm_scan_algo(desc(B=1, L=2048, D=6140, N=16, dtype="f32", disc="zoh", algo="auto")) == "chunked"
+    cplx = dict(L=4096, N=16, dtype="f32", cplx=True, algo="auto")
+    assert scan.ssm_scan_algo(desc(B=4, D=2048, disc="euler", **cplx)) == "sweep"        # 2048 waves
+    assert scan.ssm_scan_algo(desc(B=3, D=2048, disc="euler", **cplx)) == "chunked"      # 1536 waves
+    assert scan.ssm_scan_algo(desc(B=4, D=2560, disc="trap", **cplx)) == "chunked"       # 2560 waves
+    assert scan.ssm_scan_algo(desc(B=6, D=2048, disc="trap", **cplx)) == "sweep"         # 3072 waves
     # a sequence of at most one chunked tile (96 steps) always takes the sweep
     assert scan.ssm_scan_algo(desc(B=1, L=96, D=4, N=4, algo="auto")) == "sweep"
     assert scan.ssm_scan_algo(desc(B=1, L=97, D=4, N=4, algo="auto")) == "chunked"
