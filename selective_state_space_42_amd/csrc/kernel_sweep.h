@@ -12,8 +12,10 @@
 //   lane  = (channel c, state n): 16 lanes per channel, c = lane / 16; lanes
 //           with n >= N carry a zero state.
 //   wave  = 4 consecutive channels of one batch row, every step.  Waves are
-//           independent; a workgroup only packs four of them, each with its
-//           own LDS region.
+//           independent; a workgroup packs 4, 8 or 16 of them, each with its
+//           own LDS region (a complex state's waves meet at one barrier per
+//           block, so that their per-step theta pieces, adjacent in memory,
+//           are read together).
 //   block = 16 steps.  The wave stages the block's per-step terms in LDS,
 //           sweeps the 16 steps, then sums the 16 lanes' partial outputs
 //           through an LDS transpose so that lane 4 rn + rc finishes y at
@@ -58,7 +60,8 @@ namespace sweep {
 constexpr int kLPC = 16;              // lanes per channel: states n = 0 .. 15
 constexpr int kCPW = 64 / kLPC;       // channels per wave
 constexpr int kS = kLPC;              // steps per block (lane n finishes step n)
-constexpr int kWaves = 4;             // waves per workgroup (independent)
+constexpr int kWaves = 4;             // waves per workgroup (a complex state: up to kWavesWide)
+constexpr int kWavesWide = 16;        // a complex state's widest workgroup (one per CU)
 constexpr int kRedStride = kS + 1;    // padded row of the output transpose
 constexpr int kBcSteps = kS / kCPW;   // B/C steps loaded per lane and block
 // Waves of work from which the sweep beats the chunked kernel, measured on
@@ -101,6 +104,21 @@ inline bool sweep_preferred(int64_t B, int64_t L, int64_t D, bool is_complex, bo
     if (L <= sweep::kMaxStepsShort) return true;
     if (!is_complex) return sweep_waves(B, D) >= sweep::kMinWavesReal;
     return sweep_waves(B, D) >= (trap ? sweep::kMinWavesComplexTrap : sweep::kMinWavesComplex);
+}
+
+// Waves per workgroup for a launch of `waves` waves on `cus` CUs.  A real
+// state keeps 4 (its waves never meet).  A complex state takes the widest of
+// 16, 8 and 4 that loads the busiest CU no more than 4 does: its workgroup
+// reads a contiguous piece of theta per step 16 times as long as one wave's
+// (8x2048x4096 complex exp-Euler fp32 1.357 -> 1.279 ms with 16, bf16 0.898
+// -> 0.853 with 8), while a workgroup count that leaves CUs short of work
+// costs more (4x2560x8192 trapezoid, 2560 waves: 1.54 -> 1.67 ms with 16).
+inline int sweep_wg_waves(int64_t waves, bool is_complex, int cus) {
+    if (!is_complex || cus < 1) return sweep::kWaves;
+    auto busiest = [&](int64_t k) { return ((waves + k - 1) / k + cus - 1) / cus * k; };
+    for (int k = sweep::kWavesWide; k > sweep::kWaves; k /= 2)
+        if (busiest(k) <= busiest(sweep::kWaves)) return k;
+    return sweep::kWaves;
 }
 
 // The per-block byte offsets a lane forms are 32-bit: 17 rows of D elements
@@ -434,12 +452,14 @@ __device__ __forceinline__ uint32_t sweep_xcd_block(uint32_t bid, uint32_t nb) {
     return before + y;
 }
 
-template <typename T, int DISC, bool CPLX, bool PAIRS>
-__global__ void __launch_bounds__(sweep::kWaves * 64, 4) sweep_scan_kernel(SweepParams p) {
+// WAVES waves per workgroup (4, 8 or 16): four waves per SIMD in each case.
+template <typename T, int DISC, bool CPLX, bool PAIRS, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64, 16 / WAVES) sweep_scan_kernel(SweepParams p) {
     using namespace sweep;
     using E = Elem<T>;
     constexpr int kCE = CPLX ? 2 : 1;
-    __shared__ SweepLds s_all[kWaves];
+    static_assert(WAVES == 4 || WAVES == 8 || WAVES == 16, "workgroup of 4, 8 or 16 waves");
+    __shared__ SweepLds s_all[WAVES];
     // the wave index is uniform; saying so keeps every block address and
     // buffer resource in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -450,7 +470,7 @@ __global__ void __launch_bounds__(sweep::kWaves * 64, 4) sweep_scan_kernel(Sweep
     // (every load out of range, every store dropped), so that each wave of a
     // workgroup meets the same barriers.
     const int64_t waves = p.batch * n_dblk;
-    const int64_t wv = static_cast<int64_t>(sweep_xcd_block(blockIdx.x, gridDim.x)) * kWaves + wave;
+    const int64_t wv = static_cast<int64_t>(sweep_xcd_block(blockIdx.x, gridDim.x)) * WAVES + wave;
     const bool live = wv < waves;
     SweepLds& s = s_all[wave];
 

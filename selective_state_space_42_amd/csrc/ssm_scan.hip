@@ -113,35 +113,49 @@ bool sweep_unsupported(const ssm_scan_desc_t* d) {
            (ssm::sweep_waves(d->batch, d->dim) + ssm::sweep::kWaves - 1) / ssm::sweep::kWaves > INT32_MAX;
 }
 
-template <typename T, int DISC, bool CPLX>
-void launch_sweep_k(const ssm::SweepParams& p, bool pairs, dim3 grid, hipStream_t s) {
+template <typename T, int DISC, int WAVES>
+void launch_sweep_c(const ssm::SweepParams& p, bool pairs, int64_t waves, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>((waves + WAVES - 1) / WAVES)), block(WAVES * 64);
     if (pairs)
-        hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, DISC, CPLX, true>), grid, dim3(ssm::sweep::kWaves * 64), 0, s,
-                           p);
+        hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, DISC, true, true, WAVES>), grid, block, 0, s, p);
     else
-        hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, DISC, CPLX, false>), grid, dim3(ssm::sweep::kWaves * 64), 0, s,
-                           p);
+        hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, DISC, true, false, WAVES>), grid, block, 0, s, p);
+}
+template <typename T, int DISC>
+void launch_sweep_k(const ssm::SweepParams& p, bool pairs, int64_t waves, int wg_waves, hipStream_t s) {
+    if (wg_waves == 16)
+        launch_sweep_c<T, DISC, 16>(p, pairs, waves, s);
+    else if (wg_waves == 8)
+        launch_sweep_c<T, DISC, 8>(p, pairs, waves, s);
+    else
+        launch_sweep_c<T, DISC, ssm::sweep::kWaves>(p, pairs, waves, s);
 }
 
 // pairs: complex B and C aligned to whole (re, im) entries
 template <typename T>
 int launch_sweep(const ssm_scan_desc_t* d, const ssm::SweepParams& p, bool pairs, hipStream_t s) {
-    const int64_t blocks = (ssm::sweep_waves(d->batch, d->dim) + ssm::sweep::kWaves - 1) / ssm::sweep::kWaves;
+    const int64_t waves = ssm::sweep_waves(d->batch, d->dim);
+    const int64_t blocks = (waves + ssm::sweep::kWaves - 1) / ssm::sweep::kWaves;
     const dim3 grid(static_cast<unsigned>(blocks));
     if (d->is_complex) {
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_status(e);
+        const int wg = ssm::sweep_wg_waves(waves, true, cus);
         if (d->disc == SSM_DISC_EXP_EULER)
-            launch_sweep_k<T, ssm::kEuler, true>(p, pairs, grid, s);
+            launch_sweep_k<T, ssm::kEuler>(p, pairs, waves, wg, s);
         else
-            launch_sweep_k<T, ssm::kTrap, true>(p, pairs, grid, s);
+            launch_sweep_k<T, ssm::kTrap>(p, pairs, waves, wg, s);
     } else {
         if (d->disc == SSM_DISC_ZOH)
-            hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, ssm::kZOH, false, false>), grid,
+            hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, ssm::kZOH, false, false, ssm::sweep::kWaves>), grid,
                                dim3(ssm::sweep::kWaves * 64), 0, s, p);
         else if (d->disc == SSM_DISC_EXP_EULER)
-            hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, ssm::kEuler, false, false>), grid,
+            hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, ssm::kEuler, false, false, ssm::sweep::kWaves>), grid,
                                dim3(ssm::sweep::kWaves * 64), 0, s, p);
         else
-            hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, ssm::kTrap, false, false>), grid,
+            hipLaunchKernelGGL((ssm::sweep_scan_kernel<T, ssm::kTrap, false, false, ssm::sweep::kWaves>), grid,
                                dim3(ssm::sweep::kWaves * 64), 0, s, p);
     }
     return hip_status(hipGetLastError());

@@ -186,3 +186,13 @@ def test_sweep_unaligned_bc(mode):
         assert v.data_ptr() % (2 * t.element_size()) != 0
         return v
     _run(w, "sweep", inputs=dict(inp, Bm=shifted(inp["Bm"]), Cm=shifted(inp["Cm"])))
+
+
+@pytest.mark.parametrize("mode", ["complex_euler_f32", "complex_euler_bf16", "complex_trap_bf16"])
+@pytest.mark.parametrize("batch,dim", [(2, 4096), (4, 4093)])
+def test_sweep_wide_workgroups(mode, batch, dim):
+    """2048 and 4096 waves of 4 channels (the second with a ragged last
+    group): on a 256-CU GPU the complex sweep packs 8 and 16 waves per
+    workgroup, which then meet at a barrier every block."""
+    w = MODES[mode].scaled(name=f"{mode}_b{batch}_d{dim}_wide", batch=batch, dim=dim, seqlen=37)
+    _run(w, "sweep")
