@@ -130,30 +130,24 @@ inline bool sweep_offsets_fit(int64_t D, int64_t N, int64_t es) {
 // LDS of one wave.
 struct SweepLds {
     float4 bc[sweep::kS][sweep::kLPC];  // (B re, B im, C re, C im) per (step, state); real: (B, C) pairs
-    float2 dw[sweep::kS][sweep::kCPW];  // (delta, w) per (step, channel)
+    float2 dw[sweep::kS][sweep::kCPW];  // (delta, w) per (step, channel), two steps per 16 bytes
     float k[sweep::kS];                 // K_t (trapezoid)
     float red[64 * sweep::kRedStride];  // the lanes' partial outputs, one padded row per lane
 };
 
-// B/C entry of (step, state) in the LDS: 16 bytes for a complex state, the
-// first half of the array as (B, C) pairs for a real one (an 8-byte read per
-// step instead of 16).
+// B/C entry of (step, state) in the LDS: 16 bytes for a complex state; for a
+// real one the first half of the array as (B, C) pairs, the pairs of steps
+// 2k and 2k+1 side by side, so that one 16-byte read serves two steps.  The
+// (delta, w) terms are paired the same way: a real step then costs one LDS
+// read instead of two (measured 1-3 % faster).
 template <bool CPLX>
 __device__ __forceinline__ void st_bc(SweepLds& s, int st, int n, const float (&v)[4]) {
     if constexpr (CPLX)
         s.bc[st][n] = make_float4(v[0], v[1], v[2], v[3]);
     else
-        reinterpret_cast<float2*>(&s.bc[0][0])[st * sweep::kLPC + n] = make_float2(v[0], v[2]);
+        reinterpret_cast<float2*>(&s.bc[0][0])[((st >> 1) * sweep::kLPC + n) * 2 + (st & 1)] = make_float2(v[0], v[2]);
 }
-template <bool CPLX>
-__device__ __forceinline__ float4 ld_bc(const SweepLds& s, int st, int n) {
-    if constexpr (CPLX) {
-        return s.bc[st][n];
-    } else {
-        const float2 v = reinterpret_cast<const float2*>(&s.bc[0][0])[st * sweep::kLPC + n];
-        return make_float4(v.x, 0.f, v.y, 0.f);
-    }
-}
+__device__ __forceinline__ float4 ld_bc_complex(const SweepLds& s, int st, int n) { return s.bc[st][n]; }
 
 // One block's loads, as they arrive: per-(step, channel) rows for the lane's
 // step, B/C entries for its kBcSteps steps.
@@ -339,7 +333,7 @@ __device__ __forceinline__ float sweep_commit(SweepLds& s, const SweepLane& g, c
         }
         ey = (dsk - bnext * s.k[g.rn]) * x;
     }
-    s.dw[g.rn][g.rc] = make_float2(dt, w);
+    (&s.dw[0][0])[((g.rn >> 1) * kCPW + g.rc) * 2 + (g.rn & 1)] = make_float2(dt, w);
     return ey;
 }
 
@@ -353,16 +347,36 @@ __device__ __forceinline__ void sweep_steps(SweepLds& s, const SweepLane& g, Swe
                                             float& gi) {
     using namespace sweep;
     float* red = s.red + (g.c * kLPC + g.n) * kRedStride;
-    float2 nx_dw = s.dw[0][g.c];
-    float4 nx_bc = ld_bc<CPLX>(s, 0, g.n);
+    // (delta, w) and, for a real state, (B, C) of steps 2k and 2k+1 arrive
+    // in one read, one pair ahead; a complex state's B/C one step ahead
+    const float4* dw4 = reinterpret_cast<const float4*>(&s.dw[0][0]);
+    const float4* bc4 = reinterpret_cast<const float4*>(&s.bc[0][0]);
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 nx_dw2 = dw4[g.c], cur_dw2 = zero;
+    float4 nx_bc2 = zero, cur_bc2 = zero, nx_bc = zero;
+    if constexpr (CPLX)
+        nx_bc = ld_bc_complex(s, 0, g.n);
+    else
+        nx_bc2 = bc4[g.n];
 #pragma unroll
     for (int st = 0; st < kS; ++st) {
-        const float2 dw = nx_dw;  // (delta, w)
-        const float4 bc = nx_bc;
-        if (st + 1 < kS) {
-            nx_dw = s.dw[st + 1][g.c];
-            nx_bc = ld_bc<CPLX>(s, st + 1, g.n);
+        if (st % 2 == 0) {
+            cur_dw2 = nx_dw2;
+            cur_bc2 = nx_bc2;
+            if (st + 2 < kS) {
+                nx_dw2 = dw4[((st + 2) >> 1) * kCPW + g.c];
+                if constexpr (!CPLX) nx_bc2 = bc4[((st + 2) >> 1) * kLPC + g.n];
+            }
         }
+        const float2 dw = st % 2 ? make_float2(cur_dw2.z, cur_dw2.w) : make_float2(cur_dw2.x, cur_dw2.y);
+        float4 bc;
+        if constexpr (CPLX) {
+            bc = nx_bc;
+            if (st + 1 < kS) nx_bc = ld_bc_complex(s, st + 1, g.n);
+        } else {
+            bc = st % 2 ? make_float4(cur_bc2.z, 0.f, cur_bc2.w, 0.f) : make_float4(cur_bc2.x, 0.f, cur_bc2.y, 0.f);
+        }
+
         float py;
         if constexpr (CPLX) {
             const float rho = exp_dA(dw.x, a2);
